@@ -1,0 +1,207 @@
+/*
+ * dspark.h — C ABI of the DSpark draft-and-verify round on MI355X (gfx950).
+ *
+ * DSpark (arXiv:2607.05147) drafts a gamma-token block with a parallel
+ * backbone plus a light sequential head, scores every drafted position with
+ * a confidence head, lets a hardware-aware scheduler decide how many drafts
+ * of each request the target model verifies this round, and verifies them by
+ * lossless rejection sampling.  This library implements the four steps that
+ * sit between the backbone and the target model, as HIP kernels:
+ *
+ *   dspark_markov_sample  the sequential Markov-head sampling loop
+ *   dspark_confidence     the confidence head (linear + sigmoid, temperature)
+ *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
+ *   dspark_verify         rejection-sampling verification + residual draw
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to row-major arrays, 16-byte
+ *     aligned, on the device that is current when the call is made.  The
+ *     caller owns every buffer; the library never allocates, frees or
+ *     synchronises, and never reads device data on the host.
+ *   - Inputs are const and are never written.  Outputs are fully
+ *     overwritten.  Inputs and outputs must not alias.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and is safe to capture into a HIP graph: no
+ *     allocation, no memset node, no host synchronisation.
+ *   - Host-checkable preconditions (sizes, null pointers, workspace size,
+ *     data type) are checked before anything is enqueued; a failed check
+ *     returns an error code and enqueues nothing.  A failed launch returns
+ *     DSPARK_ELAUNCH.  Conditions on device data (token ranges, confidences
+ *     in [0,1], a positive non-increasing step-speed table) are the caller's
+ *     obligations and are not checked.
+ *   - No call keeps state between calls; calls on different streams with
+ *     different workspaces may run concurrently.
+ *   - dt selects the storage type of the large tensors (U, W1, W2, w, h,
+ *     target): fp32 or bf16.  Arithmetic is fp32 (scheduler: fp64 and exact
+ *     integers).  Random draws are inputs, drawn by the caller.
+ *
+ * Citations name the reading notes of the paper at zhongzhuzhou.org ("notes"),
+ * the summary at caijizhuo.github.io ("caijizhuo") and the chapter at
+ * llm-infra-atlas.github.io ("atlas").
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = 1,      /* a size or pointer argument is invalid            */
+  DSPARK_EDTYPE = 2,      /* unsupported data type for this call / shape       */
+  DSPARK_EWORKSPACE = 3,  /* workspace missing or smaller than required        */
+  DSPARK_ELAUNCH = 4,     /* a kernel launch failed                            */
+  DSPARK_EDEVICE = 5      /* the current device is not a gfx950 GPU            */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Tokens per chunk of the two-level Gumbel draw; the chunk Gumbel tensor G
+ * has ceil(V / DSPARK_CHUNK) entries per drafted position. */
+#define DSPARK_CHUNK 64
+
+/* Workspace selectors for dspark_workspace_size. */
+typedef enum { DSPARK_WS_SAMPLE = 0, DSPARK_WS_SCHEDULE = 2, DSPARK_WS_VERIFY = 3 } dspark_ws_kind;
+
+/*
+ * dspark_markov_sample — the semi-autoregressive gamma-step sampling loop.
+ *
+ * Passage: notes eq (4) (bias added inside the softmax:
+ * p_k(v) ∝ exp(U_k(v) + B_k(v))) and eq (5) (Markov head,
+ * B(x_{k-1}, .) = W1[x_{k-1}] W2, rank r); caijizhuo section 四, the
+ * sequential loop of dspark_cycle (only the sampled token is carried from
+ * position to position).  Position 1 conditions on the anchor x0.
+ *
+ * The draw at each position is an exact two-level Gumbel-max: the
+ * vocabulary is split into chunks of DSPARK_CHUNK consecutive tokens; the
+ * chunk is argmax_c (LSE_c + G[c]) where LSE_c is the log-sum-exp of the
+ * chunk's logits, and the token is the in-chunk argmax of l_v + g[v mod 64].
+ * Ties go to the lower token.
+ *
+ *   U      [R][gamma][V]  dt   base logits U_k of the parallel backbone
+ *   W1     [V][r]         dt   token -> r-vector table of the Markov head
+ *   W2t    [V][r]         dt   W2 (r x V) stored transposed: row v of W2t
+ *                              is column v of W2
+ *   x0     [R]            i32  anchor tokens; -1 = no previous token (B_1 = 0)
+ *   G      [R][gamma][ceil(V/64)] f32  chunk Gumbels
+ *   g      [R][gamma][64]         f32  in-chunk Gumbels
+ *   x      [R][gamma]     i32  out: drafted tokens
+ *   lse    [R][gamma]     f32  out: log sum_v exp(U_k(v) + B_k(v))
+ *   logit  [R][gamma]     f32  out: U_k(x_k) + B_k(x_k)
+ *   ws     workspace of at least dspark_workspace_size(DSPARK_WS_SAMPLE, ...)
+ *          bytes; contents on entry are irrelevant.
+ *
+ * Limits: R >= 1, 1 <= gamma <= 64, 2 <= V < 2^24.  bf16: r a multiple of
+ * 32, r <= 256.  fp32: 1 <= r <= 1024.
+ */
+dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int r,
+                                   const void* U, const void* W1, const void* W2t,
+                                   const int32_t* x0, const float* G, const float* g,
+                                   int32_t* x, float* lse, float* logit,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_confidence — conditional survival of every drafted position.
+ *
+ * Passage: notes eq (7), c_k = sigmoid(w^T [h_k ; W1[x_{k-1}]]), and the
+ * sequential temperature scaling paragraph (an order-preserving
+ * per-position rescaling before the cumulative product); atlas section 4.2.
+ * Computed here as z = w[:d].h_k + w[d:].W1[x_{k-1}], c = sigmoid(z / T_k),
+ * with x_{k-1} = x0 at k = 1 (x0 = -1 makes the W1 part zero).
+ *
+ *   h   [R][gamma][d]  dt   backbone hidden states
+ *   w   [d + r]        dt   weights: the h part first, then the W1 part
+ *   W1  [V][r]         dt   as in dspark_markov_sample
+ *   x0  [R], x [R][gamma]   i32 anchors and drafted tokens
+ *   T   [gamma]        f32  per-position temperatures, or NULL for T_k = 1
+ *   c   [R][gamma]     f32  out
+ *   z   [R][gamma]     f32  out, may be NULL: the logit before temperature
+ *
+ * Limits: d a multiple of 8 (bf16) or 4 (fp32); r likewise.
+ */
+dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r, int V,
+                                const void* h, const void* w, const void* W1,
+                                const int32_t* x0, const int32_t* x, const float* T,
+                                float* c, float* z, void* stream);
+
+/*
+ * dspark_schedule — hardware-aware prefix scheduler, batched.
+ *
+ * Passage: notes, "hardware-aware prefix scheduler": Algorithm 1 steps 1-6
+ * (cumulative survival, one pooled ranking of every (r, j), greedy admission
+ * from B = R, tau = R while Theta = tau * SPS(B) strictly increases, stop at
+ * the first non-increase); caijizhuo sections 三 and 四 (admit).
+ * Exactness: survival is the fp64 left-to-right product of the fp32
+ * confidences, quantised to a_fx = floor(a * 2^50); slots with a_fx = 0 are
+ * not candidates; ties in a_fx go to the lower request, then the lower
+ * position; tau is an exact integer sum and every Theta comparison is exact.
+ * The result is therefore bit-exact and independent of summation order.
+ *
+ *   c          [R][gamma]  f32  confidences (already temperature-scaled)
+ *   sps        [n_sps]     f64  sps[B-1] = SPS(B) in steps/s, positive and
+ *                               non-increasing; n_sps >= R * (1 + gamma)
+ *   ell        [R]         i32  out: admitted draft length l_r in 0..gamma
+ *   admitted   [1]         i32  out, may be NULL: A = sum_r l_r
+ *   theta_best [1]         f64  out, may be NULL:
+ *                               double(tau_fx) * 2^-50 * SPS(R + A)
+ *   ws         workspace of dspark_workspace_size(DSPARK_WS_SCHEDULE, ...) bytes
+ *
+ * Limits: R * (1 + gamma) <= 8191.
+ */
+dspark_status dspark_schedule(int R, int gamma, const float* c, const double* sps, int n_sps,
+                              int32_t* ell, int32_t* admitted, double* theta_best,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_verify — lossless rejection-sampling verification.
+ *
+ * Passage: notes, the speculative-decoding background (accept x with
+ * probability min(1, p_t(x)/p_d(x)); at the first rejection resample from
+ * norm(max(0, p_t - p_d)); a bonus token from p_t when everything is
+ * accepted), eq (8a)-(8c), steps 12-13 of the end-to-end loop; caijizhuo
+ * section 四 steps 5-6 (row i of the target logits predicts draft i).
+ * Draft i of request r is accepted iff ln u_acc[r][i] < ln p_t(x_i) -
+ * ln p_d(x_i); n_acc[r] is the length of the accepted prefix (0..ell[r]).
+ * next_tok[r] is the smallest v with cumsum(res)[v] > u_res[r] * sum(res),
+ * res = max(0, p_t - p_d) on row n_acc[r] after a rejection, res = p_t of
+ * row ell[r] otherwise; if sum(res) <= 0 the draw uses p_t of the same row.
+ *
+ *   target  target logits, dt: dense [R][gamma+1][V] when row0 == NULL, else
+ *           a packed [rows][V] array whose rows row0[r] .. row0[r] + ell[r]
+ *           belong to request r (a flattened ragged verify batch)
+ *   row0    [R] i32 or NULL
+ *   U, W1, W2t, x0  as in dspark_markov_sample (to rebuild p_d on the
+ *           residual row)
+ *   x, lse, logit   [R][gamma] outputs of dspark_markov_sample
+ *   ell     [R] i32 output of dspark_schedule (read on the device)
+ *   u_acc   [R][gamma] f32 uniforms in (0,1); u_res [R] f32 uniforms in (0,1)
+ *   n_acc   [R] i32 out; next_tok [R] i32 out
+ *   ws      workspace of dspark_workspace_size(DSPARK_WS_VERIFY, ...) bytes
+ *
+ * Limits: as dspark_markov_sample.
+ */
+dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r,
+                            const void* target, const int32_t* row0,
+                            const void* U, const void* W1, const void* W2t,
+                            const int32_t* x0, const int32_t* x, const float* lse,
+                            const float* logit, const int32_t* ell,
+                            const float* u_acc, const float* u_res,
+                            int32_t* n_acc, int32_t* next_tok,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace a call needs (0 for an invalid shape).  Arguments that a
+ * call does not take are ignored. */
+size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r, int n_sps);
+
+/* A static, human-readable description of a status code. */
+const char* dspark_status_string(dspark_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,221 @@
+"""ctypes binding of libdspark.so: argument marshalling only.
+
+Each wrapper takes torch tensors that already live on the current GPU,
+checks their shapes, types and contiguity on the host, and passes raw device
+pointers and torch's current HIP stream to the C entry point of the same
+name.  No step of the round runs in Python: if the library is missing the
+import fails, and a non-zero status raises DSparkError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdspark.so")
+
+F32, BF16 = 0, 1
+CHUNK = 64
+WS_SAMPLE, WS_SCHEDULE, WS_VERIFY = 0, 2, 3
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "dspark_markov_sample": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_confidence": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "dspark_schedule": [_I, _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P],
+    "dspark_verify": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                      _P, _SZ, _P],
+    "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
+    "dspark_status_string": [_I],
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({dspark_status_string(status)})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdspark.so (built by semi_ar_draft_round_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: run `python -m semi_ar_draft_round_amd.build` first")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.dspark_workspace_size.restype = ctypes.c_size_t
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def dspark_status_string(status: int) -> str:
+    return load_library().dspark_status_string(int(status)).decode()
+
+
+def dspark_workspace_size(kind: int, R: int, gamma: int, V: int, r: int = 0, n_sps: int = 0) -> int:
+    return int(load_library().dspark_workspace_size(kind, R, gamma, V, r, n_sps))
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(t, name, shape, dtypes, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported storage dtype {t.dtype}")
+
+
+def _raise(fn, st):
+    if st != 0:
+        raise DSparkError(fn, st)
+
+
+_ws_cache: dict = {}
+
+
+def workspace(kind: int, R: int, gamma: int, V: int, r: int, device) -> torch.Tensor:
+    """A cached device workspace of the size the library asks for."""
+    n = max(1, dspark_workspace_size(kind, R, gamma, V, r, 0))
+    key = (kind, R, gamma, V, r, str(device))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < n:
+        ws = torch.empty(n, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def dspark_markov_sample(U, W1, W2t, x0, G, g, x=None, lse=None, logit=None, ws=None):
+    """x, lse, logit = sampled tokens, log-normalisers and logits, [R][gamma]."""
+    lib = load_library()
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    sdt = (U.dtype,)
+    _check(U, "U", (R, gamma, V), sdt, dev)
+    _check(W1, "W1", (V, r), sdt, dev)
+    _check(W2t, "W2t", (V, r), sdt, dev)
+    _check(x0, "x0", (R,), (torch.int32,), dev)
+    _check(G, "G", (R, gamma, (V + CHUNK - 1) // CHUNK), (torch.float32,), dev)
+    _check(g, "g", (R, gamma, CHUNK), (torch.float32,), dev)
+    x = torch.empty((R, gamma), dtype=torch.int32, device=dev) if x is None else x
+    lse = torch.empty((R, gamma), dtype=torch.float32, device=dev) if lse is None else lse
+    logit = torch.empty((R, gamma), dtype=torch.float32, device=dev) if logit is None else logit
+    _check(x, "x", (R, gamma), (torch.int32,), dev)
+    _check(lse, "lse", (R, gamma), (torch.float32,), dev)
+    _check(logit, "logit", (R, gamma), (torch.float32,), dev)
+    ws = workspace(WS_SAMPLE, R, gamma, V, r, dev) if ws is None else ws
+    st = lib.dspark_markov_sample(_dt(U), R, gamma, V, r, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(x0),
+                                  _ptr(G), _ptr(g), _ptr(x), _ptr(lse), _ptr(logit), _ptr(ws),
+                                  ws.numel(), _stream())
+    _raise("dspark_markov_sample", st)
+    return x, lse, logit
+
+
+def dspark_confidence(h, w, W1, x0, x, T=None, c=None, z=None, want_z=True):
+    """c (and z) [R][gamma]: sigmoid(w . [h_k ; W1[x_{k-1}]] / T_k)."""
+    lib = load_library()
+    R, gamma, d = h.shape
+    V, r = W1.shape
+    dev = h.device
+    sdt = (h.dtype,)
+    _check(h, "h", (R, gamma, d), sdt, dev)
+    _check(w, "w", (d + r,), sdt, dev)
+    _check(W1, "W1", (V, r), sdt, dev)
+    _check(x0, "x0", (R,), (torch.int32,), dev)
+    _check(x, "x", (R, gamma), (torch.int32,), dev)
+    if T is not None:
+        _check(T, "T", (gamma,), (torch.float32,), dev)
+    c = torch.empty((R, gamma), dtype=torch.float32, device=dev) if c is None else c
+    if want_z and z is None:
+        z = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    st = lib.dspark_confidence(_dt(h), R, gamma, d, r, V, _ptr(h), _ptr(w), _ptr(W1), _ptr(x0),
+                               _ptr(x), _ptr(T), _ptr(c), _ptr(z), _stream())
+    _raise("dspark_confidence", st)
+    return c, z
+
+
+def dspark_schedule(c, sps, ell=None, admitted=None, theta_best=None):
+    """ell [R] int32, admitted [1] int32, theta_best [1] float64 (Algorithm 1)."""
+    lib = load_library()
+    R, gamma = c.shape
+    dev = c.device
+    _check(c, "c", (R, gamma), (torch.float32,), dev)
+    _check(sps, "sps", (sps.shape[0],), (torch.float64,), dev)
+    ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
+    admitted = torch.empty(1, dtype=torch.int32, device=dev) if admitted is None else admitted
+    theta_best = torch.empty(1, dtype=torch.float64, device=dev) if theta_best is None else theta_best
+    st = lib.dspark_schedule(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), _ptr(ell), _ptr(admitted),
+                             _ptr(theta_best), None, 0, _stream())
+    _raise("dspark_schedule", st)
+    return ell, admitted, theta_best
+
+
+def dspark_verify(target, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res, row0=None,
+                  n_acc=None, next_tok=None, ws=None):
+    """n_acc [R], next_tok [R] int32: rejection sampling with residual draw."""
+    lib = load_library()
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    sdt = (U.dtype,)
+    if row0 is None:
+        _check(target, "target", (R, gamma + 1, V), sdt, dev)
+    else:
+        _check(target, "target", (target.shape[0], V), sdt, dev)
+        _check(row0, "row0", (R,), (torch.int32,), dev)
+    _check(U, "U", (R, gamma, V), sdt, dev)
+    _check(W1, "W1", (V, r), sdt, dev)
+    _check(W2t, "W2t", (V, r), sdt, dev)
+    _check(x0, "x0", (R,), (torch.int32,), dev)
+    _check(x, "x", (R, gamma), (torch.int32,), dev)
+    _check(lse, "lse", (R, gamma), (torch.float32,), dev)
+    _check(logit, "logit", (R, gamma), (torch.float32,), dev)
+    _check(ell, "ell", (R,), (torch.int32,), dev)
+    _check(u_acc, "u_acc", (R, gamma), (torch.float32,), dev)
+    _check(u_res, "u_res", (R,), (torch.float32,), dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    next_tok = torch.empty(R, dtype=torch.int32, device=dev) if next_tok is None else next_tok
+    ws = workspace(WS_VERIFY, R, gamma, V, r, dev) if ws is None else ws
+    st = lib.dspark_verify(_dt(U), R, gamma, V, r, _ptr(target), _ptr(row0), _ptr(U), _ptr(W1),
+                           _ptr(W2t), _ptr(x0), _ptr(x), _ptr(lse), _ptr(logit), _ptr(ell),
+                           _ptr(u_acc), _ptr(u_res), _ptr(n_acc), _ptr(next_tok), _ptr(ws),
+                           ws.numel(), _stream())
+    _raise("dspark_verify", st)
+    return n_acc, next_tok

@@ -1,0 +1,178 @@
+// The C ABI: argument checks, workspace sizing and the launch sequences.
+// Every check that needs no device data happens here, before anything is
+// enqueued; the kernels themselves assume valid shapes.
+#include <string.h>
+
+#include <atomic>
+
+#include "common.hpp"
+
+namespace dspark {
+// sample.hip
+size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V);
+hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
+                         const void* W1, const void* W2t, const int32_t* x0, const float* G,
+                         const float* g, int32_t* x, float* lse, float* logit, void* ws,
+                         hipStream_t s);
+// confidence.hip
+hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
+                             const void* w, const void* W1, const int32_t* x0, const int32_t* x,
+                             const float* T, float* c, float* z, hipStream_t s);
+// schedule.hip
+size_t schedule_workspace_bytes();
+hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int32_t* ell,
+                           int32_t* admitted, double* theta_best, hipStream_t s);
+// verify.hip
+size_t verify_workspace_bytes(int R, int gamma, int V);
+hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                         const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                         const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
+                         const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
+                         int32_t* next_tok, void* ws, hipStream_t s);
+
+namespace {
+
+constexpr int kMaxGamma = 64;
+constexpr int kMaxVocab = 1 << 24;
+constexpr int kMaxSchedSlots = 8191;
+
+bool dtype_ok(dspark_dtype dt) { return dt == DSPARK_F32 || dt == DSPARK_BF16; }
+
+// r supported by the storage type: the bf16 matrix-core tile takes whole
+// k-steps of 32 with 1, 2, 4 or 8 of them in registers.
+bool rank_ok(dspark_dtype dt, int r) {
+  if (dt == DSPARK_BF16) return r == 32 || r == 64 || r == 128 || r == 256;
+  return r >= 1 && r <= 1024;
+}
+
+bool draft_shape_ok(int R, int gamma, int V) {
+  return R >= 1 && R <= 65535 && gamma >= 1 && gamma <= kMaxGamma && V >= 2 && V < kMaxVocab &&
+         static_cast<int64_t>(R) * gamma <= (1LL << 30);
+}
+
+// 0 = unknown, 1 = gfx950, 2 = something else
+std::atomic<int> g_device_kind[64];
+
+dspark_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DSPARK_EDEVICE;
+  int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSPARK_EDEVICE;
+    kind = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_kind[dev].store(kind, std::memory_order_relaxed);
+  }
+  return kind == 1 ? DSPARK_OK : DSPARK_EDEVICE;
+}
+
+}  // namespace
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+const char* dspark_status_string(dspark_status s) {
+  switch (s) {
+    case DSPARK_OK: return "success";
+    case DSPARK_EINVAL: return "invalid size or pointer argument";
+    case DSPARK_EDTYPE: return "unsupported data type or rank for this call";
+    case DSPARK_EWORKSPACE: return "workspace missing or too small";
+    case DSPARK_ELAUNCH: return "kernel launch failed";
+    case DSPARK_EDEVICE: return "current device is not a gfx950 GPU";
+  }
+  return "unknown status";
+}
+
+size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r, int n_sps) {
+  (void)r;
+  (void)n_sps;
+  switch (kind) {
+    case DSPARK_WS_SAMPLE:
+      if (!draft_shape_ok(R, gamma, V)) return 0;
+      // the fp32 path keeps one partial per chunk, the bf16 path fewer
+      return sample_workspace_bytes(DSPARK_F32, R, gamma, V) > sample_workspace_bytes(DSPARK_BF16, R, gamma, V)
+                 ? sample_workspace_bytes(DSPARK_F32, R, gamma, V)
+                 : sample_workspace_bytes(DSPARK_BF16, R, gamma, V);
+    case DSPARK_WS_SCHEDULE:
+      return schedule_workspace_bytes();
+    case DSPARK_WS_VERIFY:
+      if (!draft_shape_ok(R, gamma, V)) return 0;
+      return verify_workspace_bytes(R, gamma, V);
+  }
+  return 0;
+}
+
+dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
+                                   const void* W1, const void* W2t, const int32_t* x0, const float* G,
+                                   const float* g, int32_t* x, float* lse, float* logit, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
+  if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
+  if (!U || !W1 || !W2t || !x0 || !G || !g || !x || !lse || !logit) return DSPARK_EINVAL;
+  if (!ws || ws_bytes < sample_workspace_bytes(dt, R, gamma, V)) return DSPARK_EWORKSPACE;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws,
+                    static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
+                                const void* w, const void* W1, const int32_t* x0, const int32_t* x,
+                                const float* T, float* c, float* z, void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (!draft_shape_ok(R, gamma, V) || d < 1 || r < 1) return DSPARK_EINVAL;
+  const int vec = (dt == DSPARK_BF16) ? 8 : 4;
+  if (d % vec != 0 || r % vec != 0) return DSPARK_EINVAL;
+  if (!h || !w || !W1 || !x0 || !x || !c) return DSPARK_EINVAL;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (confidence_launch(dt, R, gamma, d, r, V, h, w, W1, x0, x, T, c, z, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_schedule(int R, int gamma, const float* c, const double* sps, int n_sps,
+                              int32_t* ell, int32_t* admitted, double* theta_best, void* ws,
+                              size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (R < 1 || gamma < 1 || gamma > kMaxGamma) return DSPARK_EINVAL;
+  if (static_cast<int64_t>(R) * (1 + gamma) > kMaxSchedSlots) return DSPARK_EINVAL;
+  if (n_sps < R * (1 + gamma)) return DSPARK_EINVAL;
+  if (!c || !sps || !ell) return DSPARK_EINVAL;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (schedule_launch(R, gamma, c, sps, ell, admitted, theta_best, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                            const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                            const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
+                            const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
+                            int32_t* next_tok, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
+  if (static_cast<int64_t>(R) * (gamma + 1) > 0x7FFFFFFF) return DSPARK_EINVAL;
+  if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
+  if (!target || !U || !W1 || !W2t || !x0 || !x || !lse || !logit || !ell || !u_acc || !u_res || !n_acc ||
+      !next_tok)
+    return DSPARK_EINVAL;
+  if (!ws || ws_bytes < verify_workspace_bytes(R, gamma, V)) return DSPARK_EWORKSPACE;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (verify_launch(dt, R, gamma, V, r, target, row0, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res,
+                    n_acc, next_tok, ws, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,476 @@
+// dspark_verify: lossless rejection-sampling verification.
+//
+// Passage: DSpark reading notes, the speculative-decoding background (accept
+// with probability min(1, p_t/p_d); at the first rejection resample from
+// norm(max(0, p_t - p_d)); a bonus token from p_t when all drafts pass),
+// eq (8a)-(8c) and steps 12-13 of the end-to-end loop; caijizhuo summary,
+// section 四 steps 5-6 (row i of the target logits predicts draft i).
+//
+// Four launches:
+//   verify_target_lse   one work group per needed target row (rows 0..l_r of
+//                       request r): its log-normaliser, and the target logit
+//                       of the drafted token on rows below l_r;
+//   verify_accept       one thread per request: the first i with
+//                       ln u_acc >= ln p_t(x_i) - ln p_d(x_i) -> n_acc;
+//   verify_residual_*   the residual row of every request in one pass over
+//                       the vocabulary: p_d is rebuilt from U and the Markov
+//                       bias of the previous token (same matrix-core tile as
+//                       the sampler), and every 64-token chunk's mass of
+//                       max(0, p_t - p_d) (or of p_t for the bonus row) and
+//                       of p_t is written out;
+//   verify_select       one work group per request: a prefix scan over the
+//                       chunk masses picks the chunk holding u_res * Z, and
+//                       one wave re-derives that chunk's 64 masses and scans
+//                       them to the token.
+#include "bias_tile.hpp"
+
+namespace dspark {
+
+constexpr int kVerifyWGs = 512;
+
+// ---------------------------------------------------------- target normalisers
+
+template <typename Elt>
+struct RowVec;
+template <>
+struct RowVec<BF16> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&o)[8]) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct RowVec<F32> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const float* p, float (&o)[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+
+__device__ __forceinline__ Lse block_reduce_lse(Lse a, Lse* sh) {
+  a = wave_reduce_lse(a);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sh[wave] = a;
+  __syncthreads();
+  Lse r = sh[0];
+  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) r = lse_combine(r, sh[w]);
+  return r;
+}
+
+template <typename Elt>
+__global__ __launch_bounds__(256) void verify_target_lse(int R, int gamma, int V,
+                                                         const typename Elt::T* __restrict__ target,
+                                                         const int32_t* __restrict__ row0,
+                                                         const int32_t* __restrict__ x,
+                                                         const int32_t* __restrict__ ell,
+                                                         float* __restrict__ lse_t, float* __restrict__ tx) {
+  __shared__ Lse sh[4];
+  const int r = blockIdx.x / (gamma + 1);
+  const int i = blockIdx.x % (gamma + 1);
+  const int L = min(max(ell[r], 0), gamma);
+  if (i > L) return;
+  const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + i : static_cast<int64_t>(r) * (gamma + 1) + i;
+  const typename Elt::T* t = target + row * V;
+  constexpr int N = RowVec<Elt>::N;
+  Lse acc{neg_inf(), 0.f};
+  if ((V % N) == 0) {
+    for (int v = threadIdx.x * N; v < V; v += 256 * N) {
+      float e[N];
+      RowVec<Elt>::load(t + v, e);
+      float m = e[0];
+#pragma unroll
+      for (int u = 1; u < N; ++u) m = fmaxf(m, e[u]);
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < N; ++u) s += __expf(e[u] - m);
+      acc = lse_combine(acc, Lse{m, s});
+    }
+  } else {
+    for (int v = threadIdx.x; v < V; v += 256) acc = lse_combine(acc, Lse{Elt::load(t, v), 1.f});
+  }
+  acc = block_reduce_lse(acc, sh);
+  if (threadIdx.x == 0) {
+    lse_t[static_cast<int64_t>(r) * (gamma + 1) + i] = acc.M + logf(acc.S);
+    if (i < L) {
+      const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
+      tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
+    }
+  }
+}
+
+// ------------------------------------------------------------------- accept
+
+__global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int32_t* __restrict__ ell,
+                                                     const float* __restrict__ tx,
+                                                     const float* __restrict__ lse_t,
+                                                     const float* __restrict__ logit,
+                                                     const float* __restrict__ lse,
+                                                     const float* __restrict__ u_acc,
+                                                     int32_t* __restrict__ n_acc) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  const int L = min(max(ell[r], 0), gamma);
+  int n = L;
+  for (int i = 0; i < L; ++i) {
+    const int64_t o = static_cast<int64_t>(r) * gamma + i;
+    const float log_ratio = (tx[o] - lse_t[static_cast<int64_t>(r) * (gamma + 1) + i]) - (logit[o] - lse[o]);
+    if (!(logf(u_acc[o]) < log_ratio)) {
+      n = i;
+      break;
+    }
+  }
+  n_acc[r] = n;
+}
+
+// ------------------------------------------------------- residual chunk masses
+
+struct ResidualRow {
+  int64_t trow;     // target row index
+  int64_t urow;     // draft row index (request * gamma + n), valid when rej
+  float lt, ld;     // target and draft log-normalisers of that row
+  int prev;         // previous token for the Markov bias, -1 if none / not needed
+  bool rej, live;
+};
+
+__device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, int V, const int32_t* row0,
+                                                    const int32_t* x0, const int32_t* x,
+                                                    const int32_t* ell, const int32_t* n_acc,
+                                                    const float* lse_t, const float* lse) {
+  ResidualRow rr{0, 0, 0.f, 0.f, -1, false, false};
+  if (req >= R) return rr;
+  rr.live = true;
+  const int L = min(max(ell[req], 0), gamma);
+  const int n = min(max(n_acc[req], 0), L);
+  rr.rej = n < L;
+  rr.trow = row0 ? static_cast<int64_t>(row0[req]) + n : static_cast<int64_t>(req) * (gamma + 1) + n;
+  rr.urow = static_cast<int64_t>(req) * gamma + (rr.rej ? n : 0);
+  rr.lt = lse_t[static_cast<int64_t>(req) * (gamma + 1) + n];
+  if (rr.rej) {
+    rr.ld = lse[rr.urow];
+    rr.prev = token_or_none((n == 0) ? x0[req] : x[static_cast<int64_t>(req) * gamma + n - 1], V);
+  }
+  return rr;
+}
+
+template <int NBW, int KS>
+__global__ __launch_bounds__(kTileThreads) void verify_residual_bf16(
+    int R, int gamma, int V, const uint16_t* __restrict__ target, const int32_t* __restrict__ row0,
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
+    const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
+    float* __restrict__ csum, float* __restrict__ psum) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[tile_lds_bytes(KS)];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 15;
+  const int q = lane >> 4;
+  const int nC = (V + kChunk - 1) / kChunk;
+  const bool vec_ok = (V & 3) == 0;
+
+  ResidualRow rr[NBW];
+  int prev[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int req = blockIdx.y * (kTileWaves * 16 * NBW) + wave * 16 * NBW + nb * 16 + j;
+    rr[nb] = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+    prev[nb] = rr[nb].prev;
+  }
+  WFrags<NBW, KS> e;
+  load_w1_frags<NBW, KS>(e, W1, prev);
+
+  for (int tile = blockIdx.x; tile < nC; tile += gridDim.x) {
+    const int v0 = tile * kChunk;
+    __syncthreads();
+    load_w2_tile<KS>(lds, W2t, V, v0);
+    uint2 tw[NBW][4], uw[NBW][4];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const uint16_t* Trow = target + rr[nb].trow * V;
+      const uint16_t* Urow = U + rr[nb].urow * V;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        tw[nb][mb] = load_row4(Trow, v0 + mb * 16 + 4 * q, V, vec_ok);
+        uw[nb][mb] = rr[nb].rej ? load_row4(Urow, v0 + mb * 16 + 4 * q, V, vec_ok) : make_uint2(0, 0);
+      }
+    }
+    __syncthreads();
+    f32x4 acc[4][NBW];
+    bias_tile<NBW, KS>(acc, lds, e);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      float sres = 0.f, spt = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = v0 + mb * 16 + 4 * q + i;
+          if (v < V) {
+            const float pt = __expf(row4_get(tw[nb][mb], i) - rr[nb].lt);
+            float res = pt;
+            if (rr[nb].rej)
+              res = fmaxf(0.f, pt - __expf(row4_get(uw[nb][mb], i) + acc[mb][nb][i] - rr[nb].ld));
+            sres += res;
+            spt += pt;
+          }
+        }
+      sres += __shfl_xor(sres, 16);
+      sres += __shfl_xor(sres, 32);
+      spt += __shfl_xor(spt, 16);
+      spt += __shfl_xor(spt, 32);
+      if (q == 0 && rr[nb].live) {
+        const int req = blockIdx.y * (kTileWaves * 16 * NBW) + wave * 16 * NBW + nb * 16 + j;
+        csum[static_cast<int64_t>(req) * nC + tile] = sres;
+        psum[static_cast<int64_t>(req) * nC + tile] = spt;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void verify_residual_f32(
+    int R, int gamma, int V, int r, const float* __restrict__ target, const int32_t* __restrict__ row0,
+    const float* __restrict__ U, const float* __restrict__ W1, const float* __restrict__ W2t,
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
+    const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
+    float* __restrict__ csum, float* __restrict__ psum) {
+  const int tile = blockIdx.x;
+  const int req = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int nC = (V + kChunk - 1) / kChunk;
+  const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  const int v = tile * kChunk + lane;
+  float res = 0.f, pt = 0.f;
+  if (v < V) {
+    pt = __expf(target[rr.trow * V + v] - rr.lt);
+    res = pt;
+    if (rr.rej) {
+      float b = 0.f;
+      if (rr.prev >= 0) {
+        const float* e = W1 + static_cast<int64_t>(rr.prev) * r;
+        const float* w = W2t + static_cast<int64_t>(v) * r;
+        for (int i = 0; i < r; ++i) b = fmaf(e[i], w[i], b);
+      }
+      res = fmaxf(0.f, pt - __expf(U[rr.urow * V + v] + b - rr.ld));
+    }
+  }
+  res = wave_reduce_sum(res);
+  pt = wave_reduce_sum(pt);
+  if (lane == 0) {
+    csum[static_cast<int64_t>(req) * nC + tile] = res;
+    psum[static_cast<int64_t>(req) * nC + tile] = pt;
+  }
+}
+
+// -------------------------------------------------------------------- select
+
+template <typename Elt>
+__device__ __forceinline__ float row_dot(const float* e_lds, const typename Elt::T* w, int r) {
+  float b = 0.f;
+  for (int i = 0; i < r; ++i) b = fmaf(e_lds[i], Elt::load(w, i), b);
+  return b;
+}
+
+template <typename Elt>
+__global__ __launch_bounds__(256) void verify_select(
+    int R, int gamma, int V, int r, const typename Elt::T* __restrict__ target,
+    const int32_t* __restrict__ row0, const typename Elt::T* __restrict__ U,
+    const typename Elt::T* __restrict__ W1, const typename Elt::T* __restrict__ W2t,
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
+    const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
+    const float* __restrict__ u_res, const float* __restrict__ csum, const float* __restrict__ psum,
+    int32_t* __restrict__ next_tok) {
+  __shared__ float scan[256];
+  __shared__ float e_row[1024];
+  __shared__ int s_chunk, s_last;
+  __shared__ float s_before;
+  const int req = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nC = (V + kChunk - 1) / kChunk;
+  const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  const int seg = (nC + 255) / 256;
+  const int lo = tid * seg;
+  const int hi = min(nC, lo + seg);
+
+  bool use_pt = !rr.rej;
+  const float* sums = rr.rej ? csum : psum;
+  float Z = 0.f, excl = 0.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    float local = 0.f;
+    for (int cc = lo; cc < hi; ++cc) local += sums[static_cast<int64_t>(req) * nC + cc];
+    scan[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const float v = (tid >= o) ? scan[tid - o] : 0.f;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    Z = scan[255];
+    excl = scan[tid] - local;
+    __syncthreads();
+    if (Z > 0.f || use_pt) break;
+    use_pt = true;                       // residual vanished: draw from p_t
+    sums = psum;
+  }
+  const float thr = u_res[req] * Z;
+  if (tid == 0) {
+    s_chunk = 0x7FFFFFFF;
+    s_last = -1;
+  }
+  __syncthreads();
+  float run = excl;
+  int first = 0x7FFFFFFF, last = -1;
+  float before = 0.f;
+  for (int cc = lo; cc < hi; ++cc) {
+    const float sv = sums[static_cast<int64_t>(req) * nC + cc];
+    if (sv > 0.f) last = cc;
+    if (first == 0x7FFFFFFF && run + sv > thr) {
+      first = cc;
+      before = run;
+    }
+    run += sv;
+  }
+  if (first != 0x7FFFFFFF) atomicMin(&s_chunk, first);
+  if (last >= 0) atomicMax(&s_last, last);
+  __syncthreads();
+  if (first != 0x7FFFFFFF && first == s_chunk) s_before = before;
+  if (s_chunk == 0x7FFFFFFF && last >= 0 && last == s_last) s_before = run - sums[static_cast<int64_t>(req) * nC + last];
+  // the previous token's W1 row, for the bias of the chunk's 64 tokens
+  if (!use_pt && rr.prev >= 0)
+    for (int i = tid; i < r; i += 256) e_row[i] = Elt::load(W1, static_cast<int64_t>(rr.prev) * r + i);
+  __syncthreads();
+  const int chunk = (s_chunk != 0x7FFFFFFF) ? s_chunk : max(s_last, 0);
+  if (tid < 64) {
+    const int v = chunk * kChunk + tid;
+    float val = 0.f;
+    if (v < V) {
+      const float pt = __expf(Elt::load(target, rr.trow * V + v) - rr.lt);
+      val = pt;
+      if (!use_pt) {
+        const float b = (rr.prev >= 0) ? row_dot<Elt>(e_row, W2t + static_cast<int64_t>(v) * r, r) : 0.f;
+        val = fmaxf(0.f, pt - __expf(Elt::load(U, rr.urow * V + v) + b - rr.ld));
+      }
+    }
+    const float cum = wave_inclusive_scan(val);
+    const float local_thr = thr - s_before;
+    const unsigned long long hit = __ballot(cum > local_thr);
+    int off;
+    if (hit) {
+      off = __ffsll(static_cast<long long>(hit)) - 1;
+    } else {
+      const unsigned long long pos = __ballot(val > 0.f);
+      off = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
+    }
+    if (tid == 0) next_tok[req] = chunk * kChunk + off;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+struct VerifyWs {
+  float* lse_t;   // [R][gamma+1]
+  float* tx;      // [R][gamma]
+  float* csum;    // [R][nC]
+  float* psum;    // [R][nC]
+};
+
+static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+size_t verify_workspace_bytes(int R, int gamma, int V) {
+  const size_t nC = static_cast<size_t>(ceil_div(V, kChunk));
+  return align256(sizeof(float) * R * (gamma + 1)) + align256(sizeof(float) * R * gamma) +
+         2 * align256(sizeof(float) * R * nC);
+}
+
+static VerifyWs carve(void* ws, int R, int gamma, int V) {
+  const size_t nC = static_cast<size_t>(ceil_div(V, kChunk));
+  char* p = static_cast<char*>(ws);
+  VerifyWs w;
+  w.lse_t = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * R * (gamma + 1));
+  w.tx = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * R * gamma);
+  w.csum = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * R * nC);
+  w.psum = reinterpret_cast<float*>(p);
+  return w;
+}
+
+template <int NBW, int KS>
+static void launch_residual_bf16(int R, int gamma, int V, const void* target, const int32_t* row0,
+                                 const void* U, const void* W1, const void* W2t, const int32_t* x0,
+                                 const int32_t* x, const float* lse, const int32_t* ell,
+                                 const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
+  const int nC = ceil_div(V, kChunk);
+  dim3 grid(nC < kVerifyWGs ? nC : kVerifyWGs, ceil_div(R, kTileWaves * 16 * NBW));
+  hipLaunchKernelGGL((verify_residual_bf16<NBW, KS>), grid, dim3(kTileThreads), 0, s, R, gamma, V,
+                     static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
+                     static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
+                     ell, n_acc, w.lse_t, w.csum, w.psum);
+}
+
+template <int KS>
+static void launch_residual_bf16_ks(int R, int gamma, int V, const void* target, const int32_t* row0,
+                                    const void* U, const void* W1, const void* W2t, const int32_t* x0,
+                                    const int32_t* x, const float* lse, const int32_t* ell,
+                                    const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
+  if (R <= 64)
+    launch_residual_bf16<1, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+  else if (R <= 128)
+    launch_residual_bf16<2, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+  else
+    launch_residual_bf16<4, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+}
+
+hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                         const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                         const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
+                         const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
+                         int32_t* next_tok, void* ws, hipStream_t s) {
+  const VerifyWs w = carve(ws, R, gamma, V);
+  const int nC = ceil_div(V, kChunk);
+  hipError_t err;
+  if (dt == DSPARK_BF16)
+    hipLaunchKernelGGL(verify_target_lse<BF16>, dim3(R * (gamma + 1)), dim3(256), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, x, ell, w.lse_t, w.tx);
+  else
+    hipLaunchKernelGGL(verify_target_lse<F32>, dim3(R * (gamma + 1)), dim3(256), 0, s, R, gamma, V,
+                       static_cast<const float*>(target), row0, x, ell, w.lse_t, w.tx);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(verify_accept, dim3(ceil_div(R, 256)), dim3(256), 0, s, R, gamma, ell, w.tx, w.lse_t,
+                     logit, lse, u_acc, n_acc);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (dt == DSPARK_BF16) {
+    switch (r / 32) {
+      case 1: launch_residual_bf16_ks<1>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      case 2: launch_residual_bf16_ks<2>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      case 4: launch_residual_bf16_ks<4>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      default: launch_residual_bf16_ks<8>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+    }
+  } else {
+    hipLaunchKernelGGL(verify_residual_f32, dim3(nC, R), dim3(64), 0, s, R, gamma, V, r,
+                       static_cast<const float*>(target), row0, static_cast<const float*>(U),
+                       static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, ell,
+                       n_acc, w.lse_t, w.csum, w.psum);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (dt == DSPARK_BF16)
+    hipLaunchKernelGGL(verify_select<BF16>, dim3(R), dim3(256), 0, s, R, gamma, V, r,
+                       static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
+                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
+                       ell, n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok);
+  else
+    hipLaunchKernelGGL(verify_select<F32>, dim3(R), dim3(256), 0, s, R, gamma, V, r,
+                       static_cast<const float*>(target), row0, static_cast<const float*>(U),
+                       static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, ell,
+                       n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

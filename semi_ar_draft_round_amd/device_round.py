@@ -1,0 +1,126 @@
+"""One draft-and-verify round on the GPU through the C ABI.
+
+`to_device` copies a RoundInputs (the seeded arrays of workloads.py) into
+device tensors once, with every output buffer and workspace preallocated, so
+that `run_round` only enqueues the four library calls and can be captured in
+a HIP graph.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _dev_store(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+@dataclasses.dataclass
+class DeviceRound:
+    R: int
+    gamma: int
+    V: int
+    r: int
+    d: int
+    U: torch.Tensor
+    W1: torch.Tensor
+    W2t: torch.Tensor
+    w: torch.Tensor
+    h: torch.Tensor
+    x0: torch.Tensor
+    target: Optional[torch.Tensor]
+    sps: torch.Tensor
+    T: Optional[torch.Tensor]
+    G: torch.Tensor
+    g: torch.Tensor
+    u_acc: torch.Tensor
+    u_res: torch.Tensor
+    # outputs
+    x: torch.Tensor
+    lse: torch.Tensor
+    logit: torch.Tensor
+    c: torch.Tensor
+    z: torch.Tensor
+    ell: torch.Tensor
+    admitted: torch.Tensor
+    theta_best: torch.Tensor
+    n_acc: torch.Tensor
+    next_tok: torch.Tensor
+    ws_sample: torch.Tensor
+    ws_verify: torch.Tensor
+
+
+def to_device(inp, device="cuda:0") -> DeviceRound:
+    w = inp.w
+    dev = torch.device(device)
+    R, gamma, V, r, d = w.R, w.gamma, w.V, w.r, w.d
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    dr = DeviceRound(
+        R, gamma, V, r, d,
+        U=_dev_store(inp.U, w.dtype, dev), W1=_dev_store(inp.E, w.dtype, dev),
+        W2t=_dev_store(inp.W2t, w.dtype, dev), w=_dev_store(inp.w_conf, w.dtype, dev),
+        h=_dev_store(inp.h, w.dtype, dev), x0=i32(inp.x0),
+        target=None if inp.target is None else _dev_store(inp.target, w.dtype, dev),
+        sps=torch.from_numpy(np.ascontiguousarray(inp.sps, dtype=np.float64)).to(dev),
+        T=None if inp.T is None else f32(inp.T),
+        G=f32(inp.G), g=f32(inp.g), u_acc=f32(inp.u_acc), u_res=f32(inp.u_res),
+        x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
+        lse=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+        logit=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+        c=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+        z=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+        ell=torch.empty(R, dtype=torch.int32, device=dev),
+        admitted=torch.empty(1, dtype=torch.int32, device=dev),
+        theta_best=torch.empty(1, dtype=torch.float64, device=dev),
+        n_acc=torch.empty(R, dtype=torch.int32, device=dev),
+        next_tok=torch.empty(R, dtype=torch.int32, device=dev),
+        ws_sample=torch.empty(max(1, B.dspark_workspace_size(B.WS_SAMPLE, R, gamma, V, r)),
+                              dtype=torch.uint8, device=dev),
+        ws_verify=torch.empty(max(1, B.dspark_workspace_size(B.WS_VERIFY, R, gamma, V, r)),
+                              dtype=torch.uint8, device=dev),
+    )
+    return dr
+
+
+def sample(d: DeviceRound):
+    B.dspark_markov_sample(d.U, d.W1, d.W2t, d.x0, d.G, d.g, d.x, d.lse, d.logit, ws=d.ws_sample)
+
+
+def confidence(d: DeviceRound):
+    B.dspark_confidence(d.h, d.w, d.W1, d.x0, d.x, d.T, d.c, d.z)
+
+
+def schedule(d: DeviceRound):
+    B.dspark_schedule(d.c, d.sps, d.ell, d.admitted, d.theta_best)
+
+
+def verify(d: DeviceRound):
+    B.dspark_verify(d.target, d.U, d.W1, d.W2t, d.x0, d.x, d.lse, d.logit, d.ell, d.u_acc,
+                    d.u_res, n_acc=d.n_acc, next_tok=d.next_tok, ws=d.ws_verify)
+
+
+def run_round(d: DeviceRound):
+    """Enqueue sample -> confidence -> schedule -> verify on the current stream."""
+    sample(d)
+    confidence(d)
+    schedule(d)
+    verify(d)
+
+
+def outputs_to_host(d: DeviceRound) -> dict:
+    torch.cuda.synchronize()
+    return dict(x=d.x.cpu().numpy(), lse=d.lse.cpu().numpy(), logit=d.logit.cpu().numpy(),
+                c=d.c.cpu().numpy(), z=d.z.cpu().numpy(), ell=d.ell.cpu().numpy(),
+                A=int(d.admitted.cpu()[0]), theta_best=float(d.theta_best.cpu()[0]),
+                n_acc=d.n_acc.cpu().numpy(), next_tok=d.next_tok.cpu().numpy())

@@ -1,0 +1,121 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, sizes workspaces, and rejects invalid host-checkable
+arguments before touching the device (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+LIB = os.path.join(ROOT, "semi_ar_draft_round_amd", "libdspark.so")
+
+EINVAL, EDTYPE, EWORKSPACE = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from semi_ar_draft_round_amd import build
+        build.build()
+    from semi_ar_draft_round_amd import binding
+    return binding.load_library(LIB)
+
+
+def test_header_declares_the_four_calls():
+    fns = declared_functions()
+    for name in ("dspark_markov_sample", "dspark_confidence", "dspark_schedule", "dspark_verify",
+                 "dspark_workspace_size", "dspark_status_string"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_declared_symbol():
+    from semi_ar_draft_round_amd import binding
+    assert sorted(binding.EXPORTED) == declared_functions()
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.dspark_status_string(s)
+    assert b"unknown" in lib.dspark_status_string(99)
+
+
+def test_workspace_sizes(lib):
+    from semi_ar_draft_round_amd import binding as B
+    n_c = (129280 + 63) // 64
+    ws = B.dspark_workspace_size(B.WS_SAMPLE, 128, 16, 129280, 256)
+    # argmax keys (8 slots per request and position) + one (max, sum) pair per
+    # chunk, request and position (the fp32 path's bound)
+    assert ws == 8 * 128 * 16 * 8 + 16 * 128 * n_c * 8
+    assert B.dspark_workspace_size(B.WS_VERIFY, 128, 16, 129280, 256) >= 4 * 128 * (2 * n_c + 33)
+    assert B.dspark_workspace_size(B.WS_SAMPLE, 0, 16, 129280, 256) == 0
+    assert B.dspark_workspace_size(B.WS_VERIFY, 4, 0, 1000, 256) == 0
+    assert B.dspark_workspace_size(B.WS_SCHEDULE, 128, 16, 0, 0) == 0
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)   # never dereferenced: every call below fails its host checks first
+
+
+def sample_call(lib, dt=1, R=4, gamma=3, V=1000, r=256, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.dspark_markov_sample(dt, R, gamma, V, r, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr,
+                                    ws, ws_bytes, None)
+
+
+def test_sample_rejects_bad_arguments(lib):
+    assert sample_call(lib, dt=7) == EDTYPE
+    assert sample_call(lib, R=0) == EINVAL
+    assert sample_call(lib, gamma=0) == EINVAL
+    assert sample_call(lib, gamma=65) == EINVAL
+    assert sample_call(lib, V=1) == EINVAL
+    assert sample_call(lib, V=1 << 24) == EINVAL
+    assert sample_call(lib, r=96) == EDTYPE       # bf16 tile needs 32, 64, 128 or 256
+    assert sample_call(lib, r=512) == EDTYPE
+    assert sample_call(lib, ptr=None) == EINVAL
+    assert sample_call(lib, ws=None) == EWORKSPACE
+    assert sample_call(lib, ws_bytes=16) == EWORKSPACE
+    assert sample_call(lib, dt=0, r=2000) == EDTYPE
+
+
+def test_confidence_rejects_bad_arguments(lib):
+    def call(dt=1, R=2, gamma=3, d=64, r=32, V=100, ptr=FAKE):
+        return lib.dspark_confidence(dt, R, gamma, d, r, V, ptr, ptr, ptr, ptr, ptr, None, ptr, None, None)
+    assert call(dt=3) == EDTYPE
+    assert call(d=63) == EINVAL
+    assert call(r=12) == EINVAL                 # bf16 needs multiples of 8
+    assert call(R=0) == EINVAL
+    assert call(ptr=None) == EINVAL
+
+
+def test_schedule_rejects_bad_arguments(lib):
+    def call(R=4, gamma=3, n_sps=16, ptr=FAKE):
+        return lib.dspark_schedule(R, gamma, ptr, ptr, n_sps, ptr, None, None, None, 0, None)
+    assert call(n_sps=15) == EINVAL             # SPS table must reach R * (1 + gamma)
+    assert call(R=0) == EINVAL
+    assert call(gamma=0) == EINVAL
+    assert call(R=482, gamma=16, n_sps=10000) == EINVAL   # 482 * 17 > 8191
+    assert call(ptr=None) == EINVAL
+
+
+def test_verify_rejects_bad_arguments(lib):
+    def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        args = [ptr] * 13
+        return lib.dspark_verify(dt, R, gamma, V, r, args[0], None, *args[1:], ws, ws_bytes, None)
+    assert call(dt=5) == EDTYPE
+    assert call(V=0) == EINVAL
+    assert call(r=48) == EDTYPE
+    assert call(ptr=None) == EINVAL
+    assert call(ws_bytes=8) == EWORKSPACE

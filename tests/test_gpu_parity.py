@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small workloads are checked on every output; the large ones (the sizes the
+benchmark times, in the same launch configuration) on a sample of requests
+the oracle recomputes one by one, plus the whole-batch scheduler."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from semi_ar_draft_round_amd import workloads as W
+
+from parity import check_confidence, check_sample, check_schedule, check_verify
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from semi_ar_draft_round_amd import binding
+    binding.load_library()
+    return torch.device("cuda:0")
+
+
+def run_gpu(inp, dev):
+    from semi_ar_draft_round_amd import device_round as DR
+    d = DR.to_device(inp, dev)
+    DR.run_round(d)
+    return d, DR.outputs_to_host(d)
+
+
+SMALL = [
+    W.BY_NAME["tiny_r1_g4_v1024_f32"],
+    W.custom("ragged_r20_g5_v1000_bf16", R=20, gamma=5, V=1000, r=256, d=512, seed=11),
+    W.custom("odd_v_r3_g3_v203_bf16", R=3, gamma=3, V=203, r=32, d=64, seed=12),
+    W.custom("r130_g4_v700_r128_bf16", R=130, gamma=4, V=700, r=128, d=256, seed=13, temperatures=True),
+    W.custom("r70_g6_v4100_r64_bf16", R=70, gamma=6, V=4100, r=64, d=128, seed=14),
+    W.custom("f32_r9_g7_v333", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=15),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_round_full_parity(w, dev):
+    say(f"[parity] {w.name}")
+    inp = W.make_inputs(w)
+    if w.name.startswith("odd_v"):
+        inp.x0[1] = -1                                  # no previous token: B_1 = 0
+    _, out = run_gpu(inp, dev)
+    idx = np.arange(w.R)
+    rs = check_sample(inp, out, idx)
+    rc = check_confidence(inp, out, idx)
+    rsch = check_schedule(inp.sps, out)
+    rv = check_verify(inp, out, idx)
+    say(f"  sample {rs}\n  conf {rc}\n  sched {rsch}\n  verify {rv}")
+
+
+LARGE = [W.BY_NAME[n] for n in ("latency_r1_g16_v151936", "batch_r32_g16_v151936",
+                                 "heavy_r128_g16_v129280", "full_r256_g16_v129280_sts")]
+
+
+@pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
+def test_full_size_sampled_parity(w, dev):
+    say(f"[parity] {w.name}: drawing inputs")
+    inp = W.make_inputs(w)
+    say(f"[parity] {w.name}: GPU round")
+    _, out = run_gpu(inp, dev)
+    rng = np.random.default_rng(7)
+    n = min(w.R, 6)
+    idx = np.sort(rng.choice(w.R, size=n, replace=False))
+    # always include the requests with the longest admitted prefix
+    longest = np.argsort(-out["ell"], kind="stable")[:2]
+    idx = np.unique(np.concatenate([idx, longest]))
+    say(f"[parity] {w.name}: oracle on requests {idx.tolist()}, A = {out['A']}")
+    rs = check_sample(inp, out, idx)
+    rc = check_confidence(inp, out, idx)
+    rsch = check_schedule(inp.sps, out)
+    rv = check_verify(inp, out, idx)
+    say(f"  sample {rs}\n  conf {rc}\n  sched {rsch}\n  verify {rv}")
+    assert np.all((out["x"] >= 0) & (out["x"] < w.V))
+    assert np.all((out["c"] >= 0) & (out["c"] <= 1))
+    assert np.all(out["n_acc"] <= out["ell"])
+    assert np.all((out["next_tok"] >= 0) & (out["next_tok"] < w.V))
+
+
+def test_packed_target_rows_match_dense(dev):
+    """A flattened ragged verify batch (row0 offsets) gives the dense result."""
+    from semi_ar_draft_round_amd import binding as B
+    from semi_ar_draft_round_amd import device_round as DR
+    w = W.custom("packed_r12_g5_v900", R=12, gamma=5, V=900, r=64, d=64, seed=21)
+    inp = W.make_inputs(w)
+    say(f"[parity] {w.name}")
+    d, out = run_gpu(inp, dev)
+    ell = out["ell"]
+    rows, row0 = [], []
+    for r in range(w.R):
+        row0.append(len(rows))
+        rows.extend(range(r * (w.gamma + 1), r * (w.gamma + 1) + ell[r] + 1))
+    packed = d.target.reshape(w.R * (w.gamma + 1), w.V)[torch.tensor(rows, device=dev)].contiguous()
+    row0_t = torch.tensor(row0, dtype=torch.int32, device=dev)
+    n2, t2 = B.dspark_verify(packed, d.U, d.W1, d.W2t, d.x0, d.x, d.lse, d.logit, d.ell,
+                             d.u_acc, d.u_res, row0=row0_t)
+    torch.cuda.synchronize()
+    assert n2.cpu().numpy().tolist() == out["n_acc"].tolist()
+    assert t2.cpu().numpy().tolist() == out["next_tok"].tolist()
+
+
+def test_determinism_and_workspace_poison(dev):
+    from semi_ar_draft_round_amd import device_round as DR
+    w = W.custom("det_r40_g6_v2000", R=40, gamma=6, V=2000, r=256, d=256, seed=31)
+    inp = W.make_inputs(w)
+    say(f"[parity] {w.name}")
+    d = DR.to_device(inp, dev)
+    DR.run_round(d)
+    a = DR.outputs_to_host(d)
+    d.ws_sample.fill_(0xFF)                       # NaN bit patterns everywhere
+    d.ws_verify.fill_(0xFF)
+    DR.run_round(d)
+    b = DR.outputs_to_host(d)
+    for k in a:
+        np.testing.assert_array_equal(np.asarray(a[k]), np.asarray(b[k]), err_msg=k)
+
+
+def test_graph_capture_replays_match_eager(dev):
+    from semi_ar_draft_round_amd import device_round as DR
+    w = W.custom("graph_r24_g4_v1500", R=24, gamma=4, V=1500, r=256, d=128, seed=41)
+    inp = W.make_inputs(w)
+    say(f"[parity] {w.name}")
+    d = DR.to_device(inp, dev)
+    DR.run_round(d)
+    ref = DR.outputs_to_host(d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            DR.run_round(d)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        d.x.fill_(-7)
+        d.next_tok.fill_(-7)
+        d.ws_sample.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        got = DR.outputs_to_host(d)
+        for k in ref:
+            np.testing.assert_array_equal(np.asarray(ref[k]), np.asarray(got[k]), err_msg=f"{k} replay {rep}")
