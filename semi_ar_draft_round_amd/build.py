@@ -16,6 +16,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libdspark.so")
 ARCH = "gfx950"
 
@@ -38,7 +39,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *sources]
+    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -52,6 +52,7 @@ bool draft_shape_ok(int R, int gamma, int V) {
 
 // 0 = unknown, 1 = gfx950, 2 = something else
 std::atomic<int> g_device_kind[64];
+std::atomic<int> g_device_cus[64];
 
 dspark_status check_device() {
   int dev = 0;
@@ -61,12 +62,23 @@ dspark_status check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DSPARK_EDEVICE;
     kind = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                            std::memory_order_relaxed);
     g_device_kind[dev].store(kind, std::memory_order_relaxed);
   }
   return kind == 1 ? DSPARK_OK : DSPARK_EDEVICE;
 }
 
 }  // namespace
+
+// Compute units of the current device (valid after a successful check_device).
+int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  const int n = g_device_cus[dev].load(std::memory_order_relaxed);
+  return n > 0 ? n : 1;
+}
+
 }  // namespace dspark
 
 using namespace dspark;

@@ -4,11 +4,11 @@
 //
 // Shape of the contraction (notes eq (5); cost eq (15)): M = 64 vocabulary
 // rows of W2t (the chunk), N = requests, K = r.  The W2t rows of the chunk
-// are one contiguous block of 64 * r bf16 in HBM; a work group copies it to
-// LDS once with coalesced 16-byte loads and all of its waves read their A
-// fragments from there.  Each wave keeps the W1 rows of its requests (the B
-// operand) in registers for the whole launch, because they do not change
-// along the vocabulary.
+// are one contiguous block of 64 * r bf16 in HBM; a work group stages it
+// through registers (coalesced 16-byte loads, issued two chunks ahead) into
+// an LDS tile, and all of its waves read their A fragments from there.  Each
+// wave keeps the W1 rows of its requests (the B operand) in registers for the
+// whole launch, because they do not change along the vocabulary.
 //
 // Lane layout of the 16x16x32 bf16 MFMA, lane = 16*q + j:
 //   A (16 x 32)  lane holds row j, k = 8q .. 8q+7
@@ -27,10 +27,13 @@ constexpr int kTileWaves = 4;
 constexpr int kTileThreads = kTileWaves * kWave;   // 256
 constexpr int kMaxKSteps = 8;                       // r <= 256
 
-// LDS row stride of a W2t tile row: r bf16 plus 16 bytes of padding so the
-// sixteen rows read by a quarter wave start in different banks.
-__host__ __device__ constexpr int tile_row_bytes(int ks) { return ks * 64 + 16; }
-__host__ __device__ constexpr int tile_lds_bytes(int ks) { return kChunk * tile_row_bytes(ks); }
+// A W2t tile is the chunk's 64 rows of r bf16 (KS * 4 sixteen-byte pieces
+// per row), stored unpadded with the piece index XOR-swizzled by the row:
+// piece c of row `row` sits in slot c ^ (row mod pieces-per-row).  The
+// sixteen rows one quarter wave reads for an A fragment then fall in
+// sixteen different bank groups, and the stores of a tile are conflict-free.
+__host__ __device__ constexpr int tile_pieces(int ks) { return ks * 4; }
+__host__ __device__ constexpr int tile_bytes(int ks) { return kChunk * ks * 64; }
 
 __device__ __forceinline__ bf16x8 load_bf16x8_global(const uint16_t* p) {
   uint4 v = *reinterpret_cast<const uint4*>(p);
@@ -61,26 +64,45 @@ __device__ __forceinline__ void load_w1_frags(WFrags<NBW, KS>& e, const uint16_t
   }
 }
 
-// Copy W2t rows v0 .. v0+63 (zeros past V) into LDS.
+// The W2t tile of one chunk staged in registers: the tile's 64 rows are one
+// contiguous block of 64 * r bf16, so thread t takes the 16-byte pieces
+// t, t + 256, ... of that block (fully coalesced); rows past V read row V-1
+// (their tokens are masked by the caller).
 template <int KS>
-__device__ __forceinline__ void load_w2_tile(uint8_t* lds, const uint16_t* W2t, int V, int v0) {
-  constexpr int kPerRow = KS * 4;                 // 16-byte pieces per row
-  constexpr int kTotal = kChunk * kPerRow;
+struct WRegs {
+  u32x4 w[KS];
+};
+
+template <int KS>
+__device__ __forceinline__ void load_w2_regs(WRegs<KS>& wr, const uint16_t* W2t, int V, int v0) {
+  constexpr int P = tile_pieces(KS);
 #pragma unroll
-  for (int t = threadIdx.x; t < kTotal; t += kTileThreads) {
-    const int row = t / kPerRow;
-    const int c = t % kPerRow;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (v0 + row < V)
-      val = *reinterpret_cast<const uint4*>(W2t + static_cast<int64_t>(v0 + row) * (KS * 32) + c * 8);
-    *reinterpret_cast<uint4*>(lds + row * tile_row_bytes(KS) + c * 16) = val;
+  for (int s = 0; s < KS; ++s) {
+    const int piece = s * kTileThreads + threadIdx.x;
+    const int row = piece / P;
+    const int c = piece % P;
+    const int vrow = min(v0 + row, V - 1);
+    wr.w[s] = *reinterpret_cast<const u32x4*>(W2t + static_cast<int64_t>(vrow) * (KS * 32) + c * 8);
+  }
+}
+
+template <int KS>
+__device__ __forceinline__ void store_w2_tile(uint8_t* tile, const WRegs<KS>& wr) {
+  constexpr int P = tile_pieces(KS);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int piece = s * kTileThreads + threadIdx.x;
+    const int row = piece / P;
+    const int slot = (piece % P) ^ (row & (P - 1));
+    *reinterpret_cast<u32x4*>(tile + (row * P + slot) * 16) = wr.w[s];
   }
 }
 
 // acc[mb][nb][i] = bias of request (nb, j) at token v0 + 16 mb + 4q + i.
 template <int NBW, int KS>
-__device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* lds,
+__device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* tile,
                                           const WFrags<NBW, KS>& e) {
+  constexpr int P = tile_pieces(KS);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   const int q = lane >> 4;
@@ -92,9 +114,11 @@ __device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* l
   for (int ks = 0; ks < KS; ++ks) {
     bf16x8 a[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      a[mb] = *reinterpret_cast<const bf16x8*>(lds + (mb * 16 + j) * tile_row_bytes(KS) +
-                                               (ks * 32 + q * 8) * 2);
+    for (int mb = 0; mb < 4; ++mb) {
+      const int row = mb * 16 + j;
+      const int slot = (ks * 4 + q) ^ (row & (P - 1));
+      a[mb] = *reinterpret_cast<const bf16x8*>(tile + (row * P + slot) * 16);
+    }
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -105,17 +129,34 @@ __device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* l
 
 // Four consecutive bf16 logits of one row starting at token `v` (a multiple
 // of 4), as raw words; entries past V read as 0 (the caller masks them).
-__device__ __forceinline__ uint2 load_row4(const uint16_t* row, int v, int V, bool vec_ok) {
-  if (vec_ok && v + 3 < V) return *reinterpret_cast<const uint2*>(row + v);
-  uint16_t w[4];
+__device__ __forceinline__ u32x2 load_row4(const uint16_t* row, int v, int V, bool vec_ok) {
+  if (vec_ok && v + 3 < V) return *reinterpret_cast<const u32x2*>(row + v);
+  uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (v + i < V) ? row[v + i] : uint16_t(0);
-  return make_uint2(w[0] | (uint32_t(w[1]) << 16), w[2] | (uint32_t(w[3]) << 16));
+  for (int i = 0; i < 4; ++i) w[i] = (v + i < V) ? row[v + i] : 0u;
+  return u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+}
+
+// Sixteen logits of one row for this lane (chunk offsets 16 mb + 4q + i).
+// VEC (V a multiple of 4): one 8-byte load per M-block; a group of four
+// tokens is either wholly inside the row or wholly past V, and groups past V
+// re-read the chunk's first group (their tokens are masked by the caller), so
+// there is no data-dependent branch.  Otherwise the checked path.
+template <bool VEC>
+__device__ __forceinline__ void load_lane_logits(u32x2 (&out)[4], const uint16_t* row, int v0, int V, int q) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int v = v0 + mb * 16 + 4 * q;
+    if constexpr (VEC)
+      out[mb] = *reinterpret_cast<const u32x2*>(row + (v < V ? v : v0));
+    else
+      out[mb] = load_row4(row, v, V, false);
+  }
 }
 
 __device__ __forceinline__ float word_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float word_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ float row4_get(uint2 p, int i) {
+__device__ __forceinline__ float row4_get(u32x2 p, int i) {
   return i == 0 ? word_lo(p.x) : i == 1 ? word_hi(p.x) : i == 2 ? word_lo(p.y) : word_hi(p.y);
 }
 

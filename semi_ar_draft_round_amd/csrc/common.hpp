@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/dspark.h"
+#include "dspark.h"
 
 namespace dspark {
 
@@ -13,6 +13,10 @@ constexpr int kChunk = DSPARK_CHUNK;   // tokens per chunk of the two-level draw
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Native vectors (not HIP's struct vector types): copies of these stay in
+// registers instead of becoming memcpy through private memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -26,7 +26,6 @@
 
 namespace dspark {
 
-constexpr int kVerifyWGs = 512;
 
 // ---------------------------------------------------------- target normalisers
 
@@ -160,77 +159,126 @@ __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, i
 }
 
 template <int NBW, int KS>
-__global__ __launch_bounds__(kTileThreads) void verify_residual_bf16(
+struct ResidualStage {
+  WRegs<KS> w;
+  u32x2 t[NBW][4];   // target logits
+  u32x2 u[NBW][4];   // draft base logits (rejected rows; others re-read U row 0)
+};
+
+// The residual row of every request of a group, chunk by chunk, staged like
+// the sampler: loads two chunks ahead in two register sets, unconditional
+// (clamped) so the compiler never drains the prefetch; chunk i+1 is parked
+// in the other half of a double-buffered LDS area at the start of chunk i.
+template <int NBW, int KS, bool VEC>
+__global__ __launch_bounds__(kTileThreads, 1) void verify_residual_bf16(
     int R, int gamma, int V, const uint16_t* __restrict__ target, const int32_t* __restrict__ row0,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
     float* __restrict__ csum, float* __restrict__ psum) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[tile_lds_bytes(KS)];
+  constexpr int NROWS = kTileWaves * 16 * NBW;
+  constexpr int kW = tile_bytes(KS);
+  constexpr int kU = kTileThreads * NBW * 4 * 8 * 2;    // this lane's target and U logits
+  constexpr int kBuf = kW + kU;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBuf];
+  constexpr float kLog2e = 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int q = lane >> 4;
   const int nC = (V + kChunk - 1) / kChunk;
-  const bool vec_ok = (V & 3) == 0;
+  // the host launches at most one work group per chunk, so nT >= 1
+  const int nT = (nC - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
 
   ResidualRow rr[NBW];
-  int prev[NBW];
+  int prev[NBW], req[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
-    const int req = blockIdx.y * (kTileWaves * 16 * NBW) + wave * 16 * NBW + nb * 16 + j;
-    rr[nb] = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+    req[nb] = blockIdx.y * NROWS + wave * 16 * NBW + nb * 16 + j;
+    rr[nb] = residual_row(min(req[nb], R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+    rr[nb].live = req[nb] < R;
     prev[nb] = rr[nb].prev;
   }
-  WFrags<NBW, KS> e;
-  load_w1_frags<NBW, KS>(e, W1, prev);
-
-  for (int tile = blockIdx.x; tile < nC; tile += gridDim.x) {
-    const int v0 = tile * kChunk;
-    __syncthreads();
-    load_w2_tile<KS>(lds, W2t, V, v0);
-    uint2 tw[NBW][4], uw[NBW][4];
+  auto load_stage = [&](ResidualStage<NBW, KS>& st, int it) {
+    const int v0 = (blockIdx.x + it * gridDim.x) * kChunk;
+    load_w2_regs<KS>(st.w, W2t, V, v0);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
-      const uint16_t* Trow = target + rr[nb].trow * V;
-      const uint16_t* Urow = U + rr[nb].urow * V;
+      load_lane_logits<VEC>(st.t[nb], target + rr[nb].trow * V, v0, V, q);
+      // rows with no rejection need no draft logits: they read U row 0 (cached)
+      load_lane_logits<VEC>(st.u[nb], U + (rr[nb].rej ? rr[nb].urow : 0) * V, v0, V, q);
+    }
+  };
+  auto park = [&](const ResidualStage<NBW, KS>& st, int buf) {
+    store_w2_tile<KS>(lds + buf * kBuf, st.w);
+    u32x2* up = reinterpret_cast<u32x2*>(lds + buf * kBuf + kW) + threadIdx.x * NBW * 8;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        tw[nb][mb] = load_row4(Trow, v0 + mb * 16 + 4 * q, V, vec_ok);
-        uw[nb][mb] = rr[nb].rej ? load_row4(Urow, v0 + mb * 16 + 4 * q, V, vec_ok) : make_uint2(0, 0);
+        up[nb * 8 + mb] = st.t[nb][mb];
+        up[nb * 8 + 4 + mb] = st.u[nb][mb];
       }
-    }
-    __syncthreads();
+  };
+  const auto clampc = [&](int it) { return it < nT ? it : nT - 1; };
+  ResidualStage<NBW, KS> even, odd;
+  load_stage(even, 0);
+  load_stage(odd, clampc(1));
+  WFrags<NBW, KS> e;
+  load_w1_frags<NBW, KS>(e, W1, prev);
+  park(even, 0);
+  __builtin_amdgcn_s_waitcnt(0);     // prologue loads have landed before the loop
+  load_stage(even, clampc(2));
+  __syncthreads();
+
+  auto chunk = [&](int it, ResidualStage<NBW, KS>& nxt) {
+    const int tile = blockIdx.x + it * gridDim.x;
+    const int v0 = tile * kChunk;
+    const int buf = it & 1;
+    park(nxt, buf ^ 1);
+    load_stage(nxt, clampc(it + 3));
+    const u32x2* up = reinterpret_cast<const u32x2*>(lds + buf * kBuf + kW) + threadIdx.x * NBW * 8;
     f32x4 acc[4][NBW];
-    bias_tile<NBW, KS>(acc, lds, e);
+    bias_tile<NBW, KS>(acc, lds + buf * kBuf, e);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
+      const float lt2 = rr[nb].lt * kLog2e;
+      const float ld2 = rr[nb].ld * kLog2e;
       float sres = 0.f, spt = 0.f;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        const u32x2 tw = up[nb * 8 + mb];
+        const u32x2 uw = up[nb * 8 + 4 + mb];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = v0 + mb * 16 + 4 * q + i;
           if (v < V) {
-            const float pt = __expf(row4_get(tw[nb][mb], i) - rr[nb].lt);
+            const float pt = __builtin_amdgcn_exp2f(fmaf(row4_get(tw, i), kLog2e, -lt2));
             float res = pt;
             if (rr[nb].rej)
-              res = fmaxf(0.f, pt - __expf(row4_get(uw[nb][mb], i) + acc[mb][nb][i] - rr[nb].ld));
+              res = fmaxf(0.f, pt - __builtin_amdgcn_exp2f(fmaf(row4_get(uw, i) + acc[mb][nb][i], kLog2e, -ld2)));
             sres += res;
             spt += pt;
           }
         }
+      }
       sres += __shfl_xor(sres, 16);
       sres += __shfl_xor(sres, 32);
       spt += __shfl_xor(spt, 16);
       spt += __shfl_xor(spt, 32);
       if (q == 0 && rr[nb].live) {
-        const int req = blockIdx.y * (kTileWaves * 16 * NBW) + wave * 16 * NBW + nb * 16 + j;
-        csum[static_cast<int64_t>(req) * nC + tile] = sres;
-        psum[static_cast<int64_t>(req) * nC + tile] = spt;
+        csum[static_cast<int64_t>(req[nb]) * nC + tile] = sres;
+        psum[static_cast<int64_t>(req[nb]) * nC + tile] = spt;
       }
     }
+    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < nT; it += 2) {
+    chunk(it, odd);
+    chunk(it + 1, even);
   }
+  if (it < nT) chunk(it, odd);
 }
 
 __global__ __launch_bounds__(64) void verify_residual_f32(
@@ -402,17 +450,28 @@ static VerifyWs carve(void* ws, int R, int gamma, int V) {
   return w;
 }
 
+int compute_units();   // abi.hip
+
 template <int NBW, int KS>
 static void launch_residual_bf16(int R, int gamma, int V, const void* target, const int32_t* row0,
                                  const void* U, const void* W1, const void* W2t, const int32_t* x0,
                                  const int32_t* x, const float* lse, const int32_t* ell,
                                  const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
   const int nC = ceil_div(V, kChunk);
-  dim3 grid(nC < kVerifyWGs ? nC : kVerifyWGs, ceil_div(R, kTileWaves * 16 * NBW));
-  hipLaunchKernelGGL((verify_residual_bf16<NBW, KS>), grid, dim3(kTileThreads), 0, s, R, gamma, V,
-                     static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
-                     static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
-                     ell, n_acc, w.lse_t, w.csum, w.psum);
+  const int groups = ceil_div(R, kTileWaves * 16 * NBW);
+  int gx = compute_units() / groups;
+  gx = gx < 1 ? 1 : (gx > nC ? nC : gx);
+  dim3 grid(gx, groups);
+  if (V % 4 == 0)
+    hipLaunchKernelGGL((verify_residual_bf16<NBW, KS, true>), grid, dim3(kTileThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
+                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
+                       ell, n_acc, w.lse_t, w.csum, w.psum);
+  else
+    hipLaunchKernelGGL((verify_residual_bf16<NBW, KS, false>), grid, dim3(kTileThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
+                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
+                       ell, n_acc, w.lse_t, w.csum, w.psum);
 }
 
 template <int KS>
@@ -422,10 +481,8 @@ static void launch_residual_bf16_ks(int R, int gamma, int V, const void* target,
                                     const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
   if (R <= 64)
     launch_residual_bf16<1, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
-  else if (R <= 128)
-    launch_residual_bf16<2, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
   else
-    launch_residual_bf16<4, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+    launch_residual_bf16<2, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
 }
 
 hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
