@@ -61,8 +61,8 @@ typedef enum {
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 
 /* Tokens per chunk of the two-level Gumbel draw; the chunk Gumbel tensor G
- * has ceil(V / DSPARK_CHUNK) entries per drafted position. */
-#define DSPARK_CHUNK 64
+ * has ceil(V / DSPARK_CHUNK) entries per drafted position and request. */
+#define DSPARK_CHUNK 16
 
 /* Workspace selectors for dspark_workspace_size. */
 typedef enum { DSPARK_WS_SAMPLE = 0, DSPARK_WS_SCHEDULE = 2, DSPARK_WS_VERIFY = 3 } dspark_ws_kind;
@@ -77,18 +77,20 @@ typedef enum { DSPARK_WS_SAMPLE = 0, DSPARK_WS_SCHEDULE = 2, DSPARK_WS_VERIFY = 
  * position to position).  Position 1 conditions on the anchor x0.
  *
  * The draw at each position is an exact two-level Gumbel-max: the
- * vocabulary is split into chunks of DSPARK_CHUNK consecutive tokens; the
- * chunk is argmax_c (LSE_c + G[c]) where LSE_c is the log-sum-exp of the
- * chunk's logits, and the token is the in-chunk argmax of l_v + g[v mod 64].
- * Ties go to the lower token.
+ * vocabulary is split into chunks of DSPARK_CHUNK (16) consecutive tokens;
+ * the chunk is argmax_c (LSE_c + G[c]) where LSE_c is the log-sum-exp of the
+ * chunk's logits, and the token is the in-chunk argmax of l_v + g[v mod 16].
+ * Ties go to the lower token (up to fp32 rounding of the chunk scores).
  *
  *   U      [R][gamma][V]  dt   base logits U_k of the parallel backbone
  *   W1     [V][r]         dt   token -> r-vector table of the Markov head
  *   W2t    [V][r]         dt   W2 (r x V) stored transposed: row v of W2t
  *                              is column v of W2
  *   x0     [R]            i32  anchor tokens; -1 = no previous token (B_1 = 0)
- *   G      [R][gamma][ceil(V/64)] f32  chunk Gumbels
- *   g      [R][gamma][64]         f32  in-chunk Gumbels
+ *   G      [gamma][ceil(V/16)][R] f32  chunk Gumbels, request-minor: the
+ *                                      Gumbel of chunk c of request i at
+ *                                      position k is G[(k*nC + c)*R + i]
+ *   g      [R][gamma][16]         f32  in-chunk Gumbels
  *   x      [R][gamma]     i32  out: drafted tokens
  *   lse    [R][gamma]     f32  out: log sum_v exp(U_k(v) + B_k(v))
  *   logit  [R][gamma]     f32  out: U_k(x_k) + B_k(x_k)

@@ -27,7 +27,7 @@ def run_round(inp, requests=None) -> dict:
     E = as_f64(inp.E, dt)
     W2t = as_f64(inp.W2t, dt)
     x0 = inp.x0[idx].astype(np.int64)
-    s = markov_sample(U, E, W2t, x0, inp.G[idx], inp.g[idx])
+    s = markov_sample(U, E, W2t, x0, inp.G_by_request(idx), inp.g[idx])
     cf = confidence(as_f64(inp.h[idx], dt), as_f64(inp.w_conf, dt), E, x0, s["x"], inp.T)
     sc = admit(cf["c"].astype(np.float32), inp.sps)
     ell = sc["ell"]

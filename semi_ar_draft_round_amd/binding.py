@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 F32, BF16 = 0, 1
-CHUNK = 64
+CHUNK = 16   # tokens per chunk of the two-level Gumbel draw
 WS_SAMPLE, WS_SCHEDULE, WS_VERIFY = 0, 2, 3
 
 _lib = None
@@ -132,7 +132,7 @@ def dspark_markov_sample(U, W1, W2t, x0, G, g, x=None, lse=None, logit=None, ws=
     _check(W1, "W1", (V, r), sdt, dev)
     _check(W2t, "W2t", (V, r), sdt, dev)
     _check(x0, "x0", (R,), (torch.int32,), dev)
-    _check(G, "G", (R, gamma, (V + CHUNK - 1) // CHUNK), (torch.float32,), dev)
+    _check(G, "G", (gamma, (V + CHUNK - 1) // CHUNK, R), (torch.float32,), dev)
     _check(g, "g", (R, gamma, CHUNK), (torch.float32,), dev)
     x = torch.empty((R, gamma), dtype=torch.int32, device=dev) if x is None else x
     lse = torch.empty((R, gamma), dtype=torch.float32, device=dev) if lse is None else lse

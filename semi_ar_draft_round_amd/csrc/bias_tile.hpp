@@ -98,18 +98,37 @@ __device__ __forceinline__ void store_w2_tile(uint8_t* tile, const WRegs<KS>& wr
   }
 }
 
-// acc[mb][nb][i] = bias of request (nb, j) at token v0 + 16 mb + 4q + i.
+// Second tile layout, for kernels where each lane owns sixteen consecutive
+// tokens: the tile row of token offset t (0..63) is stored at row
+// lane16_row(t), which swaps the bit fields [5:4] and [3:2] of t.  Reading
+// stored row 16 mb + j as A row j of M-block mb then gives lane (q, j) the
+// tokens 16 q + 4 mb + i (i = 0..3) of the chunk: over the four M-blocks,
+// the sixteen consecutive tokens 16 q .. 16 q + 15.
+__host__ __device__ constexpr int lane16_row(int t) {
+  return (((t >> 2) & 3) << 4) | (((t >> 4) & 3) << 2) | (t & 3);
+}
+
+template <int KS>
+__device__ __forceinline__ void store_w2_tile_lane16(uint8_t* tile, const WRegs<KS>& wr) {
+  constexpr int P = tile_pieces(KS);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int piece = s * kTileThreads + threadIdx.x;
+    const int row = lane16_row(piece / P);
+    const int slot = (piece % P) ^ (row & (P - 1));
+    *reinterpret_cast<u32x4*>(tile + (row * P + slot) * 16) = wr.w[s];
+  }
+}
+
+// acc[mb][nb] += the bias block of M-block mb for request group nb (the C
+// operand comes in through acc).
 template <int NBW, int KS>
-__device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* tile,
-                                          const WFrags<NBW, KS>& e) {
+__device__ __forceinline__ void bias_tile_acc(f32x4 (&acc)[4][NBW], const uint8_t* tile,
+                                              const WFrags<NBW, KS>& e) {
   constexpr int P = tile_pieces(KS);
   const int lane = threadIdx.x & 63;
   const int j = lane & 15;
   const int q = lane >> 4;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     bf16x8 a[4];
@@ -125,6 +144,18 @@ __device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* t
       for (int mb = 0; mb < 4; ++mb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], e.f[nb][ks], acc[mb][nb], 0, 0, 0);
   }
+}
+
+// acc[mb][nb][i] = bias of request (nb, j) at token v0 + 16 mb + 4q + i
+// (tile stored by store_w2_tile).
+template <int NBW, int KS>
+__device__ __forceinline__ void bias_tile(f32x4 (&acc)[4][NBW], const uint8_t* tile,
+                                          const WFrags<NBW, KS>& e) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bias_tile_acc<NBW, KS>(acc, tile, e);
 }
 
 // Four consecutive bf16 logits of one row starting at token `v` (a multiple

@@ -9,7 +9,9 @@
 namespace dspark {
 
 constexpr int kWave = 64;
-constexpr int kChunk = DSPARK_CHUNK;   // tokens per chunk of the two-level draw
+constexpr int kChunk = 64;              // vocabulary tile of the kernels (MFMA M extent)
+constexpr int kGChunk = DSPARK_CHUNK;   // tokens per chunk of the two-level Gumbel draw
+static_assert(kChunk % kGChunk == 0, "a tile holds whole Gumbel chunks");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

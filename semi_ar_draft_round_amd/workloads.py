@@ -13,8 +13,10 @@ does not increase with the batch size.  The second argument of N(., .) is a
 variance throughout (the pages write the logit spread as N(0, 2^2)).
 
 Random draws that the method itself makes are inputs too:
-  G     [R][gamma][nC]  one Gumbel per 64-token chunk of the vocabulary,
-  g     [R][gamma][64]  the in-chunk Gumbels, shared by every chunk,
+  G     [gamma][nC][R]  one Gumbel per 16-token chunk of the vocabulary, per
+                        position and request (request-minor, the layout the
+                        library reads),
+  g     [R][gamma][16]  the in-chunk Gumbels, shared by every chunk,
   u_acc [R][gamma]      one uniform per drafted position for the accept test,
   u_res [R]             one uniform per request for the residual / bonus draw.
 Uniforms are odd multiples of 2^-24, so they lie strictly inside (0, 1) and
@@ -30,7 +32,7 @@ from typing import Optional
 
 import numpy as np
 
-CHUNK = 64  # tokens per chunk of the two-level Gumbel draw (shape of G and g)
+CHUNK = 16  # tokens per chunk of the two-level Gumbel draw (shape of G and g)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,7 +154,7 @@ class RoundInputs:
     target: np.ndarray     # [R][gamma+1][V] target logits; row i predicts draft position i
     sps: np.ndarray        # [n_sps] float64
     T: Optional[np.ndarray]  # [gamma] float32 or None
-    G: np.ndarray          # [R][gamma][nC] float32
+    G: np.ndarray          # [gamma][nC][R] float32
     g: np.ndarray          # [R][gamma][CHUNK] float32
     u_acc: np.ndarray      # [R][gamma] float32
     u_res: np.ndarray      # [R] float32
@@ -160,6 +162,11 @@ class RoundInputs:
     @property
     def dtype(self) -> str:
         return self.w.dtype
+
+    def G_by_request(self, idx=None) -> np.ndarray:
+        """G as [R][gamma][nC] (a transposed view), optionally for requests idx."""
+        Gr = np.transpose(self.G, (2, 0, 1))
+        return Gr if idx is None else Gr[idx]
 
 
 def make_inputs(w: Workload, round_index: int = 0, with_target: bool = True) -> RoundInputs:
@@ -217,7 +224,7 @@ def make_inputs(w: Workload, round_index: int = 0, with_target: bool = True) -> 
         T = (1.0 + k / max(1, gamma - 1)).astype(np.float32)
 
     nC = w.n_chunks
-    G = gumbel_from_uniform(odd_uniform(rng, (R, gamma, nC)))
+    G = gumbel_from_uniform(odd_uniform(rng, (gamma, nC, R)))
     g = gumbel_from_uniform(odd_uniform(rng, (R, gamma, CHUNK)))
     u_acc = odd_uniform(rng, (R, gamma))
     u_res = odd_uniform(rng, (R,))

@@ -42,7 +42,7 @@ def check_sample(inp, gpu, idx):
     E = as_f64(inp.E, dt)
     W2t = as_f64(inp.W2t, dt)
     xg = gpu["x"][idx].astype(np.int64)
-    out = markov_sample(U, E, W2t, inp.x0[idx].astype(np.int64), inp.G[idx], inp.g[idx],
+    out = markov_sample(U, E, W2t, inp.x0[idx].astype(np.int64), inp.G_by_request(idx), inp.g[idx],
                         teacher_x=xg, keep_steps=True)
     gamma = U.shape[1]
     worst = dict(chunk_gap=0.0, inner_gap=0.0, lse=0.0, logit=0.0, exact=0, total=0)

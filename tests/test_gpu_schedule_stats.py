@@ -141,8 +141,8 @@ def test_gpu_lossless_and_acceptance_rate(dev):
     W2t = bf(np.zeros((V, r)))
     rng = np.random.default_rng(11)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
-    G = f32(W.gumbel_from_uniform(W.odd_uniform(rng, (R, gamma, 1))))
-    g = f32(W.gumbel_from_uniform(W.odd_uniform(rng, (R, gamma, 64))))
+    G = f32(W.gumbel_from_uniform(W.odd_uniform(rng, (gamma, 1, R))))
+    g = f32(W.gumbel_from_uniform(W.odd_uniform(rng, (R, gamma, W.CHUNK))))
     x0 = torch.zeros(R, dtype=torch.int32, device=dev)
     x, lse, logit = B.dspark_markov_sample(U, W1, W2t, x0, G, g)
     ell = torch.ones(R, dtype=torch.int32, device=dev)

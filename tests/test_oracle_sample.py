@@ -45,15 +45,16 @@ def test_bias_one_hot_rows_select_columns_of_w2():
     np.testing.assert_array_equal(B[3], W2t[:, 49 % r])
 
 
-def test_single_chunk_reduces_to_textbook_gumbel_max():
+@pytest.mark.parametrize("C,V", [(64, 50), (16, 12), (16, 16)])
+def test_single_chunk_reduces_to_textbook_gumbel_max(C, V):
     rng = np.random.default_rng(1)
-    R, V, r = 64, 50, 4
+    R, r = 64, 4
     U = rng.normal(0, 2, size=(R, 1, V))
     E = rng.normal(0, 0.5, size=(V, r))
     W2t = rng.normal(0, 0.5, size=(V, r))
     x0 = rng.integers(-1, V, size=R)
     G = gumbels(rng, (R, 1, 1))
-    g = gumbels(rng, (R, 1, 64))
+    g = gumbels(rng, (R, 1, C))
     out = markov_sample(U, E, W2t, x0, G, g)
     for i in range(R):
         bias = np.zeros(V) if x0[i] < 0 else sum(E[x0[i], k] * W2t[:, k] for k in range(r))
@@ -64,25 +65,32 @@ def test_single_chunk_reduces_to_textbook_gumbel_max():
         assert out["logit"][i, 0] == pytest.approx(l[out["x"][i, 0]], rel=1e-13, abs=1e-13)
 
 
-def test_chunk_log_normalisers_closed_form():
-    R, V = 1, 150          # chunks of 64, 64 and a short tail of 22
+@pytest.mark.parametrize("C,V,sizes", [(64, 150, [64.0, 64.0, 22.0]),
+                                       (16, 40, [16.0, 16.0, 8.0])])
+def test_chunk_log_normalisers_closed_form(C, V, sizes):
+    R = 1          # two full chunks and a short tail
     U = np.full((R, 1, V), 0.7)
     E = np.zeros((V, 4))
     W2t = np.zeros((V, 4))
-    st = sample_position(U[:, 0], E, W2t, np.array([-1]), np.zeros((1, 3)), np.zeros((1, 64)))
-    np.testing.assert_allclose(st["chunk_score"][0], 0.7 + np.log([64.0, 64.0, 22.0]), rtol=1e-14)
-    assert st["lse"][0] == pytest.approx(0.7 + np.log(150.0), rel=1e-14)
+    st = sample_position(U[:, 0], E, W2t, np.array([-1]), np.zeros((1, 3)), np.zeros((1, C)))
+    np.testing.assert_allclose(st["chunk_score"][0], 0.7 + np.log(sizes), rtol=1e-14)
+    assert st["lse"][0] == pytest.approx(0.7 + np.log(float(V)), rel=1e-14)
     # equal chunk scores: the lowest chunk wins; equal in-chunk scores: lowest offset
-    st = sample_position(U[:, 0], E, W2t, np.array([-1]),
-                         -np.log([[64.0, 64.0, 22.0]]), np.zeros((1, 64)))
+    st = sample_position(U[:, 0], E, W2t, np.array([-1]), -np.log([sizes]), np.zeros((1, C)))
     assert st["token"][0] == 0
+    # a dominant chunk Gumbel picks that chunk; the in-chunk Gumbels pick the offset
+    gg = np.zeros((1, C))
+    gg[0, 5] = 1.0
+    st = sample_position(U[:, 0], E, W2t, np.array([-1]), np.array([[0.0, 50.0, 0.0]]), gg)
+    assert st["token"][0] == C + 5
 
 
-@pytest.mark.parametrize("with_bias", [False, True])
-def test_two_level_draw_follows_softmax(with_bias):
+@pytest.mark.parametrize("with_bias,C", [(False, 64), (True, 64), (True, 16)])
+def test_two_level_draw_follows_softmax(with_bias, C):
     """The sampled token follows p(v) = softmax(U + B)(v) (chi-square), over a
-    vocabulary of 200 = 3 full chunks and a ragged tail of 8."""
-    rng = np.random.default_rng(42 + with_bias)
+    vocabulary of 200 = 3 full chunks of 64 and a ragged tail of 8 (or 12
+    full chunks of 16 and a tail of 8)."""
+    rng = np.random.default_rng(42 + with_bias + C)
     V, r, R = 200, 6, 60000
     base = rng.normal(0, 1.0, size=V)
     base[17] += 3.0
@@ -95,8 +103,8 @@ def test_two_level_draw_follows_softmax(with_bias):
     p /= p.sum()
     U = np.broadcast_to(base, (R, 1, V)).copy()
     x0 = np.full(R, prev)
-    G = gumbels(rng, (R, 1, 4))
-    g = gumbels(rng, (R, 1, 64))
+    G = gumbels(rng, (R, 1, (V + C - 1) // C))
+    g = gumbels(rng, (R, 1, C))
     x = markov_sample(U, E, W2t, x0, G, g)["x"][:, 0]
     counts = np.bincount(x, minlength=V).astype(float)
     exp = R * p

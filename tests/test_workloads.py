@@ -38,7 +38,7 @@ def test_small_workload_shapes_and_determinism():
         np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
     assert a.U.shape == (1, 4, 1024) and a.U.dtype == np.float32
     assert a.target.shape == (1, 5, 1024)
-    assert a.G.shape == (1, 4, 16) and a.g.shape == (1, 4, 64)
+    assert a.G.shape == (4, 64, 1) and a.g.shape == (1, 4, 16)
     assert a.E.shape == (1024, 32) and a.W2t.shape == (1024, 32)
     assert a.w_conf.shape == (96,) and a.h.shape == (1, 4, 64)
     assert a.sps.shape == (8,) and np.all(np.diff(a.sps) <= 0)
@@ -55,7 +55,7 @@ def test_bf16_custom_workload_distributions():
     U = W.bf16_to_f32(a.U)
     # half of the positions carry a spike on top of N(0, 4)
     assert abs(float(np.std(U)) - 2.0) < 0.3
-    assert a.G.shape == (4, 3, 5)
+    assert a.G.shape == (3, 19, 4)
     np.testing.assert_allclose(a.T, [1.0, 1.5, 2.0])
     assert a.sps.shape[0] == w.R * (1 + w.gamma)
 
