@@ -32,8 +32,13 @@ __host__ __device__ constexpr int sample_reqs_per_wg() { return kTileWaves * 16 
 
 struct SampleWs {
   unsigned long long* keys;   // [gamma][kKeySlots][R]
+  unsigned int* bar;          // [0]: grid-barrier arrivals, [1]: barrier time-out flag
   float2* lsep;               // [gamma][R][nPart]  (M, S) log-sum-exp partials
 };
+// 64-bit words after the keys that sample_init also clears (the barrier words:
+// the top counter and time-out flag, then kBarGroups group counters 128 bytes apart)
+constexpr int kBarWords = 256;
+constexpr int kBarGroups = 8;
 
 // Token drawn at position k-1 (or the anchor at k = 0).
 __device__ __forceinline__ int previous_token(const unsigned long long* keys, const int32_t* x0, int R,
@@ -62,6 +67,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // drop out of every reduction without a per-element test.
 __device__ u32x4 kNegInfBf16x16[2] = {{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u},
                                             {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}};
+
+// A W1 row of zeros (r <= 256): the B operand when there is no previous token.
+__device__ __attribute__((aligned(16))) uint16_t kZeroRow[256] = {};
 
 // The bf16 logits of one lane's Gumbel chunk, tokens v .. v + 15 of `row`.
 // VEC (V a multiple of 16): the chunk lies wholly inside the row or wholly
@@ -166,8 +174,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
   constexpr int kW = tile_bytes(KS);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
   __shared__ float gsh[NROWS][kGChunk];        // in-chunk Gumbels of the group's requests
-  // each lane's best chunk per request group: [nb][mb][thread], flat
-  __shared__ f32x4 keepsh[NBW * 4 * kTileThreads];
+  // each lane's last two folded chunks per request group, one of them its
+  // best: [nb][slot][mb][thread], flat
+  __shared__ f32x4 keepsh[NBW * 2 * 4 * kTileThreads];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int j = lane & 15;
@@ -222,22 +231,27 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
   load_w1_frags<NBW, KS>(e, W1, prev);
 
   LaneDraw dr[NBW];
+  int bestSlot[NBW];   // which of the lane's two keep slots holds its best chunk
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     lane_draw_init(dr[nb]);
+    bestSlot[nb] = 0;
     *reinterpret_cast<f32x4*>(&gsh[loc[nb]][4 * q]) = gq[nb];
   }
   store_w2_tile_lane16<KS>(lds, wr);
   load_w2_regs<KS>(wr, W2t, V, tile_of(clampc(1)) * kChunk);
   __syncthreads();
 
-  // tile `it` from LDS half it & 1 and register set `cur`; refills `cur` with
-  // tile it + 2, then stores tile it + 1 into the other half and issues the
-  // W2t loads of tile it + 2
-  auto step = [&](int it, LaneLoads<NBW>& cur) {
-    const int v0 = tile_of(it) * kChunk;
-    f32x4 acc[4][NBW];
-    float Gc[NBW];
+  // Software pipeline: the products of tile `it` are formed while tile
+  // it - 1 is folded, so the matrix cores and the vector ALUs of a wave work
+  // on independent data.  accP holds the finished logits of the previous
+  // tile.
+  f32x4 accP[4][NBW];
+  float GcP[NBW];
+  int v0P = 0;
+  // products of tile `it` (LDS half it & 1, logits from register set `cur`,
+  // which is refilled with tile it + 2)
+  auto products = [&](int it, LaneLoads<NBW>& cur, f32x4 (&acc)[4][NBW], float (&Gc)[NBW]) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
 #pragma unroll
@@ -246,26 +260,54 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
     }
     load_lane(cur, clampc(it + 2));
     bias_tile_acc<NBW, KS>(acc, lds + (it & 1) * kW, e);
+  };
+  // fold the previous tile: its logits go to the free keep slot whatever
+  // happens, and the slot becomes the best one if the chunk wins (no branch)
+  auto fold_prev = [&]() {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
-      f32x4 a[4] = {acc[0][nb], acc[1][nb], acc[2][nb], acc[3][nb]};
-      if (fold_chunk(a, Gc[nb], v0 + q * kGChunk, dr[nb])) {
+      f32x4 a[4] = {accP[0][nb], accP[1][nb], accP[2][nb], accP[3][nb]};
+      const int freeSlot = bestSlot[nb] ^ 1;
+      f32x4* kp = keepsh + ((nb * 2 + freeSlot) * 4) * kTileThreads + threadIdx.x;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) keepsh[(nb * 4 + mb) * kTileThreads + threadIdx.x] = a[mb];
-      }
+      for (int mb = 0; mb < 4; ++mb) kp[mb * kTileThreads] = a[mb];
+      if (fold_chunk(a, GcP[nb], v0P + q * kGChunk, dr[nb])) bestSlot[nb] = freeSlot;
     }
+  };
+  // stores tile it + 1 into the other LDS half, issues the W2t loads of
+  // tile it + 2, and waits for every wave
+  auto advance = [&](int it) {
     store_w2_tile_lane16<KS>(lds + ((it + 1) & 1) * kW, wr);
     load_w2_regs<KS>(wr, W2t, V, tile_of(clampc(it + 2)) * kChunk);
     __syncthreads();
   };
+  auto body = [&](int it, LaneLoads<NBW>& cur) {
+    f32x4 accN[4][NBW];
+    float GcN[NBW];
+    products(it, cur, accN, GcN);
+    fold_prev();
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) accP[mb][nb] = accN[mb][nb];
+      GcP[nb] = GcN[nb];
+    }
+    v0P = tile_of(it) * kChunk;
+    advance(it);
+  };
+
+  products(0, even, accP, GcP);
+  v0P = tile_of(0) * kChunk;
+  advance(0);
   // pairs of tiles, so every path back to the loop head has issued both
   // register sets' loads in the same order; an odd last tile follows the loop
-  int it = 0;
+  int it = 1;
   for (; it + 1 < nT; it += 2) {
-    step(it, even);
-    step(it + 1, odd);
+    body(it, odd);
+    body(it + 1, even);
   }
-  if (it < nT) step(it, even);
+  if (it < nT) body(it, odd);
+  fold_prev();
 
   // the in-chunk draw on each lane's best chunk, then the best of the four
   // lanes of a request, merged across work groups by atomic max
@@ -275,7 +317,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
     float kept[kGChunk];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const f32x4 v = keepsh[(nb * 4 + mb) * kTileThreads + threadIdx.x];
+      const f32x4 v = keepsh[((nb * 2 + bestSlot[nb]) * 4 + mb) * kTileThreads + threadIdx.x];
 #pragma unroll
       for (int i = 0; i < 4; ++i) kept[4 * mb + i] = v[i];
     }
@@ -306,6 +348,352 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
       if (key != 0ull)
         atomicMax(ws.keys + (static_cast<int64_t>(k) * kKeySlots + blockIdx.x % kKeySlots) * R + req[nb], key);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide path: 32x32x16 MFMAs, two waves per SIMD at 128 requests.
+//
+// A work group of 2 RQ waves covers 32 RQ requests over 64-token tiles.  Wave
+// w takes token half th = w & 1 (tokens 32 th .. 32 th + 31 of the tile) and
+// request quarter rq = w >> 1 (requests 32 rq .. 32 rq + 31 of the group).
+// Lane (h, j) of the 32x32x16 output holds column j (a request) and rows
+// 8 g + 4 h + t (g, t = 0..3).  The tile rows are stored in LDS so that MFMA
+// row 8 g + 4 h + t of a half is its token 16 h + 4 g + t: the lane's sixteen
+// accumulators are its request's logits for the sixteen consecutive tokens
+// v0 + 32 th + 16 h + (0..15), one Gumbel chunk, and every reduction of the
+// chunk stays inside the lane.  Each wave reads only its half of the tile
+// (16 KB at r = 256) per tile, so the LDS traffic per tile is the same as
+// with four waves of 32 requests x 64 tokens, while two waves per SIMD let
+// one wave's vector work run under the other's matrix products.
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Stored LDS row of tile row (token offset) t: bits [th h g1 g0 t1 t0] ->
+// [th g1 g0 h t1 t0].
+__host__ __device__ constexpr int row32_of_token(int t) {
+  return (t & 32) | (((t >> 2) & 3) << 3) | (((t >> 4) & 1) << 2) | (t & 3);
+}
+
+template <int RQ>
+__host__ __device__ constexpr int wide_threads() { return 128 * RQ; }
+
+// The W2t tile (64 rows of r = 16 KS16 bf16) staged in registers: thread t
+// takes the 16-byte pieces t, t + T, ... of the tile's contiguous block.
+template <int KS16, int RQ>
+struct WideW {
+  static constexpr int P = 2 * KS16;   // 16-byte pieces per row
+  static constexpr int T = wide_threads<RQ>();
+  static constexpr int NP = (64 * P + T - 1) / T;
+  u32x4 w[NP];
+};
+
+template <int KS16, int RQ>
+__device__ __forceinline__ void wide_load_w(WideW<KS16, RQ>& st, const uint16_t* W2t, int V, int v0) {
+  constexpr int P = WideW<KS16, RQ>::P, T = WideW<KS16, RQ>::T;
+#pragma unroll
+  for (int n = 0; n < WideW<KS16, RQ>::NP; ++n) {
+    const int piece = n * T + static_cast<int>(threadIdx.x);
+    if ((64 * P) % T == 0 || piece < 64 * P) {   // only small r leaves threads idle (wave-uniform)
+      const int vrow = min(v0 + piece / P, V - 1);
+      st.w[n] = *reinterpret_cast<const u32x4*>(W2t + static_cast<int64_t>(vrow) * (KS16 * 16) + (piece % P) * 8);
+    }
+  }
+}
+
+// Rows go to row32_of_token(row); piece c of stored row s sits in slot
+// c ^ (s mod P), so the 32 rows one half-wave reads for an A fragment fall in
+// different bank groups.
+template <int KS16, int RQ>
+__device__ __forceinline__ void wide_store_w(uint8_t* tile, const WideW<KS16, RQ>& st) {
+  constexpr int P = WideW<KS16, RQ>::P, T = WideW<KS16, RQ>::T;
+#pragma unroll
+  for (int n = 0; n < WideW<KS16, RQ>::NP; ++n) {
+    const int piece = n * T + static_cast<int>(threadIdx.x);
+    if ((64 * P) % T == 0 || piece < 64 * P) {
+      const int srow = row32_of_token(piece / P);
+      const int slot = (piece % P) ^ (srow & (P - 1));
+      *reinterpret_cast<u32x4*>(tile + (srow * P + slot) * 16) = st.w[n];
+    }
+  }
+}
+
+// Grid-wide barrier between positions of the persistent kernel: every work
+// group of the launch is resident (one per compute unit, at most as many as
+// the device has), so a counter of arrivals suffices.  The key slots and the
+// counter are updated with system-scope atomics, which are performed in
+// memory rather than in the issuing die's L2, so no cache write-back is
+// needed to publish them; each wave waits for its own atomics to complete
+// before the work group arrives.  The wait is bounded: after kBarrierTicks of
+// the 100 MHz real-time clock the work group raises the time-out flag and
+// the launch ends early (sample_finalize then reports every token as -1), so
+// a grid that is not resident as a whole cannot hang.
+constexpr unsigned long long kBarrierTicks = 50000000ull;   // 0.5 s
+
+__device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int round, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's key atomics have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // two levels: work group b arrives at group counter b mod kBarGroups; the
+    // last arrival of a group arrives at the top counter, which everyone polls
+    const unsigned int nWG = gridDim.x * gridDim.y;
+    const unsigned int id = blockIdx.y * gridDim.x + blockIdx.x;
+    const unsigned int groups = nWG < kBarGroups ? nWG : kBarGroups;
+    const unsigned int grp = id % groups;
+    const unsigned int per = (nWG - grp + groups - 1) / groups;
+    const unsigned int old =
+        __hip_atomic_fetch_add(bar + 64 + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (old + 1 == round * per) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    int ok = 1;
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < round * groups) {
+      if (__hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u ||
+          __builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks) {
+        __hip_atomic_fetch_or(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// All gamma positions in one launch.  Position k + 1 needs the tokens drawn
+// at position k, so the work groups meet at a grid barrier between positions;
+// the loads that do not depend on the tokens (the next position's logits and
+// chunk Gumbels, its first two W2t tiles) are issued before the barrier and
+// land while it waits.  A work group walks its tiles in snake order (forward
+// on even positions, backward on odd ones), so the W2t tile it ends a
+// position with is the one it starts the next with.  Tiles are handed out in
+// pairs, so every work group has an even number of positions per sweep (a
+// phantom tile past the vocabulary, if the tile count is odd, reads -inf
+// logits and drops out) and the two register sets keep their roles across
+// positions.
+template <int RQ, int KS16, bool VEC>
+__global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
+    int R, int gamma, int V, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
+    const float* __restrict__ g, SampleWs ws, int nPart) {
+  static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
+  constexpr int T = wide_threads<RQ>();
+  constexpr int NROWS = 32 * RQ;
+  constexpr int P = 2 * KS16;
+  constexpr int kW = 64 * P * 16;   // tile bytes
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
+  __shared__ float gsh[NROWS][kGChunk];        // in-chunk Gumbels of the group's requests
+  __shared__ f32x4 keepsh[2 * 4 * T];          // each lane's last two folded chunks: [slot][quarter][thread]
+  __shared__ float2 lsh[NROWS];                // token half 1 -> token half 0 hand-over
+  __shared__ unsigned long long ksh[NROWS];
+  __shared__ int barflag;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int th = wave & 1;
+  const int rq = wave >> 1;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int loc = rq * 32 + j;
+  const int req = static_cast<int>(blockIdx.y) * NROWS + loc;
+  const bool live = req < R;
+  const int reqc = min(req, R - 1);
+  const int lofs = 32 * th + 16 * h;   // the lane's first token in a tile
+  const int nTiles = (V + kChunk - 1) / kChunk;
+  const int nG = (V + kGChunk - 1) / kGChunk;
+  const int nPairs = (nTiles + 1) / 2;
+  // the host launches at most one work group per tile pair, so nT >= 2
+  const int nT = 2 * ((nPairs - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                      static_cast<int>(gridDim.x));
+  // tile at sweep position p of position k (snake order over this group's pairs)
+  const auto tile_at = [&](int k, int p) {
+    const int q = (k & 1) ? nT - 1 - p : p;
+    return 2 * (static_cast<int>(blockIdx.x) + (q >> 1) * static_cast<int>(gridDim.x)) + (q & 1);
+  };
+  // a sweep position past the last belongs to the next position (the last
+  // position repeats its last tile)
+  const auto next_k = [&](int k, int p) { return p < nT ? k : (k + 1 < gamma ? k + 1 : k); };
+  const auto next_p = [&](int k, int p) { return p < nT ? p : (k + 1 < gamma ? p - nT : nT - 1); };
+
+  struct Lane {
+    u32x4 u[2];
+    float G;
+  };
+  auto load_lane = [&](Lane& ll, int k, int p) {
+    const int k2 = next_k(k, p), p2 = next_p(k, p);
+    const int t = tile_at(k2, p2);
+    const int64_t row = static_cast<int64_t>(reqc) * gamma + k2;
+    load_lane16<VEC>(ll.u, U + row * V, t * kChunk + lofs, V);
+    ll.G = G[(static_cast<int64_t>(k2) * nG + min(4 * t + 2 * th + h, nG - 1)) * R + reqc];
+  };
+  auto load_w = [&](WideW<KS16, RQ>& w, int k, int p) {
+    wide_load_w<KS16, RQ>(w, W2t, V, tile_at(next_k(k, p), next_p(k, p)) * kChunk);
+  };
+  // in-chunk Gumbels of position k: each of the request's four lanes brings four offsets
+  auto load_gq = [&](int k) {
+    return *reinterpret_cast<const f32x4*>(g + (static_cast<int64_t>(reqc) * gamma + k) * kGChunk + 8 * th + 4 * h);
+  };
+  // B operand: k-step ks takes elements 16 ks + 8 h .. + 7 of the W1 row, or
+  // of a row of zeros when there is no previous token (bias 0)
+  bf16x8 e[KS16];
+  auto load_e = [&](int prev) {
+    const uint16_t* w1row = (prev >= 0 ? W1 + static_cast<int64_t>(prev) * (KS16 * 16) : kZeroRow) + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS16; ++ks) e[ks] = load_bf16x8_global(w1row + 16 * ks);
+  };
+
+  WideW<KS16, RQ> wr;
+  Lane even, odd;
+  LaneDraw dr;
+  int bestSlot = 0;
+  f32x16 accP;
+  float GcP = 0.f;
+  int v0P = 0;
+
+  auto products = [&](int k, int p, Lane& cur, f32x16& acc, float& Gc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t w = cur.u[r >> 3][(r >> 1) & 3];
+      acc[r] = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    Gc = cur.G;
+    load_lane(cur, k, p + 2);
+    const uint8_t* tile = lds + (p & 1) * kW;
+    const int srow = 32 * th + j;
+    // A fragments in batches of eight reads ahead of their products; two
+    // accumulator chains (even and odd k-steps) keep the matrix pipe busy
+    constexpr int KB = KS16 < 8 ? KS16 : 8;
+    f32x16 acc2 = {};
+#pragma unroll
+    for (int k0 = 0; k0 < KS16; k0 += KB) {
+      bf16x8 a[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int slot = (2 * (k0 + kk) + h) ^ (srow & (P - 1));
+        a[kk] = *reinterpret_cast<const bf16x8*>(tile + (srow * P + slot) * 16);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        if (kk & 1)
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], e[k0 + kk], acc2, 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], e[k0 + kk], acc, 0, 0, 0);
+      }
+    }
+    acc += acc2;
+  };
+  // fold the previous tile: its logits go to the free keep slot whatever
+  // happens, and that slot becomes the best one if the chunk wins
+  auto fold_prev = [&]() {
+    f32x4 a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] = f32x4{accP[4 * m], accP[4 * m + 1], accP[4 * m + 2], accP[4 * m + 3]};
+    const int freeSlot = bestSlot ^ 1;
+    f32x4* kp = keepsh + freeSlot * 4 * T + threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kp[m * T] = a[m];
+    if (fold_chunk(a, GcP, v0P + lofs, dr)) bestSlot = freeSlot;
+  };
+  // stores the tile of sweep position p + 1 into the other LDS half, issues
+  // the W2t loads of position p + 2, and waits for every wave
+  auto advance = [&](int k, int p) {
+    wide_store_w<KS16, RQ>(lds + ((p + 1) & 1) * kW, wr);
+    load_w(wr, k, p + 2);
+    __syncthreads();
+  };
+  auto body = [&](int k, int p, Lane& cur) {
+    f32x16 accN;
+    float GcN;
+    products(k, p, cur, accN, GcN);
+    fold_prev();
+    accP = accN;
+    GcP = GcN;
+    v0P = tile_at(k, p) * kChunk;
+    advance(k, p);
+  };
+
+  // position 0: its previous token is the anchor
+  const int x0v = x0[reqc];
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 gq = load_gq(0);
+  load_w(wr, 0, 0);
+  load_lane(even, 0, 0);
+  load_lane(odd, 0, 1);
+  load_e(live ? token_or_none(x0v, V) : -1);
+  *reinterpret_cast<f32x4*>(&gsh[loc][8 * th + 4 * h]) = gq;
+  wide_store_w<KS16, RQ>(lds, wr);
+  load_w(wr, 0, 1);
+  __syncthreads();
+
+  for (int k = 0; k < gamma; ++k) {
+    lane_draw_init(dr);
+    bestSlot = 0;
+    products(k, 0, even, accP, GcP);
+    v0P = tile_at(k, 0) * kChunk;
+    advance(k, 0);
+    int p = 1;
+    for (; p + 1 < nT; p += 2) {
+      body(k, p, odd);
+      body(k, p + 1, even);
+    }
+    body(k, p, odd);   // nT is even: the last sweep position is odd
+    fold_prev();
+
+    // the in-chunk draw on the lane's best chunk
+    float bs = neg_inf();
+    int bo = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 v = keepsh[(bestSlot * 4 + m) * T + threadIdx.x];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = v[i] + gsh[loc][4 * m + i];
+        if (sc > bs) {
+          bs = sc;
+          bo = 4 * m + i;
+        }
+      }
+    }
+    unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
+    float M2 = dr.M2, Ts = dr.T;
+    // the request's two lanes in this wave (h = 0, 1), then its two waves
+    auto merge = [&](unsigned long long ok, float M2o, float To) {
+      key = ok > key ? ok : key;
+      const float Mn = fmaxf(M2, M2o);
+      Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);
+      M2 = Mn;
+    };
+    merge(__shfl_xor(key, 32), __shfl_xor(M2, 32), __shfl_xor(Ts, 32));
+    if (th == 1 && h == 0) {
+      lsh[loc] = make_float2(M2, Ts);
+      ksh[loc] = key;
+    }
+    __syncthreads();
+    if (th == 0 && h == 0 && live) {
+      const float2 o = lsh[loc];
+      merge(ksh[loc], o.x, o.y);
+      ws.lsep[(static_cast<int64_t>(k) * R + req) * nPart + blockIdx.x] = make_float2(M2 * kLn2, Ts);
+      if (key != 0ull)
+        __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * kKeySlots + blockIdx.x % kKeySlots) * R + req,
+                               key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (k + 1 == gamma) break;
+
+    // next position: its in-chunk Gumbels are fetched before the barrier; its
+    // logits and first two W2t tiles are already in flight
+    gq = load_gq(k + 1);
+    if (!grid_barrier(ws.bar, k + 1, &barflag)) return;
+    const unsigned long long* kp = ws.keys + static_cast<int64_t>(k) * kKeySlots * R + reqc;
+    unsigned long long best = 0;
+#pragma unroll
+    for (int sl = 0; sl < kKeySlots; ++sl) {
+      const unsigned long long v = __hip_atomic_load(kp + static_cast<int64_t>(sl) * R, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_SYSTEM);
+      best = v > best ? v : best;
+    }
+    load_e(live ? token_or_none(key_token(best), V) : -1);
+    *reinterpret_cast<f32x4*>(&gsh[loc][8 * th + 4 * h]) = gq;
+    __syncthreads();
   }
 }
 
@@ -382,6 +770,14 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   if (row >= static_cast<int64_t>(R) * gamma) return;
   const int req = static_cast<int>(row / gamma);
   const int k = static_cast<int>(row % gamma);
+  if (ws.bar[1] != 0u) {   // the persistent launch timed out at a grid barrier: no valid draw
+    if (lane == 0) {
+      x[row] = -1;
+      lse[row] = __builtin_nanf("");
+      logit[row] = __builtin_nanf("");
+    }
+    return;
+  }
   const int drawn = previous_token(ws.keys, x0, R, V, k + 1, req);
   const int tok = drawn < 0 ? 0 : drawn;   // every position draws a token in [0, V)
   const int prev = previous_token(ws.keys, x0, R, V, k, req);
@@ -415,22 +811,39 @@ int sample_parts(dspark_dtype dt, int V) {
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+static size_t cleared_words(int R, int gamma) {   // keys + barrier words, cleared per call
+  return static_cast<size_t>(kKeySlots) * R * gamma + kBarWords;
+}
 size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V) {
-  return align256(sizeof(unsigned long long) * kKeySlots * static_cast<size_t>(R) * gamma) +
+  return align256(sizeof(unsigned long long) * cleared_words(R, gamma)) +
          sizeof(float2) * static_cast<size_t>(gamma) * R * sample_parts(dt, V);
 }
 
 static SampleWs carve(void* ws, int R, int gamma) {
   SampleWs w;
   w.keys = static_cast<unsigned long long*>(ws);
-  w.lsep = reinterpret_cast<float2*>(static_cast<char*>(ws) +
-                                     align256(sizeof(unsigned long long) * kKeySlots * static_cast<size_t>(R) * gamma));
+  w.bar = reinterpret_cast<unsigned int*>(w.keys + static_cast<size_t>(kKeySlots) * R * gamma);
+  w.lsep = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(sizeof(unsigned long long) * cleared_words(R, gamma)));
   return w;
 }
 
 // Request groups of 64 (R <= 64) or 128 rows; one work group per compute
 // unit across all groups.
 static int sample_nbw(int R) { return R <= 64 ? 1 : 2; }
+// Batches above 32 requests take the 32x32x16 path (groups of 64 or 128
+// requests, the same group sizes as the 16x16x32 path's).
+static bool sample_wide(int R) { return R > 32; }
+
+// Work groups along the vocabulary for the persistent 32x32x16 path: one
+// per compute unit across all request groups, and at most one per tile pair,
+// so the whole grid is resident at once (the grid barrier needs it).  0 when
+// the request groups alone outnumber the compute units.
+static int wide_grid_x(int R, int V) {
+  const int groups = ceil_div(R, R <= 64 ? 64 : 128);
+  const int gx = compute_units() / groups;
+  const int nPairs = ceil_div(ceil_div(V, kChunk), 2);
+  return gx < 1 ? 0 : (gx < nPairs ? gx : nPairs);
+}
 
 static int bf16_grid_x(int R, int V) {
   const int groups = ceil_div(R, kTileWaves * 16 * sample_nbw(R));
@@ -450,6 +863,30 @@ static void launch_step_bf16(int R, int gamma, int V, int k, const void* U, cons
   hipLaunchKernelGGL((sample_step_bf16<NBW, KS, VEC>), grid, dim3(kTileThreads), 0, s, R, gamma, V, k,
                      static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
                      static_cast<const uint16_t*>(W2t), x0, G, g, w, gx);
+}
+
+template <int RQ, int KS16, bool VEC>
+static void launch_steps_wide(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
+                              const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
+                              hipStream_t s) {
+  dim3 grid(gx, ceil_div(R, 32 * RQ));
+  hipLaunchKernelGGL((sample_steps_wide<RQ, KS16, VEC>), grid, dim3(wide_threads<RQ>()), 0, s, R, gamma, V,
+                     static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
+                     static_cast<const uint16_t*>(W2t), x0, G, g, w, gx);
+}
+
+template <int KS16>
+static void launch_steps_wide_ks(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
+                                 const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
+                                 hipStream_t s) {
+  const bool vec = (V % kGChunk) == 0;
+  if (R <= 64) {
+    if (vec) launch_steps_wide<2, KS16, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
+    else launch_steps_wide<2, KS16, false>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
+  } else {
+    if (vec) launch_steps_wide<4, KS16, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
+    else launch_steps_wide<4, KS16, false>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
+  }
 }
 
 template <int KS>
@@ -473,19 +910,31 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
                          hipStream_t s) {
   const SampleWs w = carve(ws, R, gamma);
-  const int nPart = dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
-  const int64_t nkeys = static_cast<int64_t>(kKeySlots) * R * gamma;
+  const int gxw = dt == DSPARK_BF16 && sample_wide(R) ? wide_grid_x(R, V) : 0;
+  const int nPart = gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
+  const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
   hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys, 256) < 1024 ? ceil_div(nkeys, 256) : 1024),
                      dim3(256), 0, s, w.keys, nkeys);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  for (int k = 0; k < gamma; ++k) {
+  if (gxw > 0) {
+    switch (r / 32) {
+      case 1: launch_steps_wide_ks<2>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
+      case 2: launch_steps_wide_ks<4>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
+      case 4: launch_steps_wide_ks<8>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
+      default: launch_steps_wide_ks<16>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  for (int k = 0; k < gamma && gxw == 0; ++k) {
     if (dt == DSPARK_BF16) {
-      switch (r / 32) {
-        case 1: launch_step_bf16_ks<1>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-        case 2: launch_step_bf16_ks<2>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-        case 4: launch_step_bf16_ks<4>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-        default: launch_step_bf16_ks<8>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
+      {
+        switch (r / 32) {
+          case 1: launch_step_bf16_ks<1>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
+          case 2: launch_step_bf16_ks<2>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
+          case 4: launch_step_bf16_ks<4>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
+          default: launch_step_bf16_ks<8>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
+        }
       }
     } else {
       hipLaunchKernelGGL(sample_step_f32, dim3(nPart, R), dim3(64), 0, s, R, gamma, V, r, k,
