@@ -10,8 +10,12 @@
 //      request);
 //   2. ranking: each slot gets a 64-bit key ((2^50 - a_fx) << 13) | (r*gamma + j)
 //      so that ascending keys are descending a_fx, then ascending request,
-//      then ascending position, and the keys are sorted by a bitonic network;
-//      slots with a_fx = 0 sort after every candidate;
+//      then ascending position; slots with a_fx = 0 sort after every
+//      candidate.  Survival never increases along a request, so each
+//      request's keys already form a sorted run, and the ranking is a merge
+//      of R runs: ceil(log2 R) levels of pairwise merges in which every key
+//      finds its place by one binary search in the partner run (keys are
+//      distinct);
 //   3. tau_fx(m) = R 2^50 + the exact integer prefix sum of the ranked a_fx;
 //   4. the first m with Theta(m) <= Theta(m-1) (exact comparison of
 //      tau_fx(m) * SPS(R+m) with tau_fx(m-1) * SPS(R+m-1)) gives A = m - 1;
@@ -23,7 +27,7 @@
 namespace dspark {
 
 constexpr int kSchedThreads = 1024;
-constexpr int kSchedMaxSlots = 8192;    // keys in LDS: 8192 * 8 bytes = 64 KiB
+constexpr int kSchedMaxSlots = 8192;    // keys in LDS: two buffers of 8192 * 8 bytes = 128 KiB
 constexpr int kQ = 50;
 constexpr uint64_t kOne = 1ull << kQ;
 
@@ -83,44 +87,86 @@ __device__ int cmp_products(uint64_t t1, double d1, uint64_t t2, double d2) {
   return cmp128(p1, p2);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamma, int P,
+// The same sign, decided in double precision when the two products are
+// clearly apart (each is within 2^-52 relative of its exact value, so a gap
+// above 2^-40 of the larger cannot be a rounding artefact) and exactly
+// otherwise.
+__device__ int cmp_theta(uint64_t t1, double d1, uint64_t t2, double d2) {
+  const double p1 = static_cast<double>(t1) * d1, p2 = static_cast<double>(t2) * d2;
+  const double diff = p1 - p2;
+  if (fabs(diff) > fmax(p1, p2) * 0x1p-40) return diff > 0 ? 1 : -1;
+  return cmp_products(t1, d1, t2, d2);
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamma,
                                                                  const float* __restrict__ c,
                                                                  const double* __restrict__ sps,
                                                                  int32_t* __restrict__ ell,
                                                                  int32_t* __restrict__ admitted,
                                                                  double* __restrict__ theta_best) {
-  extern __shared__ uint64_t keys[];   // P entries; reused for the scan afterwards
+  __shared__ uint64_t lds_keys[2 * kSchedMaxSlots];   // two buffers of n keys; reused for the scan afterwards
   const int tid = threadIdx.x;
   const int n = R * gamma;
 
-  // 1-2: keys in LDS (one thread per request walks its positions in order)
+  // 1-2: the confidences go to LDS in one coalesced pass (through the
+  // second key buffer, free until the first merge), then one thread per
+  // request walks its positions in order and writes the keys
+  uint64_t* keys = lds_keys;
+  uint64_t* other = lds_keys + n;
+  float* cl = reinterpret_cast<float*>(other);
+  for (int i = tid; i < n; i += kSchedThreads) cl[i] = c[i];
+  for (int req = tid; req < R; req += kSchedThreads) ell[req] = 0;
+  __syncthreads();
   for (int req = tid; req < R; req += kSchedThreads) {
     double s = 1.0;
     for (int j = 0; j < gamma; ++j) {
-      s = s * static_cast<double>(c[static_cast<int64_t>(req) * gamma + j]);
+      s = s * static_cast<double>(cl[req * gamma + j]);
       const uint64_t afx = static_cast<uint64_t>(floor(s * static_cast<double>(kOne)));
       keys[req * gamma + j] = ((kOne - afx) << 13) | static_cast<uint64_t>(req * gamma + j);
     }
   }
-  for (int i = n + tid; i < P; i += kSchedThreads) keys[i] = ~0ull;
   __syncthreads();
 
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = tid; i < P; i += kSchedThreads) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const uint64_t a = keys[i], b = keys[ixj];
-          const bool up = (i & kk) == 0;
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[ixj] = a;
-          }
+  // merge levels: runs of length L = gamma 2^l are merged in pairs; a key's
+  // place in its partner run is a fixed-depth binary descent, two keys per
+  // thread side by side
+  for (int L = gamma; L < n; L <<= 1) {
+    int top = 1;
+    while ((top << 1) <= L) top <<= 1;   // highest power of two <= L
+    for (int i0 = tid; i0 < n; i0 += 2 * kSchedThreads) {
+      int idx[2], part0[2], plen[2], pos[2], dst[2];
+      uint64_t key[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = i0 + e * kSchedThreads;
+        const int ii = i < n ? i : n - 1;
+        const int run = ii / L;
+        const int a0 = (run & ~1) * L;               // start of the merged pair
+        part0[e] = (run & 1) ? a0 : a0 + L;          // start of the partner run
+        const int rest = n - part0[e];
+        plen[e] = (run & 1) ? L : (rest < L ? (rest > 0 ? rest : 0) : L);
+        idx[e] = i;
+        key[e] = keys[ii];
+        dst[e] = a0 + (ii - run * L);
+        pos[e] = 0;
+      }
+      for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int q = pos[e] + step;
+          if (q <= plen[e] && keys[part0[e] + q - 1] < key[e]) pos[e] = q;
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        if (idx[e] < n) other[dst[e] + pos[e]] = key[e];
     }
+    __syncthreads();
+    uint64_t* t = keys;
+    keys = other;
+    other = t;
   }
+  const int P = n;   // ranked keys: keys[0 .. n)
 
   // 3: thread t owns ranked positions [t*8, t*8+8)
   constexpr int kPer = kSchedMaxSlots / kSchedThreads;   // 8
@@ -134,21 +180,32 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
     if (myk[t] < cand_limit) local += kOne - (myk[t] >> 13);
   }
   __syncthreads();                     // keys now live in registers
-  uint64_t* part = keys;               // kSchedThreads entries
-  int* sh = reinterpret_cast<int*>(keys + kSchedThreads);   // scalars
-  part[tid] = local;
+  // exclusive prefix of the per-thread sums: a scan inside each wave, then
+  // one pass over the wave totals
+  uint64_t incl = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint64_t v = __shfl_up(incl, o);
+    if ((tid & (kWave - 1)) >= o) incl += v;
+  }
+  constexpr int kWaves = kSchedThreads / kWave;
+  uint64_t* wsum = keys;                                     // kWaves entries
+  int* sh = reinterpret_cast<int*>(keys + kWaves);           // scalars
+  if ((tid & (kWave - 1)) == kWave - 1) wsum[tid / kWave] = incl;
   if (tid == 0) {
     sh[0] = 0x7FFFFFFF;                // first drop position m
     sh[1] = 0;                         // candidate count M
   }
   __syncthreads();
-  for (int o = 1; o < kSchedThreads; o <<= 1) {     // inclusive scan of the partials
-    const uint64_t v = (tid >= o) ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  uint64_t before = 0, total = 0;
+#pragma unroll
+  for (int wv = 0; wv < kWaves; ++wv) {
+    const uint64_t v = wsum[wv];
+    before += wv < tid / kWave ? v : 0;
+    total += v;
   }
-  uint64_t tau_prev = static_cast<uint64_t>(R) * kOne + (tid > 0 ? part[tid - 1] : 0);
+  const uint64_t excl = before + incl - local;   // sum of the ranked values before this thread's
+  uint64_t tau_prev = static_cast<uint64_t>(R) * kOne + excl;
   int my_first_drop = 0x7FFFFFFF;
   int my_count = 0;
 #pragma unroll
@@ -158,7 +215,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
     const int m = tid * kPer + t + 1;               // admitting the m-th ranked slot
     const uint64_t tau = tau_prev + (kOne - (myk[t] >> 13));
     if (my_first_drop == 0x7FFFFFFF &&
-        cmp_products(tau, sps[R + m - 1], tau_prev, sps[R + m - 2]) <= 0)
+        cmp_theta(tau, sps[R + m - 1], tau_prev, sps[R + m - 2]) <= 0)
       my_first_drop = m;
     tau_prev = tau;
   }
@@ -176,7 +233,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
     for (int t = 0; t < kPer; ++t)
       if (tid * kPer + t == A) v = myk[t];
     thr[0] = v;
-    thr[1] = static_cast<uint64_t>(R) * kOne + (tid > 0 ? part[tid - 1] : 0);
+    thr[1] = static_cast<uint64_t>(R) * kOne + excl;
     uint64_t tauA = thr[1];
 #pragma unroll
     for (int t = 0; t < kPer; ++t)
@@ -185,22 +242,21 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
   }
   if (A == kSchedThreads * kPer && tid == 0) {   // every slot admitted (P = 8192)
     thr[0] = ~0ull;
-    thr[1] = static_cast<uint64_t>(R) * kOne + part[kSchedThreads - 1];
+    thr[1] = static_cast<uint64_t>(R) * kOne + total;
   }
   __syncthreads();
   const uint64_t threshold = thr[0];
 
-  // 5: lengths by recount (the ranked prefix is prefix-closed per request)
-  for (int req = tid; req < R; req += kSchedThreads) {
-    double s = 1.0;
-    int cnt = 0;
-    for (int j = 0; j < gamma; ++j) {
-      s = s * static_cast<double>(c[static_cast<int64_t>(req) * gamma + j]);
-      const uint64_t afx = static_cast<uint64_t>(floor(s * static_cast<double>(kOne)));
-      const uint64_t key = ((kOne - afx) << 13) | static_cast<uint64_t>(req * gamma + j);
-      if (afx > 0 && key < threshold) ++cnt;
+  // 5: lengths from the admitted ranked slots: the ranked prefix is
+  // prefix-closed per request, so l_r is one more than the largest admitted
+  // position of request r
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int p = tid * kPer + t;
+    if (p < A && myk[t] < threshold) {
+      const int slot = static_cast<int>(myk[t] & 0x1FFF);
+      atomicMax(ell + slot / gamma, slot % gamma + 1);
     }
-    ell[req] = cnt;
   }
   if (tid == 0) {
     if (admitted) admitted[0] = A;
@@ -210,21 +266,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
 
 size_t schedule_workspace_bytes() { return 0; }
 
-int schedule_pow2(int n) {
-  int P = 1;
-  while (P < n) P <<= 1;
-  return P < 2 ? 2 : P;
-}
-
 hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int32_t* ell,
                            int32_t* admitted, double* theta_best, hipStream_t s) {
-  const int P = schedule_pow2(R * gamma);
-  // LDS holds max(P keys, 1024 partial sums + scalars)
-  size_t lds = static_cast<size_t>(P) * sizeof(uint64_t);
-  const size_t need_scan = kSchedThreads * sizeof(uint64_t) + 64;
-  if (lds < need_scan) lds = need_scan;
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), lds, s, R, gamma, P, c, sps, ell,
-                     admitted, theta_best);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, R, gamma, c, sps, ell, admitted,
+                     theta_best);
   return hipGetLastError();
 }
 
