@@ -120,6 +120,6 @@ __device__ __forceinline__ float wave_inclusive_scan(float v) {
   return v;
 }
 
-inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+__host__ __device__ inline int ceil_div(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
 }  // namespace dspark

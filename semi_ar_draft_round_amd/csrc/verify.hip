@@ -7,10 +7,12 @@
 // section 四 steps 5-6 (row i of the target logits predicts draft i).
 //
 // Four launches:
-//   verify_target_lse   one work group per needed target row (rows 0..l_r of
-//                       request r): its log-normaliser, and the target logit
-//                       of the drafted token on rows below l_r;
-//   verify_accept       one thread per request: the first i with
+//   verify_target_part  the needed target rows (rows 0..l_r of request r),
+//                       each split into parts along the vocabulary: (max,
+//                       sum) parts of the log-normaliser, and the target
+//                       logit of the drafted token on rows below l_r;
+//   verify_accept       one wave per request: the parts merged into each
+//                       row's log-normaliser, then the first i with
 //                       ln u_acc >= ln p_t(x_i) - ln p_d(x_i) -> n_acc;
 //   verify_residual_*   the residual row of every request in one pass over
 //                       the vocabulary: p_d is rebuilt from U and the Markov
@@ -63,69 +65,113 @@ __device__ __forceinline__ Lse block_reduce_lse(Lse a, Lse* sh) {
   return r;
 }
 
+// Target rows are split along the vocabulary into kLseSplits parts; a work
+// group takes (row, part) items in grid-stride order and skips the rows no
+// request needs (i > l_r).  Each thread keeps four 16-byte loads in flight.
+// Part 0 of a draft row also fetches the target logit of the drafted token.
+constexpr int kLseSplits = 8;
+constexpr int kLseThreads = 256;
+constexpr int kLseUnroll = 4;
+
 template <typename Elt>
-__global__ __launch_bounds__(256) void verify_target_lse(int R, int gamma, int V,
-                                                         const typename Elt::T* __restrict__ target,
-                                                         const int32_t* __restrict__ row0,
-                                                         const int32_t* __restrict__ x,
-                                                         const int32_t* __restrict__ ell,
-                                                         float* __restrict__ lse_t, float* __restrict__ tx) {
-  __shared__ Lse sh[4];
-  const int r = blockIdx.x / (gamma + 1);
-  const int i = blockIdx.x % (gamma + 1);
-  const int L = min(max(ell[r], 0), gamma);
-  if (i > L) return;
-  const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + i : static_cast<int64_t>(r) * (gamma + 1) + i;
-  const typename Elt::T* t = target + row * V;
+__global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gamma, int V,
+                                                                  const typename Elt::T* __restrict__ target,
+                                                                  const int32_t* __restrict__ row0,
+                                                                  const int32_t* __restrict__ x,
+                                                                  const int32_t* __restrict__ ell,
+                                                                  float2* __restrict__ part, float* __restrict__ tx) {
+  __shared__ Lse sh[kLseThreads / kWave];
   constexpr int N = RowVec<Elt>::N;
-  Lse acc{neg_inf(), 0.f};
-  if ((V % N) == 0) {
-    for (int v = threadIdx.x * N; v < V; v += 256 * N) {
-      float e[N];
-      RowVec<Elt>::load(t + v, e);
-      float m = e[0];
+  const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
+  const int span = ceil_div(ceil_div(V, kLseSplits), N * kLseThreads) * N * kLseThreads;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int sp = static_cast<int>(it % kLseSplits);
+    const int64_t ri = it / kLseSplits;
+    const int r = static_cast<int>(ri / (gamma + 1));
+    const int i = static_cast<int>(ri % (gamma + 1));
+    const int L = min(max(ell[r], 0), gamma);
+    if (i > L) continue;   // uniform across the work group
+    const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + i : static_cast<int64_t>(r) * (gamma + 1) + i;
+    const typename Elt::T* t = target + row * V;
+    const int v0 = sp * span;
+    const int v1 = min(v0 + span, V);
+    Lse acc{neg_inf(), 0.f};
+    if ((V % N) == 0) {
+      for (int vb = v0 + static_cast<int>(threadIdx.x) * N; vb < v1; vb += kLseUnroll * N * kLseThreads) {
+        float e[kLseUnroll][N];
 #pragma unroll
-      for (int u = 1; u < N; ++u) m = fmaxf(m, e[u]);
-      float s = 0.f;
+        for (int u = 0; u < kLseUnroll; ++u) {
+          const int v = vb + u * N * kLseThreads;
+          RowVec<Elt>::load(t + (v < v1 ? v : v0), e[u]);
+        }
 #pragma unroll
-      for (int u = 0; u < N; ++u) s += __expf(e[u] - m);
-      acc = lse_combine(acc, Lse{m, s});
+        for (int u = 0; u < kLseUnroll; ++u) {
+          if (vb + u * N * kLseThreads >= v1) break;
+          float m = e[u][0];
+#pragma unroll
+          for (int q = 1; q < N; ++q) m = fmaxf(m, e[u][q]);
+          float sum = 0.f;
+#pragma unroll
+          for (int q = 0; q < N; ++q) sum += __expf(e[u][q] - m);
+          acc = lse_combine(acc, Lse{m, sum});
+        }
+      }
+    } else {
+      for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kLseThreads)
+        acc = lse_combine(acc, Lse{Elt::load(t, v), 1.f});
     }
-  } else {
-    for (int v = threadIdx.x; v < V; v += 256) acc = lse_combine(acc, Lse{Elt::load(t, v), 1.f});
-  }
-  acc = block_reduce_lse(acc, sh);
-  if (threadIdx.x == 0) {
-    lse_t[static_cast<int64_t>(r) * (gamma + 1) + i] = acc.M + logf(acc.S);
-    if (i < L) {
-      const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
-      tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
+    acc = block_reduce_lse(acc, sh);
+    if (threadIdx.x == 0) {
+      part[ri * kLseSplits + sp] = make_float2(acc.M, acc.S);
+      if (sp == 0 && i < L) {
+        const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
+        tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
+      }
     }
+    __syncthreads();   // sh is reused by the next item
   }
 }
 
 // ------------------------------------------------------------------- accept
 
+// One wave per request: lane i merges the parts of target row i into its
+// log-normaliser (rows 0..l_r), evaluates the accept test of draft i, and the
+// first failing draft, found by a ballot, ends the accepted prefix.
 __global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int32_t* __restrict__ ell,
+                                                     const float2* __restrict__ part,
                                                      const float* __restrict__ tx,
-                                                     const float* __restrict__ lse_t,
                                                      const float* __restrict__ logit,
                                                      const float* __restrict__ lse,
                                                      const float* __restrict__ u_acc,
-                                                     int32_t* __restrict__ n_acc) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
+                                                     float* __restrict__ lse_t, int32_t* __restrict__ n_acc) {
+  const int r = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (r >= R) return;
   const int L = min(max(ell[r], 0), gamma);
-  int n = L;
-  for (int i = 0; i < L; ++i) {
-    const int64_t o = static_cast<int64_t>(r) * gamma + i;
-    const float log_ratio = (tx[o] - lse_t[static_cast<int64_t>(r) * (gamma + 1) + i]) - (logit[o] - lse[o]);
-    if (!(logf(u_acc[o]) < log_ratio)) {
-      n = i;
-      break;
+  int first_fail = L;
+  for (int i0 = 0; i0 <= L; i0 += kWave) {   // gamma <= 64: at most two passes
+    const int i = i0 + lane;
+    bool fail = false;
+    if (i <= L) {
+      const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + i;
+      Lse acc{neg_inf(), 0.f};
+#pragma unroll
+      for (int sp = 0; sp < kLseSplits; ++sp) {
+        const float2 pv = part[ri * kLseSplits + sp];
+        acc = lse_combine(acc, Lse{pv.x, pv.y});
+      }
+      const float lt = acc.M + logf(acc.S);
+      lse_t[ri] = lt;
+      if (i < L) {
+        const int64_t o = static_cast<int64_t>(r) * gamma + i;
+        const float log_ratio = (tx[o] - lt) - (logit[o] - lse[o]);
+        fail = !(logf(u_acc[o]) < log_ratio);
+      }
     }
+    const unsigned long long b = __ballot(fail);
+    if (b != 0ull && first_fail == L) first_fail = i0 + __ffsll(static_cast<long long>(b)) - 1;
   }
-  n_acc[r] = n;
+  if (lane == 0) n_acc[r] = first_fail;
 }
 
 // ------------------------------------------------------- residual chunk masses
@@ -423,6 +469,7 @@ __global__ __launch_bounds__(256) void verify_select(
 
 struct VerifyWs {
   float* lse_t;   // [R][gamma+1]
+  float2* part;   // [R][gamma+1][kLseSplits] (max, sum) parts of the target log-normalisers
   float* tx;      // [R][gamma]
   float* csum;    // [R][nC]
   float* psum;    // [R][nC]
@@ -432,8 +479,8 @@ static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 
 size_t verify_workspace_bytes(int R, int gamma, int V) {
   const size_t nC = static_cast<size_t>(ceil_div(V, kChunk));
-  return align256(sizeof(float) * R * (gamma + 1)) + align256(sizeof(float) * R * gamma) +
-         2 * align256(sizeof(float) * R * nC);
+  return align256(sizeof(float) * R * (gamma + 1)) + align256(sizeof(float2) * R * (gamma + 1) * kLseSplits) +
+         align256(sizeof(float) * R * gamma) + 2 * align256(sizeof(float) * R * nC);
 }
 
 static VerifyWs carve(void* ws, int R, int gamma, int V) {
@@ -442,6 +489,8 @@ static VerifyWs carve(void* ws, int R, int gamma, int V) {
   VerifyWs w;
   w.lse_t = reinterpret_cast<float*>(p);
   p += align256(sizeof(float) * R * (gamma + 1));
+  w.part = reinterpret_cast<float2*>(p);
+  p += align256(sizeof(float2) * R * (gamma + 1) * kLseSplits);
   w.tx = reinterpret_cast<float*>(p);
   p += align256(sizeof(float) * R * gamma);
   w.csum = reinterpret_cast<float*>(p);
@@ -493,15 +542,17 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   const VerifyWs w = carve(ws, R, gamma, V);
   const int nC = ceil_div(V, kChunk);
   hipError_t err;
+  const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
+  const int gridp = static_cast<int>(items < 4LL * compute_units() ? items : 4LL * compute_units());
   if (dt == DSPARK_BF16)
-    hipLaunchKernelGGL(verify_target_lse<BF16>, dim3(R * (gamma + 1)), dim3(256), 0, s, R, gamma, V,
-                       static_cast<const uint16_t*>(target), row0, x, ell, w.lse_t, w.tx);
+    hipLaunchKernelGGL(verify_target_part<BF16>, dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, x, ell, w.part, w.tx);
   else
-    hipLaunchKernelGGL(verify_target_lse<F32>, dim3(R * (gamma + 1)), dim3(256), 0, s, R, gamma, V,
-                       static_cast<const float*>(target), row0, x, ell, w.lse_t, w.tx);
+    hipLaunchKernelGGL(verify_target_part<F32>, dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
+                       static_cast<const float*>(target), row0, x, ell, w.part, w.tx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(verify_accept, dim3(ceil_div(R, 256)), dim3(256), 0, s, R, gamma, ell, w.tx, w.lse_t,
-                     logit, lse, u_acc, n_acc);
+  hipLaunchKernelGGL(verify_accept, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, ell, w.part, w.tx, logit, lse,
+                     u_acc, w.lse_t, n_acc);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (dt == DSPARK_BF16) {
     switch (r / 32) {
