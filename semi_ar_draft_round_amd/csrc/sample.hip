@@ -401,9 +401,15 @@ __device__ __forceinline__ void wide_load_w(WideW<KS16, RQ>& st, const uint16_t*
   }
 }
 
-// Rows go to row32_of_token(row); piece c of stored row s sits in slot
-// c ^ (s mod P), so the 32 rows one half-wave reads for an A fragment fall in
-// different bank groups.
+// Rows go to row32_of_token(row), at a stride of P + 1 pieces: the padding
+// piece puts the rows one half-wave reads for an A fragment (consecutive
+// stored rows, same piece) in different bank groups, and a fragment's
+// address is the lane's row base plus a constant offset per k-step.
+template <int KS16>
+__host__ __device__ constexpr int wide_row_pieces() { return 2 * KS16 + 1; }
+template <int KS16>
+__host__ __device__ constexpr int wide_tile_bytes() { return 64 * wide_row_pieces<KS16>() * 16; }
+
 template <int KS16, int RQ>
 __device__ __forceinline__ void wide_store_w(uint8_t* tile, const WideW<KS16, RQ>& st) {
   constexpr int P = WideW<KS16, RQ>::P, T = WideW<KS16, RQ>::T;
@@ -412,8 +418,7 @@ __device__ __forceinline__ void wide_store_w(uint8_t* tile, const WideW<KS16, RQ
     const int piece = n * T + static_cast<int>(threadIdx.x);
     if ((64 * P) % T == 0 || piece < 64 * P) {
       const int srow = row32_of_token(piece / P);
-      const int slot = (piece % P) ^ (srow & (P - 1));
-      *reinterpret_cast<u32x4*>(tile + (srow * P + slot) * 16) = st.w[n];
+      *reinterpret_cast<u32x4*>(tile + (srow * wide_row_pieces<KS16>() + piece % P) * 16) = st.w[n];
     }
   }
 }
@@ -480,8 +485,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
   constexpr int T = wide_threads<RQ>();
   constexpr int NROWS = 32 * RQ;
-  constexpr int P = 2 * KS16;
-  constexpr int kW = 64 * P * 16;   // tile bytes
+  constexpr int kW = wide_tile_bytes<KS16>();   // tile bytes (padded rows)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
   __shared__ float gsh[NROWS][kGChunk];        // in-chunk Gumbels of the group's requests
   __shared__ f32x4 keepsh[2 * 4 * T];          // each lane's last two folded chunks: [slot][quarter][thread]
@@ -558,8 +562,8 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     }
     Gc = cur.G;
     load_lane(cur, k, p + 2);
-    const uint8_t* tile = lds + (p & 1) * kW;
-    const int srow = 32 * th + j;
+    // the lane's A rows: stored row 32 th + j, piece 2 ks + h at k-step ks
+    const uint8_t* arow = lds + (p & 1) * kW + ((32 * th + j) * wide_row_pieces<KS16>() + h) * 16;
     // A fragments in batches of eight reads ahead of their products; two
     // accumulator chains (even and odd k-steps) keep the matrix pipe busy
     constexpr int KB = KS16 < 8 ? KS16 : 8;
@@ -568,10 +572,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     for (int k0 = 0; k0 < KS16; k0 += KB) {
       bf16x8 a[KB];
 #pragma unroll
-      for (int kk = 0; kk < KB; ++kk) {
-        const int slot = (2 * (k0 + kk) + h) ^ (srow & (P - 1));
-        a[kk] = *reinterpret_cast<const bf16x8*>(tile + (srow * P + slot) * 16);
-      }
+      for (int kk = 0; kk < KB; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(arow + (k0 + kk) * 32);
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
         if (kk & 1)
