@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-requests", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only copy a buffer of this many MiB a few times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build measures the per-GPU hot path; "
@@ -99,6 +102,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_probe_mib} MiB three times")
+        return
     from semi_ar_draft_round_amd import binding, workloads as W
     from semi_ar_draft_round_amd import device_round as DR
 
