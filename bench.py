@@ -31,11 +31,12 @@ def log(*a):
 
 
 def source_hash() -> str:
+    """Hash of the sources the sampling launch is built from."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "semi_ar_draft_round_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for rel in ("semi_ar_draft_round_amd/csrc/sample.hip", "semi_ar_draft_round_amd/csrc/bias_tile.hpp",
+                "semi_ar_draft_round_amd/csrc/common.hpp", "include/dspark.h"):
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(rel.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
