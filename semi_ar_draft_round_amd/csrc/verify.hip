@@ -65,13 +65,64 @@ __device__ __forceinline__ Lse block_reduce_lse(Lse a, Lse* sh) {
   return r;
 }
 
-// Target rows are split along the vocabulary into kLseSplits parts; a work
-// group takes (row, part) items in grid-stride order and skips the rows no
-// request needs (i > l_r).  Each thread keeps four 16-byte loads in flight.
-// Part 0 of a draft row also fetches the target logit of the drafted token.
+// Target rows are split along the vocabulary into kLseSplits parts.  Only
+// rows 0..l_r of request r are needed, so every work group first builds the
+// prefix of the needed-row counts (for up to kLseCompactR requests) and
+// deals the needed (row, part) items out evenly: item a goes to work group
+// a mod gridDim.  Larger batches walk every (row, part) item and skip the
+// unneeded ones.  Each thread keeps kLseUnroll 16-byte loads in flight; part
+// 0 of a draft row also fetches the target logit of the drafted token.
 constexpr int kLseSplits = 8;
 constexpr int kLseThreads = 256;
-constexpr int kLseUnroll = 4;
+constexpr int kLseUnroll = 8;
+constexpr int kLseCompactR = 4096;
+
+template <typename Elt>
+__device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, int gamma, int V, int span,
+                                                 const typename Elt::T* __restrict__ target,
+                                                 const int32_t* __restrict__ row0, const int32_t* __restrict__ x,
+                                                 float2* __restrict__ part, float* __restrict__ tx, Lse* sh) {
+  constexpr int N = RowVec<Elt>::N;
+  const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + i;
+  const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + i : ri;
+  const typename Elt::T* t = target + row * V;
+  const int v0 = sp * span;
+  const int v1 = min(v0 + span, V);
+  Lse acc{neg_inf(), 0.f};
+  if ((V % N) == 0) {
+    for (int vb = v0 + static_cast<int>(threadIdx.x) * N; vb < v1; vb += kLseUnroll * N * kLseThreads) {
+      float e[kLseUnroll][N];
+#pragma unroll
+      for (int u = 0; u < kLseUnroll; ++u) {
+        const int v = vb + u * N * kLseThreads;
+        RowVec<Elt>::load(t + (v < v1 ? v : v0), e[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kLseUnroll; ++u) {
+        if (vb + u * N * kLseThreads >= v1) break;
+        float m = e[u][0];
+#pragma unroll
+        for (int q = 1; q < N; ++q) m = fmaxf(m, e[u][q]);
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < N; ++q) sum += __expf(e[u][q] - m);
+        acc = lse_combine(acc, Lse{m, sum});
+      }
+    }
+  } else {
+    for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kLseThreads)
+      acc = lse_combine(acc, Lse{Elt::load(t, v), 1.f});
+  }
+  acc = block_reduce_lse(acc, sh);
+  if (threadIdx.x == 0) {
+    part[ri * kLseSplits + sp] = make_float2(acc.M, acc.S);
+    if (sp == 0 && i < L) {
+      const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
+      tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
+    }
+  }
+  __syncthreads();   // sh is reused by the next item
+}
 
 template <typename Elt>
 __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gamma, int V,
@@ -81,54 +132,63 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
                                                                   const int32_t* __restrict__ ell,
                                                                   float2* __restrict__ part, float* __restrict__ tx) {
   __shared__ Lse sh[kLseThreads / kWave];
+  __shared__ int pref[kLseCompactR + 1];   // pref[r] = needed rows of requests < r
   constexpr int N = RowVec<Elt>::N;
-  const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
   const int span = ceil_div(ceil_div(V, kLseSplits), N * kLseThreads) * N * kLseThreads;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int sp = static_cast<int>(it % kLseSplits);
-    const int64_t ri = it / kLseSplits;
-    const int r = static_cast<int>(ri / (gamma + 1));
-    const int i = static_cast<int>(ri % (gamma + 1));
-    const int L = min(max(ell[r], 0), gamma);
-    if (i > L) continue;   // uniform across the work group
-    const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + i : static_cast<int64_t>(r) * (gamma + 1) + i;
-    const typename Elt::T* t = target + row * V;
-    const int v0 = sp * span;
-    const int v1 = min(v0 + span, V);
-    Lse acc{neg_inf(), 0.f};
-    if ((V % N) == 0) {
-      for (int vb = v0 + static_cast<int>(threadIdx.x) * N; vb < v1; vb += kLseUnroll * N * kLseThreads) {
-        float e[kLseUnroll][N];
+  if (R <= kLseCompactR) {
+    // counts of needed rows, then an exclusive prefix: each thread sums a
+    // run of requests, the runs are scanned in one wave, then filled in
+    const int per = ceil_div(R, kLseThreads);
+    const int b0 = min(static_cast<int>(threadIdx.x) * per, R), b1 = min(b0 + per, R);
+    int mine = 0;
+    for (int q = b0; q < b1; ++q) mine += min(max(ell[q], 0), gamma) + 1;
+    __shared__ int wtot[kLseThreads / kWave];
+    int incl = mine;
 #pragma unroll
-        for (int u = 0; u < kLseUnroll; ++u) {
-          const int v = vb + u * N * kLseThreads;
-          RowVec<Elt>::load(t + (v < v1 ? v : v0), e[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < kLseUnroll; ++u) {
-          if (vb + u * N * kLseThreads >= v1) break;
-          float m = e[u][0];
-#pragma unroll
-          for (int q = 1; q < N; ++q) m = fmaxf(m, e[u][q]);
-          float sum = 0.f;
-#pragma unroll
-          for (int q = 0; q < N; ++q) sum += __expf(e[u][q] - m);
-          acc = lse_combine(acc, Lse{m, sum});
-        }
-      }
-    } else {
-      for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kLseThreads)
-        acc = lse_combine(acc, Lse{Elt::load(t, v), 1.f});
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if ((threadIdx.x & (kWave - 1)) >= o) incl += v;
     }
-    acc = block_reduce_lse(acc, sh);
-    if (threadIdx.x == 0) {
-      part[ri * kLseSplits + sp] = make_float2(acc.M, acc.S);
-      if (sp == 0 && i < L) {
-        const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
-        tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
-      }
+    if ((threadIdx.x & (kWave - 1)) == kWave - 1) wtot[threadIdx.x / kWave] = incl;
+    __syncthreads();
+    int run = incl - mine, total = 0;
+#pragma unroll
+    for (int wv = 0; wv < kLseThreads / kWave; ++wv) {
+      run += wv < static_cast<int>(threadIdx.x / kWave) ? wtot[wv] : 0;
+      total += wtot[wv];
     }
-    __syncthreads();   // sh is reused by the next item
+    if (threadIdx.x == 0) pref[R] = total;
+    for (int q = b0; q < b1; ++q) {
+      pref[q] = run;
+      run += min(max(ell[q], 0), gamma) + 1;
+    }
+    __syncthreads();
+    const int64_t items = static_cast<int64_t>(pref[R]) * kLseSplits;
+    for (int64_t a = blockIdx.x; a < items; a += gridDim.x) {
+      const int sp = static_cast<int>(a % kLseSplits);
+      const int act = static_cast<int>(a / kLseSplits);
+      int lo = 0, hi = R - 1;   // the request r with pref[r] <= act < pref[r + 1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pref[mid] <= act)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      const int L = min(max(ell[lo], 0), gamma);
+      target_part_item<Elt>(lo, act - pref[lo], sp, L, gamma, V, span, target, row0, x, part, tx, sh);
+    }
+  } else {
+    const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+      const int sp = static_cast<int>(it % kLseSplits);
+      const int64_t ri = it / kLseSplits;
+      const int r = static_cast<int>(ri / (gamma + 1));
+      const int i = static_cast<int>(ri % (gamma + 1));
+      const int L = min(max(ell[r], 0), gamma);
+      if (i > L) continue;   // uniform across the work group
+      target_part_item<Elt>(r, i, sp, L, gamma, V, span, target, row0, x, part, tx, sh);
+    }
   }
 }
 
