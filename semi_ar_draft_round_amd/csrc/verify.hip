@@ -24,7 +24,7 @@
 //                       chunk masses picks the chunk holding u_res * Z, and
 //                       one wave re-derives that chunk's 64 masses and scans
 //                       them to the token.
-#include "bias_tile.hpp"
+#include "wide_tile.hpp"
 
 namespace dspark {
 
@@ -264,127 +264,124 @@ __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, i
   return rr;
 }
 
-template <int NBW, int KS>
-struct ResidualStage {
-  WRegs<KS> w;
-  u32x2 t[NBW][4];   // target logits
-  u32x2 u[NBW][4];   // draft base logits (rejected rows; others re-read U row 0)
-};
-
-// The residual row of every request of a group, chunk by chunk, staged like
-// the sampler: loads two chunks ahead in two register sets, unconditional
-// (clamped) so the compiler never drains the prefetch; chunk i+1 is parked
-// in the other half of a double-buffered LDS area at the start of chunk i.
-template <int NBW, int KS, bool VEC>
-__global__ __launch_bounds__(kTileThreads, 1) void verify_residual_bf16(
+// The residual row of every request, one sweep over the vocabulary in
+// 64-token tiles with the sampler's 32x32x16 layout: work group = 2 RQ waves
+// over 32 RQ requests, wave = (token half th, request quarter rq), lane (h, j)
+// = request j and the sixteen tokens v0 + 32 th + 16 h + (0..15).  The draft
+// logits U_n + B (Markov bias of the previous token on the matrix cores, U
+// seeding the accumulators) and the target logits give each lane's sixteen
+// values of p_t and max(0, p_t - p_d); their sums are the lane's 16-token
+// chunk masses, stored directly.  Rows where every draft was accepted use
+// p_t (the bonus row) and skip nothing: their draft part is computed on U
+// row 0 and ignored.  W2t tiles go through registers into a double-buffered
+// LDS area one tile ahead; the lane's own logits are loaded two tiles ahead.
+template <int RQ, int KS16, bool VEC>
+__global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     int R, int gamma, int V, const uint16_t* __restrict__ target, const int32_t* __restrict__ row0,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
     float* __restrict__ csum, float* __restrict__ psum) {
-  constexpr int NROWS = kTileWaves * 16 * NBW;
-  constexpr int kW = tile_bytes(KS);
-  constexpr int kU = kTileThreads * NBW * 4 * 8 * 2;    // this lane's target and U logits
-  constexpr int kBuf = kW + kU;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kBuf];
-  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kL2e = 1.4426950408889634f;
+  constexpr int NROWS = 32 * RQ;
+  constexpr int kW = wide_tile_bytes<KS16>();
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int j = lane & 15;
-  const int q = lane >> 4;
-  const int nC = (V + kChunk - 1) / kChunk;
-  // the host launches at most one work group per chunk, so nT >= 1
-  const int nT = (nC - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
-
-  ResidualRow rr[NBW];
-  int prev[NBW], req[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    req[nb] = blockIdx.y * NROWS + wave * 16 * NBW + nb * 16 + j;
-    rr[nb] = residual_row(min(req[nb], R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
-    rr[nb].live = req[nb] < R;
-    prev[nb] = rr[nb].prev;
-  }
-  auto load_stage = [&](ResidualStage<NBW, KS>& st, int it) {
-    const int v0 = (blockIdx.x + it * gridDim.x) * kChunk;
-    load_w2_regs<KS>(st.w, W2t, V, v0);
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      load_lane_logits<VEC>(st.t[nb], target + rr[nb].trow * V, v0, V, q);
-      // rows with no rejection need no draft logits: they read U row 0 (cached)
-      load_lane_logits<VEC>(st.u[nb], U + (rr[nb].rej ? rr[nb].urow : 0) * V, v0, V, q);
-    }
-  };
-  auto park = [&](const ResidualStage<NBW, KS>& st, int buf) {
-    store_w2_tile<KS>(lds + buf * kBuf, st.w);
-    u32x2* up = reinterpret_cast<u32x2*>(lds + buf * kBuf + kW) + threadIdx.x * NBW * 8;
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        up[nb * 8 + mb] = st.t[nb][mb];
-        up[nb * 8 + 4 + mb] = st.u[nb][mb];
-      }
-  };
+  const int th = wave & 1;
+  const int rq = wave >> 1;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int req = static_cast<int>(blockIdx.y) * NROWS + rq * 32 + j;
+  const bool live = req < R;
+  const int lofs = 32 * th + 16 * h;
+  const int nTiles = (V + kChunk - 1) / kChunk;
+  const int nG = (V + kGChunk - 1) / kGChunk;
+  // the host launches at most one work group per tile, so nT >= 1
+  const int nT = (nTiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                 static_cast<int>(gridDim.x);
   const auto clampc = [&](int it) { return it < nT ? it : nT - 1; };
-  ResidualStage<NBW, KS> even, odd;
-  load_stage(even, 0);
-  load_stage(odd, clampc(1));
-  WFrags<NBW, KS> e;
-  load_w1_frags<NBW, KS>(e, W1, prev);
-  park(even, 0);
-  __builtin_amdgcn_s_waitcnt(0);     // prologue loads have landed before the loop
-  load_stage(even, clampc(2));
+  const auto tile_of = [&](int it) { return static_cast<int>(blockIdx.x) + it * static_cast<int>(gridDim.x); };
+
+  const ResidualRow rr = residual_row(min(req, R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  const uint16_t* trow = target + rr.trow * V;
+  const uint16_t* urow = U + (rr.rej ? rr.urow : 0) * V;
+  const float lt2 = rr.lt * kL2e;
+  const float ld2 = rr.ld * kL2e;
+
+  struct Lane {
+    u32x4 t[2], u[2];
+  };
+  auto load_lane = [&](Lane& ll, int it) {
+    const int v = tile_of(clampc(it)) * kChunk + lofs;
+    load_lane16<VEC>(ll.t, trow, v, V);
+    load_lane16<VEC>(ll.u, urow, v, V);
+  };
+  WideW<KS16, RQ> wr;
+  wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(0) * kChunk);
+  Lane even, odd;
+  load_lane(even, 0);
+  load_lane(odd, 1);
+  bf16x8 e[KS16];
+  const uint16_t* w1row = (rr.rej && rr.prev >= 0 ? W1 + static_cast<int64_t>(rr.prev) * (KS16 * 16) : kZeroRow) + 8 * h;
+#pragma unroll
+  for (int ks = 0; ks < KS16; ++ks) e[ks] = load_bf16x8_global(w1row + 16 * ks);
+  wide_store_w<KS16, RQ>(lds, wr);
+  wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(1)) * kChunk);
   __syncthreads();
 
-  auto chunk = [&](int it, ResidualStage<NBW, KS>& nxt) {
-    const int tile = blockIdx.x + it * gridDim.x;
-    const int v0 = tile * kChunk;
-    const int buf = it & 1;
-    park(nxt, buf ^ 1);
-    load_stage(nxt, clampc(it + 3));
-    const u32x2* up = reinterpret_cast<const u32x2*>(lds + buf * kBuf + kW) + threadIdx.x * NBW * 8;
-    f32x4 acc[4][NBW];
-    bias_tile<NBW, KS>(acc, lds + buf * kBuf, e);
+  auto step = [&](int it, Lane& cur) {
+    f32x16 acc, acc2 = {};
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const float lt2 = rr[nb].lt * kLog2e;
-      const float ld2 = rr[nb].ld * kLog2e;
-      float sres = 0.f, spt = 0.f;
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t w = cur.u[q >> 3][(q >> 1) & 3];
+      acc[q] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    float tv[16];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const u32x2 tw = up[nb * 8 + mb];
-        const u32x2 uw = up[nb * 8 + 4 + mb];
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t w = cur.t[q >> 3][(q >> 1) & 3];
+      tv[q] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    load_lane(cur, it + 2);
+    const uint8_t* arow = lds + (it & 1) * kW + ((32 * th + j) * wide_row_pieces<KS16>() + h) * 16;
+    constexpr int KB = KS16 < 8 ? KS16 : 8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = v0 + mb * 16 + 4 * q + i;
-          if (v < V) {
-            const float pt = __builtin_amdgcn_exp2f(fmaf(row4_get(tw, i), kLog2e, -lt2));
-            float res = pt;
-            if (rr[nb].rej)
-              res = fmaxf(0.f, pt - __builtin_amdgcn_exp2f(fmaf(row4_get(uw, i) + acc[mb][nb][i], kLog2e, -ld2)));
-            sres += res;
-            spt += pt;
-          }
-        }
-      }
-      sres += __shfl_xor(sres, 16);
-      sres += __shfl_xor(sres, 32);
-      spt += __shfl_xor(spt, 16);
-      spt += __shfl_xor(spt, 32);
-      if (q == 0 && rr[nb].live) {
-        csum[static_cast<int64_t>(req[nb]) * nC + tile] = sres;
-        psum[static_cast<int64_t>(req[nb]) * nC + tile] = spt;
+    for (int k0 = 0; k0 < KS16; k0 += KB) {
+      bf16x8 a[KB];
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(arow + (k0 + kk) * 32);
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        if (kk & 1)
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], e[k0 + kk], acc2, 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], e[k0 + kk], acc, 0, 0, 0);
       }
     }
+    float cs = 0.f, ps = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float pt = __builtin_amdgcn_exp2f(fmaf(tv[q], kL2e, -lt2));
+      const float pd = __builtin_amdgcn_exp2f(fmaf(acc[q] + acc2[q], kL2e, -ld2));
+      ps += pt;
+      cs += rr.rej ? fmaxf(0.f, pt - pd) : pt;
+    }
+    const int c16 = 4 * tile_of(it) + 2 * th + h;
+    if (live && c16 < nG) {
+      csum[static_cast<int64_t>(req) * nG + c16] = cs;
+      psum[static_cast<int64_t>(req) * nG + c16] = ps;
+    }
+    wide_store_w<KS16, RQ>(lds + ((it + 1) & 1) * kW, wr);
+    wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(it + 2)) * kChunk);
     __syncthreads();
   };
   int it = 0;
   for (; it + 1 < nT; it += 2) {
-    chunk(it, odd);
-    chunk(it + 1, even);
+    step(it, even);
+    step(it + 1, odd);
   }
-  if (it < nT) chunk(it, odd);
+  if (it < nT) step(it, even);
 }
 
 __global__ __launch_bounds__(64) void verify_residual_f32(
@@ -396,7 +393,6 @@ __global__ __launch_bounds__(64) void verify_residual_f32(
   const int tile = blockIdx.x;
   const int req = blockIdx.y;
   const int lane = threadIdx.x;
-  const int nC = (V + kChunk - 1) / kChunk;
   const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
   const int v = tile * kChunk + lane;
   float res = 0.f, pt = 0.f;
@@ -413,11 +409,17 @@ __global__ __launch_bounds__(64) void verify_residual_f32(
       res = fmaxf(0.f, pt - __expf(U[rr.urow * V + v] + b - rr.ld));
     }
   }
-  res = wave_reduce_sum(res);
-  pt = wave_reduce_sum(pt);
-  if (lane == 0) {
-    csum[static_cast<int64_t>(req) * nC + tile] = res;
-    psum[static_cast<int64_t>(req) * nC + tile] = pt;
+  // masses of each 16-token chunk: a reduction over each quarter of the wave
+#pragma unroll
+  for (int o = 1; o < kGChunk; o <<= 1) {
+    res += __shfl_xor(res, o);
+    pt += __shfl_xor(pt, o);
+  }
+  const int nG = (V + kGChunk - 1) / kGChunk;
+  const int c16 = tile * (kChunk / kGChunk) + lane / kGChunk;
+  if ((lane & (kGChunk - 1)) == 0 && c16 < nG) {
+    csum[static_cast<int64_t>(req) * nG + c16] = res;
+    psum[static_cast<int64_t>(req) * nG + c16] = pt;
   }
 }
 
@@ -439,38 +441,58 @@ __global__ __launch_bounds__(256) void verify_select(
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
     const float* __restrict__ u_res, const float* __restrict__ csum, const float* __restrict__ psum,
     int32_t* __restrict__ next_tok) {
-  __shared__ float scan[256];
+  constexpr int kT = 256;
+  __shared__ float wsum[kT / kWave];
   __shared__ float e_row[1024];
   __shared__ int s_chunk, s_last;
-  __shared__ float s_before;
+  __shared__ float s_before, s_last_before;
   const int req = blockIdx.x;
   const int tid = threadIdx.x;
-  const int nC = (V + kChunk - 1) / kChunk;
+  const int nG = (V + kGChunk - 1) / kGChunk;
   const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
-  const int seg = (nC + 255) / 256;
+  const int seg = (nG + kT - 1) / kT;
   const int lo = tid * seg;
-  const int hi = min(nC, lo + seg);
+  const int hi = min(nG, lo + seg);
 
+  // prefix over this thread's run of chunk masses (held in registers when
+  // the run is at most kSelRun long): a wave scan, then the wave totals; if
+  // the residual vanished (Z <= 0) draw from p_t instead
+  constexpr int kSelRun = 48;
+  const bool inreg = seg <= kSelRun;
+  float vals[kSelRun];
   bool use_pt = !rr.rej;
-  const float* sums = rr.rej ? csum : psum;
+  const float* sums = (rr.rej ? csum : psum) + static_cast<int64_t>(req) * nG;
   float Z = 0.f, excl = 0.f;
   for (int pass = 0; pass < 2; ++pass) {
     float local = 0.f;
-    for (int cc = lo; cc < hi; ++cc) local += sums[static_cast<int64_t>(req) * nC + cc];
-    scan[tid] = local;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const float v = (tid >= o) ? scan[tid - o] : 0.f;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
+    if (inreg) {
+#pragma unroll
+      for (int q = 0; q < kSelRun; ++q) vals[q] = lo + q < hi ? sums[lo + q] : 0.f;
+#pragma unroll
+      for (int q = 0; q < kSelRun; ++q) local += vals[q];
+    } else {
+      for (int cc = lo; cc < hi; ++cc) local += sums[cc];
     }
-    Z = scan[255];
-    excl = scan[tid] - local;
+    float incl = local;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float v = __shfl_up(incl, o);
+      if ((tid & (kWave - 1)) >= o) incl += v;
+    }
+    if ((tid & (kWave - 1)) == kWave - 1) wsum[tid / kWave] = incl;
+    __syncthreads();
+    float before = 0.f;
+    Z = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kT / kWave; ++wv) {
+      before += wv < tid / kWave ? wsum[wv] : 0.f;
+      Z += wsum[wv];
+    }
+    excl = before + incl - local;
     __syncthreads();
     if (Z > 0.f || use_pt) break;
     use_pt = true;                       // residual vanished: draw from p_t
-    sums = psum;
+    sums = psum + static_cast<int64_t>(req) * nG;
   }
   const float thr = u_res[req] * Z;
   if (tid == 0) {
@@ -480,30 +502,43 @@ __global__ __launch_bounds__(256) void verify_select(
   __syncthreads();
   float run = excl;
   int first = 0x7FFFFFFF, last = -1;
-  float before = 0.f;
-  for (int cc = lo; cc < hi; ++cc) {
-    const float sv = sums[static_cast<int64_t>(req) * nC + cc];
-    if (sv > 0.f) last = cc;
+  float before = 0.f, last_before = 0.f;
+  auto visit = [&](int cc, float sv) {
+    if (sv > 0.f) {
+      last = cc;
+      last_before = run;
+    }
     if (first == 0x7FFFFFFF && run + sv > thr) {
       first = cc;
       before = run;
     }
     run += sv;
+  };
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < kSelRun; ++q)
+      if (lo + q < hi) visit(lo + q, vals[q]);
+  } else {
+    for (int cc = lo; cc < hi; ++cc) visit(cc, sums[cc]);
   }
   if (first != 0x7FFFFFFF) atomicMin(&s_chunk, first);
   if (last >= 0) atomicMax(&s_last, last);
   __syncthreads();
   if (first != 0x7FFFFFFF && first == s_chunk) s_before = before;
-  if (s_chunk == 0x7FFFFFFF && last >= 0 && last == s_last) s_before = run - sums[static_cast<int64_t>(req) * nC + last];
-  // the previous token's W1 row, for the bias of the chunk's 64 tokens
+  if (last >= 0 && last == s_last) s_last_before = last_before;
+  // the previous token's W1 row, for the bias of the chunk's tokens
   if (!use_pt && rr.prev >= 0)
-    for (int i = tid; i < r; i += 256) e_row[i] = Elt::load(W1, static_cast<int64_t>(rr.prev) * r + i);
+    for (int i = tid; i < r; i += kT) e_row[i] = Elt::load(W1, static_cast<int64_t>(rr.prev) * r + i);
   __syncthreads();
-  const int chunk = (s_chunk != 0x7FFFFFFF) ? s_chunk : max(s_last, 0);
-  if (tid < 64) {
-    const int v = chunk * kChunk + tid;
+  // the chunk holding u * Z; rounding past the end falls back to the last
+  // chunk with mass
+  const bool found = s_chunk != 0x7FFFFFFF;
+  const int chunk = found ? s_chunk : max(s_last, 0);
+  const float base = found ? s_before : s_last_before;
+  if (tid < kWave) {
+    const int v = chunk * kGChunk + tid;
     float val = 0.f;
-    if (v < V) {
+    if (tid < kGChunk && v < V) {
       const float pt = __expf(Elt::load(target, rr.trow * V + v) - rr.lt);
       val = pt;
       if (!use_pt) {
@@ -512,8 +547,7 @@ __global__ __launch_bounds__(256) void verify_select(
       }
     }
     const float cum = wave_inclusive_scan(val);
-    const float local_thr = thr - s_before;
-    const unsigned long long hit = __ballot(cum > local_thr);
+    const unsigned long long hit = __ballot(tid < kGChunk && cum > thr - base);
     int off;
     if (hit) {
       off = __ffsll(static_cast<long long>(hit)) - 1;
@@ -521,7 +555,7 @@ __global__ __launch_bounds__(256) void verify_select(
       const unsigned long long pos = __ballot(val > 0.f);
       off = pos ? 63 - __clzll(static_cast<long long>(pos)) : 0;
     }
-    if (tid == 0) next_tok[req] = chunk * kChunk + off;
+    if (tid == 0) next_tok[req] = chunk * kGChunk + off;
   }
 }
 
@@ -531,20 +565,20 @@ struct VerifyWs {
   float* lse_t;   // [R][gamma+1]
   float2* part;   // [R][gamma+1][kLseSplits] (max, sum) parts of the target log-normalisers
   float* tx;      // [R][gamma]
-  float* csum;    // [R][nC]
-  float* psum;    // [R][nC]
+  float* csum;    // [R][nG] residual mass of each 16-token chunk
+  float* psum;    // [R][nG] p_t mass of each 16-token chunk
 };
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 size_t verify_workspace_bytes(int R, int gamma, int V) {
-  const size_t nC = static_cast<size_t>(ceil_div(V, kChunk));
+  const size_t nC = static_cast<size_t>(ceil_div(V, kGChunk));
   return align256(sizeof(float) * R * (gamma + 1)) + align256(sizeof(float2) * R * (gamma + 1) * kLseSplits) +
          align256(sizeof(float) * R * gamma) + 2 * align256(sizeof(float) * R * nC);
 }
 
 static VerifyWs carve(void* ws, int R, int gamma, int V) {
-  const size_t nC = static_cast<size_t>(ceil_div(V, kChunk));
+  const size_t nC = static_cast<size_t>(ceil_div(V, kGChunk));
   char* p = static_cast<char*>(ws);
   VerifyWs w;
   w.lse_t = reinterpret_cast<float*>(p);
@@ -561,37 +595,39 @@ static VerifyWs carve(void* ws, int R, int gamma, int V) {
 
 int compute_units();   // abi.hip
 
-template <int NBW, int KS>
-static void launch_residual_bf16(int R, int gamma, int V, const void* target, const int32_t* row0,
+template <int RQ, int KS16>
+static void launch_residual_wide(int R, int gamma, int V, const void* target, const int32_t* row0,
                                  const void* U, const void* W1, const void* W2t, const int32_t* x0,
                                  const int32_t* x, const float* lse, const int32_t* ell,
                                  const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
-  const int nC = ceil_div(V, kChunk);
-  const int groups = ceil_div(R, kTileWaves * 16 * NBW);
+  const int nTiles = ceil_div(V, kChunk);
+  const int groups = ceil_div(R, 32 * RQ);
   int gx = compute_units() / groups;
-  gx = gx < 1 ? 1 : (gx > nC ? nC : gx);
+  gx = gx < 1 ? 1 : (gx > nTiles ? nTiles : gx);
   dim3 grid(gx, groups);
-  if (V % 4 == 0)
-    hipLaunchKernelGGL((verify_residual_bf16<NBW, KS, true>), grid, dim3(kTileThreads), 0, s, R, gamma, V,
+  if (V % kGChunk == 0)
+    hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, true>), grid, dim3(wide_threads<RQ>()), 0, s, R, gamma, V,
                        static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
                        static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
                        ell, n_acc, w.lse_t, w.csum, w.psum);
   else
-    hipLaunchKernelGGL((verify_residual_bf16<NBW, KS, false>), grid, dim3(kTileThreads), 0, s, R, gamma, V,
+    hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, false>), grid, dim3(wide_threads<RQ>()), 0, s, R, gamma, V,
                        static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
                        static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
                        ell, n_acc, w.lse_t, w.csum, w.psum);
 }
 
-template <int KS>
-static void launch_residual_bf16_ks(int R, int gamma, int V, const void* target, const int32_t* row0,
+template <int KS16>
+static void launch_residual_wide_ks(int R, int gamma, int V, const void* target, const int32_t* row0,
                                     const void* U, const void* W1, const void* W2t, const int32_t* x0,
                                     const int32_t* x, const float* lse, const int32_t* ell,
                                     const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
-  if (R <= 64)
-    launch_residual_bf16<1, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+  if (R <= 32)
+    launch_residual_wide<1, KS16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+  else if (R <= 64)
+    launch_residual_wide<2, KS16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
   else
-    launch_residual_bf16<2, KS>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+    launch_residual_wide<4, KS16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
 }
 
 hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
@@ -600,7 +636,6 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                          const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
                          int32_t* next_tok, void* ws, hipStream_t s) {
   const VerifyWs w = carve(ws, R, gamma, V);
-  const int nC = ceil_div(V, kChunk);
   hipError_t err;
   const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
   const int gridp = static_cast<int>(items < 4LL * compute_units() ? items : 4LL * compute_units());
@@ -616,13 +651,13 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (dt == DSPARK_BF16) {
     switch (r / 32) {
-      case 1: launch_residual_bf16_ks<1>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-      case 2: launch_residual_bf16_ks<2>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-      case 4: launch_residual_bf16_ks<4>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-      default: launch_residual_bf16_ks<8>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      case 1: launch_residual_wide_ks<2>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      case 2: launch_residual_wide_ks<4>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      case 4: launch_residual_wide_ks<8>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
+      default: launch_residual_wide_ks<16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
     }
   } else {
-    hipLaunchKernelGGL(verify_residual_f32, dim3(nC, R), dim3(64), 0, s, R, gamma, V, r,
+    hipLaunchKernelGGL(verify_residual_f32, dim3(ceil_div(V, kChunk), R), dim3(64), 0, s, R, gamma, V, r,
                        static_cast<const float*>(target), row0, static_cast<const float*>(U),
                        static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, ell,
                        n_acc, w.lse_t, w.csum, w.psum);
