@@ -17,13 +17,13 @@
 //   verify_residual_*   the residual row of every request in one pass over
 //                       the vocabulary: p_d is rebuilt from U and the Markov
 //                       bias of the previous token (same matrix-core tile as
-//                       the sampler), and every 64-token chunk's mass of
+//                       the sampler), and every 16-token chunk's mass of
 //                       max(0, p_t - p_d) (or of p_t for the bonus row) and
 //                       of p_t is written out;
 //   verify_select       one work group per request: a prefix scan over the
 //                       chunk masses picks the chunk holding u_res * Z, and
-//                       one wave re-derives that chunk's 64 masses and scans
-//                       them to the token.
+//                       the chunk's 16 masses are re-derived and scanned to
+//                       the token.
 #include "wide_tile.hpp"
 
 namespace dspark {
@@ -236,6 +236,12 @@ __global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int
 
 // ------------------------------------------------------- residual chunk masses
 
+// Row stride of the per-request chunk-mass arrays: ceil(V/16) rounded up to
+// a multiple of four floats, so select can read them as 16-byte vectors.
+__host__ __device__ __forceinline__ int mass_stride(int V) {
+  return (V + 4 * kGChunk - 1) / (4 * kGChunk) * 4;
+}
+
 struct ResidualRow {
   int64_t trow;     // target row index
   int64_t urow;     // draft row index (request * gamma + n), valid when rej
@@ -297,6 +303,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   const int lofs = 32 * th + 16 * h;
   const int nTiles = (V + kChunk - 1) / kChunk;
   const int nG = (V + kGChunk - 1) / kGChunk;
+  const int ldm = mass_stride(V);
   // the host launches at most one work group per tile, so nT >= 1
   const int nT = (nTiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
                  static_cast<int>(gridDim.x);
@@ -369,8 +376,8 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     }
     const int c16 = 4 * tile_of(it) + 2 * th + h;
     if (live && c16 < nG) {
-      csum[static_cast<int64_t>(req) * nG + c16] = cs;
-      psum[static_cast<int64_t>(req) * nG + c16] = ps;
+      csum[static_cast<int64_t>(req) * ldm + c16] = cs;
+      psum[static_cast<int64_t>(req) * ldm + c16] = ps;
     }
     wide_store_w<KS16, RQ>(lds + ((it + 1) & 1) * kW, wr);
     wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(it + 2)) * kChunk);
@@ -416,22 +423,23 @@ __global__ __launch_bounds__(64) void verify_residual_f32(
     pt += __shfl_xor(pt, o);
   }
   const int nG = (V + kGChunk - 1) / kGChunk;
+  const int ldm = mass_stride(V);
   const int c16 = tile * (kChunk / kGChunk) + lane / kGChunk;
   if ((lane & (kGChunk - 1)) == 0 && c16 < nG) {
-    csum[static_cast<int64_t>(req) * nG + c16] = res;
-    psum[static_cast<int64_t>(req) * nG + c16] = pt;
+    csum[static_cast<int64_t>(req) * ldm + c16] = res;
+    psum[static_cast<int64_t>(req) * ldm + c16] = pt;
   }
 }
 
 // -------------------------------------------------------------------- select
 
-template <typename Elt>
-__device__ __forceinline__ float row_dot(const float* e_lds, const typename Elt::T* w, int r) {
-  float b = 0.f;
-  for (int i = 0; i < r; ++i) b = fmaf(e_lds[i], Elt::load(w, i), b);
-  return b;
-}
-
+// The next token of every request, one work group each: the chunk holding
+// u * Z in the prefix of the chunk masses (Z their total; when the residual
+// vanished, Z <= 0, the draw falls back to p_t), then the token inside that
+// chunk from its sixteen recomputed values.  The masses are read as 16-byte
+// vectors into registers (a run of 4 kSelVec per thread), scanned per wave and
+// across the waves; the chunk's Markov biases are dot products split over
+// sixteen threads per token against the previous token's W1 row in LDS.
 template <typename Elt>
 __global__ __launch_bounds__(256) void verify_select(
     int R, int gamma, int V, int r, const typename Elt::T* __restrict__ target,
@@ -442,34 +450,43 @@ __global__ __launch_bounds__(256) void verify_select(
     const float* __restrict__ u_res, const float* __restrict__ csum, const float* __restrict__ psum,
     int32_t* __restrict__ next_tok) {
   constexpr int kT = 256;
+  constexpr int kSelVec = 12;
   __shared__ float wsum[kT / kWave];
   __shared__ float e_row[1024];
+  __shared__ float s_val[kGChunk];
   __shared__ int s_chunk, s_last;
   __shared__ float s_before, s_last_before;
   const int req = blockIdx.x;
   const int tid = threadIdx.x;
   const int nG = (V + kGChunk - 1) / kGChunk;
+  const int ldm = mass_stride(V);
   const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
-  const int seg = (nG + kT - 1) / kT;
-  const int lo = tid * seg;
-  const int hi = min(nG, lo + seg);
-
-  // prefix over this thread's run of chunk masses (held in registers when
-  // the run is at most kSelRun long): a wave scan, then the wave totals; if
-  // the residual vanished (Z <= 0) draw from p_t instead
-  constexpr int kSelRun = 48;
-  const bool inreg = seg <= kSelRun;
-  float vals[kSelRun];
+  // the previous token's W1 row, for the bias of the chunk's tokens
+  if (rr.rej && rr.prev >= 0)
+    for (int i = tid; i < r; i += kT) e_row[i] = Elt::load(W1, static_cast<int64_t>(rr.prev) * r + i);
+  const int seg4 = (ldm / 4 + kT - 1) / kT;    // vectors per thread
+  const int lo = tid * seg4 * 4;
+  const int hi = min(nG, lo + seg4 * 4);
+  const bool inreg = seg4 <= kSelVec;
+  float vals[4 * kSelVec];
   bool use_pt = !rr.rej;
-  const float* sums = (rr.rej ? csum : psum) + static_cast<int64_t>(req) * nG;
+  const float* sums = (rr.rej ? csum : psum) + static_cast<int64_t>(req) * ldm;
   float Z = 0.f, excl = 0.f;
   for (int pass = 0; pass < 2; ++pass) {
     float local = 0.f;
     if (inreg) {
+      const float4* s4 = reinterpret_cast<const float4*>(sums);
 #pragma unroll
-      for (int q = 0; q < kSelRun; ++q) vals[q] = lo + q < hi ? sums[lo + q] : 0.f;
+      for (int q = 0; q < kSelVec; ++q) {
+        const int c = lo + 4 * q;
+        const float4 f = (q < seg4 && c < ldm) ? s4[c / 4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        vals[4 * q] = c < nG ? f.x : 0.f;
+        vals[4 * q + 1] = c + 1 < nG ? f.y : 0.f;
+        vals[4 * q + 2] = c + 2 < nG ? f.z : 0.f;
+        vals[4 * q + 3] = c + 3 < nG ? f.w : 0.f;
+      }
 #pragma unroll
-      for (int q = 0; q < kSelRun; ++q) local += vals[q];
+      for (int q = 0; q < 4 * kSelVec; ++q) local += vals[q];
     } else {
       for (int cc = lo; cc < hi; ++cc) local += sums[cc];
     }
@@ -492,7 +509,7 @@ __global__ __launch_bounds__(256) void verify_select(
     __syncthreads();
     if (Z > 0.f || use_pt) break;
     use_pt = true;                       // residual vanished: draw from p_t
-    sums = psum + static_cast<int64_t>(req) * nG;
+    sums = psum + static_cast<int64_t>(req) * ldm;
   }
   const float thr = u_res[req] * Z;
   if (tid == 0) {
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(256) void verify_select(
   };
   if (inreg) {
 #pragma unroll
-    for (int q = 0; q < kSelRun; ++q)
+    for (int q = 0; q < 4 * kSelVec; ++q)
       if (lo + q < hi) visit(lo + q, vals[q]);
   } else {
     for (int cc = lo; cc < hi; ++cc) visit(cc, sums[cc]);
@@ -526,26 +543,40 @@ __global__ __launch_bounds__(256) void verify_select(
   __syncthreads();
   if (first != 0x7FFFFFFF && first == s_chunk) s_before = before;
   if (last >= 0 && last == s_last) s_last_before = last_before;
-  // the previous token's W1 row, for the bias of the chunk's tokens
-  if (!use_pt && rr.prev >= 0)
-    for (int i = tid; i < r; i += kT) e_row[i] = Elt::load(W1, static_cast<int64_t>(rr.prev) * r + i);
   __syncthreads();
   // the chunk holding u * Z; rounding past the end falls back to the last
   // chunk with mass
   const bool found = s_chunk != 0x7FFFFFFF;
   const int chunk = found ? s_chunk : max(s_last, 0);
   const float base = found ? s_before : s_last_before;
-  if (tid < kWave) {
-    const int v = chunk * kGChunk + tid;
-    float val = 0.f;
-    if (tid < kGChunk && v < V) {
-      const float pt = __expf(Elt::load(target, rr.trow * V + v) - rr.lt);
-      val = pt;
-      if (!use_pt) {
-        const float b = (rr.prev >= 0) ? row_dot<Elt>(e_row, W2t + static_cast<int64_t>(v) * r, r) : 0.f;
-        val = fmaxf(0.f, pt - __expf(Elt::load(U, rr.urow * V + v) + b - rr.ld));
-      }
+  const int tk = tid / kGChunk;      // token of the chunk
+  const int sl = tid % kGChunk;      // slice of its bias dot product
+  const int v = chunk * kGChunk + tk;
+  float tl = 0.f, ul = 0.f, b = 0.f;
+  if (v < V) {
+    if (sl == 0) {
+      tl = Elt::load(target, rr.trow * V + v);
+      if (!use_pt) ul = Elt::load(U, rr.urow * V + v);
     }
+    if (!use_pt && rr.prev >= 0) {
+      const typename Elt::T* w = W2t + static_cast<int64_t>(v) * r;
+#pragma unroll 16
+      for (int i = sl; i < r; i += kGChunk) b = fmaf(e_row[i], Elt::load(w, i), b);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < kGChunk; o <<= 1) b += __shfl_xor(b, o);
+  if (sl == 0) {
+    float val = 0.f;
+    if (v < V) {
+      const float pt = __expf(tl - rr.lt);
+      val = use_pt ? pt : fmaxf(0.f, pt - __expf(ul + b - rr.ld));
+    }
+    s_val[tk] = val;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const float val = tid < kGChunk ? s_val[tid] : 0.f;
     const float cum = wave_inclusive_scan(val);
     const unsigned long long hit = __ballot(tid < kGChunk && cum > thr - base);
     int off;
@@ -565,20 +596,20 @@ struct VerifyWs {
   float* lse_t;   // [R][gamma+1]
   float2* part;   // [R][gamma+1][kLseSplits] (max, sum) parts of the target log-normalisers
   float* tx;      // [R][gamma]
-  float* csum;    // [R][nG] residual mass of each 16-token chunk
-  float* psum;    // [R][nG] p_t mass of each 16-token chunk
+  float* csum;    // [R][mass_stride(V)] residual mass of each 16-token chunk
+  float* psum;    // [R][mass_stride(V)] p_t mass of each 16-token chunk
 };
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 size_t verify_workspace_bytes(int R, int gamma, int V) {
-  const size_t nC = static_cast<size_t>(ceil_div(V, kGChunk));
+  const size_t nC = static_cast<size_t>(mass_stride(V));
   return align256(sizeof(float) * R * (gamma + 1)) + align256(sizeof(float2) * R * (gamma + 1) * kLseSplits) +
          align256(sizeof(float) * R * gamma) + 2 * align256(sizeof(float) * R * nC);
 }
 
 static VerifyWs carve(void* ws, int R, int gamma, int V) {
-  const size_t nC = static_cast<size_t>(ceil_div(V, kGChunk));
+  const size_t nC = static_cast<size_t>(mass_stride(V));
   char* p = static_cast<char*>(ws);
   VerifyWs w;
   w.lse_t = reinterpret_cast<float*>(p);
