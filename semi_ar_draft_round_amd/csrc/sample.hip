@@ -365,6 +365,11 @@ __device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int rou
   return *flag != 0;
 }
 
+// W2t tiles of each work group that stay in LDS for the whole launch (the
+// middle pair of its tiles): they are read from HBM once instead of once per
+// position.
+constexpr int kResident = 2;
+
 // All gamma positions in one launch.  Position k + 1 needs the tokens drawn
 // at position k, so the work groups meet at a grid barrier between positions;
 // the loads that do not depend on the tokens (the next position's logits and
@@ -385,9 +390,9 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
   constexpr int T = wide_threads<RQ>();
   constexpr int NROWS = 32 * RQ;
   constexpr int kW = wide_tile_bytes<KS16>();   // tile bytes (padded rows)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
+  // two streaming slots, then the kResident tiles kept for the whole launch
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[(2 + kResident) * kW];
   __shared__ float gsh[NROWS][kGChunk];        // in-chunk Gumbels of the group's requests
-  __shared__ f32x4 keepsh[2 * 4 * T];          // each lane's last two folded chunks: [slot][quarter][thread]
   __shared__ float2 lsh[NROWS];                // token half 1 -> token half 0 hand-over
   __shared__ unsigned long long ksh[NROWS];
   __shared__ int barflag;
@@ -409,14 +414,23 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
   const int nT = 2 * ((nPairs - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
                       static_cast<int>(gridDim.x));
   // tile at sweep position p of position k (snake order over this group's pairs)
+  const auto q_at = [&](int k, int p) { return (k & 1) ? nT - 1 - p : p; };
   const auto tile_at = [&](int k, int p) {
-    const int q = (k & 1) ? nT - 1 - p : p;
+    const int q = q_at(k, p);
     return 2 * (static_cast<int>(blockIdx.x) + (q >> 1) * static_cast<int>(gridDim.x)) + (q & 1);
   };
   // a sweep position past the last belongs to the next position (the last
   // position repeats its last tile)
   const auto next_k = [&](int k, int p) { return p < nT ? k : (k + 1 < gamma ? k + 1 : k); };
   const auto next_p = [&](int k, int p) { return p < nT ? p : (k + 1 < gamma ? p - nT : nT - 1); };
+  // the middle pair of the group's tiles stays in LDS (so that every
+  // position starts on streamed tiles, whose loads are issued before the
+  // grid barrier); the others stream through two slots, alternating with
+  // the sweep position
+  const int qr = nT / 2 - 1;
+  const auto is_res = [&](int q) { return q >= qr && q < qr + kResident; };
+  const auto resident = [&](int k, int p) { return is_res(q_at(next_k(k, p), next_p(k, p))); };
+  const auto slot_of = [&](int k, int p) { return resident(k, p) ? 2 + q_at(k, p) - qr : (p & 1); };
 
   struct Lane {
     u32x4 u[2];
@@ -430,7 +444,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     ll.G = G[(static_cast<int64_t>(k2) * nG + min(4 * t + 2 * th + h, nG - 1)) * R + reqc];
   };
   auto load_w = [&](WideW<KS16, RQ>& w, int k, int p) {
-    wide_load_w<KS16, RQ>(w, W2t, V, tile_at(next_k(k, p), next_p(k, p)) * kChunk);
+    if (!resident(k, p)) wide_load_w<KS16, RQ>(w, W2t, V, tile_at(next_k(k, p), next_p(k, p)) * kChunk);
   };
   // in-chunk Gumbels of position k: each of the request's four lanes brings four offsets
   auto load_gq = [&](int k) {
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
   WideW<KS16, RQ> wr;
   Lane even, odd;
   LaneDraw dr;
-  int bestSlot = 0;
+  f32x16 bestL = {};   // logits of the lane's best chunk so far
   f32x16 accP;
   float GcP = 0.f;
   int v0P = 0;
@@ -462,7 +476,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     Gc = cur.G;
     load_lane(cur, k, p + 2);
     // the lane's A rows: stored row 32 th + j, piece 2 ks + h at k-step ks
-    const uint8_t* arow = lds + (p & 1) * kW + ((32 * th + j) * wide_row_pieces<KS16>() + h) * 16;
+    const uint8_t* arow = lds + slot_of(k, p) * kW + ((32 * th + j) * wide_row_pieces<KS16>() + h) * 16;
     // A fragments in batches of eight reads ahead of their products; two
     // accumulator chains (even and odd k-steps) keep the matrix pipe busy
     constexpr int KB = KS16 < 8 ? KS16 : 8;
@@ -482,22 +496,20 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     }
     acc += acc2;
   };
-  // fold the previous tile: its logits go to the free keep slot whatever
-  // happens, and that slot becomes the best one if the chunk wins
+  // fold the previous tile; its logits become the best chunk's if it wins
   auto fold_prev = [&]() {
     f32x4 a[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) a[m] = f32x4{accP[4 * m], accP[4 * m + 1], accP[4 * m + 2], accP[4 * m + 3]};
-    const int freeSlot = bestSlot ^ 1;
-    f32x4* kp = keepsh + freeSlot * 4 * T + threadIdx.x;
+    const bool take = fold_chunk(a, GcP, v0P + lofs, dr);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) kp[m * T] = a[m];
-    if (fold_chunk(a, GcP, v0P + lofs, dr)) bestSlot = freeSlot;
+    for (int c = 0; c < kGChunk; ++c) bestL[c] = take ? accP[c] : bestL[c];
   };
-  // stores the tile of sweep position p + 1 into the other LDS half, issues
-  // the W2t loads of position p + 2, and waits for every wave
+  // stores the tile of sweep position p + 1 into its streaming slot (unless
+  // it is resident), issues the W2t loads of position p + 2, and waits for
+  // every wave
   auto advance = [&](int k, int p) {
-    wide_store_w<KS16, RQ>(lds + ((p + 1) & 1) * kW, wr);
+    if (!resident(k, p + 1)) wide_store_w<KS16, RQ>(lds + ((p + 1) & 1) * kW, wr);
     load_w(wr, k, p + 2);
     __syncthreads();
   };
@@ -516,18 +528,22 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
   const int x0v = x0[reqc];
   __builtin_amdgcn_sched_barrier(0);
   f32x4 gq = load_gq(0);
-  load_w(wr, 0, 0);
+  static_assert(kResident == 2, "the resident tiles are one pair");
+  wide_load_w<KS16, RQ>(wr, W2t, V, tile_at(0, qr) * kChunk);
   load_lane(even, 0, 0);
   load_lane(odd, 0, 1);
   load_e(live ? token_or_none(x0v, V) : -1);
   *reinterpret_cast<f32x4*>(&gsh[loc][8 * th + 4 * h]) = gq;
-  wide_store_w<KS16, RQ>(lds, wr);
+  wide_store_w<KS16, RQ>(lds + 2 * kW, wr);
+  wide_load_w<KS16, RQ>(wr, W2t, V, tile_at(0, qr + 1) * kChunk);
+  wide_store_w<KS16, RQ>(lds + 3 * kW, wr);
+  load_w(wr, 0, 0);
+  if (!resident(0, 0)) wide_store_w<KS16, RQ>(lds, wr);
   load_w(wr, 0, 1);
   __syncthreads();
 
   for (int k = 0; k < gamma; ++k) {
     lane_draw_init(dr);
-    bestSlot = 0;
     products(k, 0, even, accP, GcP);
     v0P = tile_at(k, 0) * kChunk;
     advance(k, 0);
@@ -543,15 +559,11 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     float bs = neg_inf();
     int bo = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f32x4 v = keepsh[(bestSlot * 4 + m) * T + threadIdx.x];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = v[i] + gsh[loc][4 * m + i];
-        if (sc > bs) {
-          bs = sc;
-          bo = 4 * m + i;
-        }
+    for (int c = 0; c < kGChunk; ++c) {
+      const float sc = bestL[c] + gsh[loc][c];
+      if (sc > bs) {
+        bs = sc;
+        bo = c;
       }
     }
     unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
