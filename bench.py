@@ -34,7 +34,8 @@ def source_hash() -> str:
     """Hash of the sources the sampling launch is built from."""
     h = hashlib.sha256()
     for rel in ("semi_ar_draft_round_amd/csrc/sample.hip", "semi_ar_draft_round_amd/csrc/bias_tile.hpp",
-                "semi_ar_draft_round_amd/csrc/common.hpp", "include/dspark.h"):
+                "semi_ar_draft_round_amd/csrc/wide_tile.hpp", "semi_ar_draft_round_amd/csrc/common.hpp",
+                "include/dspark.h"):
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(rel.encode() + fh.read())
     return h.hexdigest()[:16]
