@@ -30,6 +30,23 @@ the GPU scheduler, which must agree bit for bit):
   * the table must cover every batch the walk can reach: n_sps >= R (1 + gamma);
   * Theta_best is reported as float64: float(tau_fx) * 2^-50 * SPS(R + A),
     rounded in that order.
+
+The production variant (DSpark reading notes, "adapting Algorithm 1 to real
+hardware: two conflicts" and "the asynchronous fix, and why it stays
+lossless"; paper-breakdown page, "engineering challenges in production",
+inference paragraph): a stepped SPS curve can trap the early stop at a local
+peak, and graph replay needs the verification batch before the current
+round's confidences exist.  So the capacity K of round t is the optimum of a
+walk with NO early stop over the confidences of round t - 2, and round t
+fills exactly that many slots from its own, current ranking.  Readings:
+  * the whole-walk optimum is the smallest m with the largest Theta(m),
+    m = 0..M, compared exactly (an equal Theta does not buy more slots, as
+    with the early stop's tie rule);
+  * K counts admitted draft slots (A); the verification batch is R + K;
+  * a round whose pool holds fewer than K candidates admits all M of them;
+    K < 0 admits nothing;
+  * rounds 0 and 1 have no confidences two rounds back: their capacity is
+    given by the caller.
 """
 
 from __future__ import annotations
@@ -174,3 +191,71 @@ def brute_force_tau(c: np.ndarray, B: int) -> Fraction:
         if best is None or tau > best:
             best = tau
     return best
+
+
+def theta_walk_exact(c: np.ndarray, sps: np.ndarray) -> list:
+    """The ranked walk in Q50 without the early stop: [(m, tau_fx(m), Theta(m))]
+    for m = 0..M, Theta as an exact Fraction of the integer tau and the table
+    entry (step 3 of the optimality sketch, in the scheduler's arithmetic)."""
+    c = np.asarray(c, dtype=np.float32)
+    R, gamma = c.shape
+    sps = np.asarray(sps, dtype=np.float64)
+    if sps.shape[0] < R * (1 + gamma):
+        raise ValueError("step-speed table shorter than R*(1+gamma)")
+    pool = ranked_pool(c)
+    tau = R * ONE
+    out = [(0, tau, Fraction(tau) * Fraction(float(sps[R - 1])))]
+    for m, (v, r, j) in enumerate(pool, start=1):
+        tau += v
+        out.append((m, tau, Fraction(tau) * Fraction(float(sps[R + m - 1]))))
+    return out
+
+
+def _lengths_of_first(pool: list, A: int, R: int) -> np.ndarray:
+    """l_r = one more than the largest position of request r among the first A
+    ranked slots (the ranked prefix is prefix-closed per request, Lemma 1)."""
+    ell = [0] * R
+    for v, r, j in pool[:A]:
+        ell[r] = max(ell[r], j + 1)
+    return np.array(ell, dtype=np.int64)
+
+
+def admit_full_scan(c: np.ndarray, sps: np.ndarray) -> dict:
+    """The whole-walk optimum: A = the smallest m maximising Theta(m) over
+    m = 0..M.  Run on the confidences of round t - 2, its A is the capacity K
+    of round t."""
+    c = np.asarray(c, dtype=np.float32)
+    R = c.shape[0]
+    walk = theta_walk_exact(c, sps)
+    best_m, best_tau, best_theta = walk[0]
+    for m, tau, theta in walk[1:]:
+        if theta > best_theta:
+            best_m, best_tau, best_theta = m, tau, theta
+    pool = ranked_pool(c)
+    theta_best = float(best_tau) * 2.0 ** -Q * float(np.asarray(sps, dtype=np.float64)[R + best_m - 1])
+    return dict(ell=_lengths_of_first(pool, best_m, R), A=best_m, theta_best=theta_best, tau_fx=best_tau)
+
+
+def admit_capacity(c: np.ndarray, sps: np.ndarray, K: int) -> dict:
+    """Fill a capacity of K draft slots from the current ranking: the first
+    min(max(K, 0), M) ranked slots are admitted, whatever Theta does."""
+    c = np.asarray(c, dtype=np.float32)
+    R = c.shape[0]
+    walk = theta_walk_exact(c, sps)
+    M = len(walk) - 1
+    A = min(max(int(K), 0), M)
+    _, tau, _ = walk[A]
+    theta_best = float(tau) * 2.0 ** -Q * float(np.asarray(sps, dtype=np.float64)[R + A - 1])
+    return dict(ell=_lengths_of_first(ranked_pool(c), A, R), A=A, theta_best=theta_best, tau_fx=tau)
+
+
+def production_schedule(c_rounds: list, sps: np.ndarray, K_init: int) -> list:
+    """The asynchronous scheduler over a sequence of rounds: round t admits
+    with capacity K_t = admit_full_scan(c_{t-2}).A (K_init for t = 0, 1)."""
+    out = []
+    for t, c in enumerate(c_rounds):
+        K = K_init if t < 2 else admit_full_scan(c_rounds[t - 2], sps)["A"]
+        res = admit_capacity(c, sps, K)
+        res["K"] = K
+        out.append(res)
+    return out
