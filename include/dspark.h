@@ -11,6 +11,7 @@
  *   dspark_markov_sample  the sequential Markov-head sampling loop
  *   dspark_confidence     the confidence head (linear + sigmoid, temperature)
  *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
+ *   dspark_schedule_ex    the same with the production admission rules
  *   dspark_verify         rejection-sampling verification + residual draw
  *
  * Conventions shared by every entry point
@@ -157,6 +158,49 @@ dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r,
 dspark_status dspark_schedule(int R, int gamma, const float* c, const double* sps, int n_sps,
                               int32_t* ell, int32_t* admitted, double* theta_best,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* Admission rules of dspark_schedule_ex. */
+typedef enum {
+  DSPARK_SCHED_EARLY_STOP = 0,  /* Algorithm 1 as in dspark_schedule */
+  DSPARK_SCHED_WHOLE_WALK = 1,  /* no early stop: the best Theta over the whole ranked walk */
+  DSPARK_SCHED_CAPACITY = 2     /* fill a given capacity of K slots from the ranking */
+} dspark_sched_mode;
+
+/*
+ * dspark_schedule_ex — the scheduler with a choice of admission rule: the
+ * production (asynchronous) scheduler is two calls of it.
+ *
+ * Passage: notes, "adapting Algorithm 1 to real hardware: two conflicts" (a
+ * stepped SPS curve traps the early stop at a local peak; graph replay needs
+ * the verification batch before the round's confidences exist) and "the
+ * asynchronous fix, and why it stays lossless" (the capacity comes from the
+ * confidences of two rounds earlier with no early stop; the current round's
+ * ranking decides which slots fill it); step 9 of the notes' end-to-end loop.
+ * A production round t therefore runs
+ *   dspark_schedule_ex(..., c_t, ..., DSPARK_SCHED_CAPACITY, K_t, ell_t, ...)
+ *   dspark_schedule_ex(..., c_t, ..., DSPARK_SCHED_WHOLE_WALK, NULL, tmp, K_{t+2}, ...)
+ * where the `admitted` output of the second call is the capacity two rounds
+ * later (K_0 and K_1 are the caller's choice).
+ *
+ * Ranking, survival, Q50 quantisation, tie rules and exact Theta comparisons
+ * are those of dspark_schedule.  By mode, A (the number of admitted slots) is
+ *   DSPARK_SCHED_EARLY_STOP  the early stop of dspark_schedule;
+ *   DSPARK_SCHED_WHOLE_WALK  the smallest m in 0..M with the largest
+ *                            Theta(m) = tau_fx(m) * SPS(R + m), M the number
+ *                            of candidates (a_fx > 0);
+ *   DSPARK_SCHED_CAPACITY    min(max(*cap, 0), M).
+ *
+ *   c, sps, ell, admitted, theta_best, ws: as for dspark_schedule
+ *   mode       one of dspark_sched_mode; anything else -> DSPARK_EINVAL
+ *   cap        [1] i32 device pointer, read on the device: the capacity K.
+ *              Required (non-NULL) for DSPARK_SCHED_CAPACITY, ignored
+ *              otherwise.
+ *
+ * Limits: R * (1 + gamma) <= 8191.
+ */
+dspark_status dspark_schedule_ex(int R, int gamma, const float* c, const double* sps, int n_sps,
+                                 int mode, const int32_t* cap, int32_t* ell, int32_t* admitted,
+                                 double* theta_best, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_verify — lossless rejection-sampling verification.

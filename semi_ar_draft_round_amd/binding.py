@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 F32, BF16 = 0, 1
 CHUNK = 16   # tokens per chunk of the two-level Gumbel draw
 WS_SAMPLE, WS_SCHEDULE, WS_VERIFY = 0, 2, 3
+SCHED_EARLY_STOP, SCHED_WHOLE_WALK, SCHED_CAPACITY = 0, 1, 2
 
 _lib = None
 
@@ -31,6 +32,7 @@ _SIGNATURES = {
     "dspark_markov_sample": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_confidence": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "dspark_schedule": [_I, _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P],
+    "dspark_schedule_ex": [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_verify": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, _SZ, _P],
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
@@ -184,6 +186,27 @@ def dspark_schedule(c, sps, ell=None, admitted=None, theta_best=None):
     st = lib.dspark_schedule(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), _ptr(ell), _ptr(admitted),
                              _ptr(theta_best), None, 0, _stream())
     _raise("dspark_schedule", st)
+    return ell, admitted, theta_best
+
+
+def dspark_schedule_ex(c, sps, mode, cap=None, ell=None, admitted=None, theta_best=None):
+    """The scheduler with an admission rule (SCHED_EARLY_STOP, SCHED_WHOLE_WALK
+    or SCHED_CAPACITY; the last reads the capacity from the int32 [1] device
+    tensor `cap`).  Returns ell [R] int32, admitted [1] int32, theta_best [1]
+    float64."""
+    lib = load_library()
+    R, gamma = c.shape
+    dev = c.device
+    _check(c, "c", (R, gamma), (torch.float32,), dev)
+    _check(sps, "sps", (sps.shape[0],), (torch.float64,), dev)
+    if cap is not None:
+        _check(cap, "cap", (1,), (torch.int32,), dev)
+    ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
+    admitted = torch.empty(1, dtype=torch.int32, device=dev) if admitted is None else admitted
+    theta_best = torch.empty(1, dtype=torch.float64, device=dev) if theta_best is None else theta_best
+    st = lib.dspark_schedule_ex(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), int(mode), _ptr(cap), _ptr(ell),
+                                _ptr(admitted), _ptr(theta_best), None, 0, _stream())
+    _raise("dspark_schedule_ex", st)
     return ell, admitted, theta_best
 
 

@@ -20,8 +20,8 @@ hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, in
                              const float* T, float* c, float* z, hipStream_t s);
 // schedule.hip
 size_t schedule_workspace_bytes();
-hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int32_t* ell,
-                           int32_t* admitted, double* theta_best, hipStream_t s);
+hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
+                           int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s);
 // verify.hip
 size_t verify_workspace_bytes(int R, int gamma, int V);
 hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
@@ -149,21 +149,31 @@ dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r,
   return DSPARK_OK;
 }
 
-dspark_status dspark_schedule(int R, int gamma, const float* c, const double* sps, int n_sps,
-                              int32_t* ell, int32_t* admitted, double* theta_best, void* ws,
-                              size_t ws_bytes, void* stream) {
+dspark_status dspark_schedule_ex(int R, int gamma, const float* c, const double* sps, int n_sps, int mode,
+                                 const int32_t* cap, int32_t* ell, int32_t* admitted, double* theta_best,
+                                 void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
   if (R < 1 || gamma < 1 || gamma > kMaxGamma) return DSPARK_EINVAL;
   if (static_cast<int64_t>(R) * (1 + gamma) > kMaxSchedSlots) return DSPARK_EINVAL;
   if (n_sps < R * (1 + gamma)) return DSPARK_EINVAL;
   if (!c || !sps || !ell) return DSPARK_EINVAL;
+  if (mode != DSPARK_SCHED_EARLY_STOP && mode != DSPARK_SCHED_WHOLE_WALK && mode != DSPARK_SCHED_CAPACITY)
+    return DSPARK_EINVAL;
+  if (mode == DSPARK_SCHED_CAPACITY && !cap) return DSPARK_EINVAL;
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
-  if (schedule_launch(R, gamma, c, sps, ell, admitted, theta_best, static_cast<hipStream_t>(stream)) !=
+  if (schedule_launch(R, gamma, c, sps, mode, cap, ell, admitted, theta_best, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
+}
+
+dspark_status dspark_schedule(int R, int gamma, const float* c, const double* sps, int n_sps,
+                              int32_t* ell, int32_t* admitted, double* theta_best, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return dspark_schedule_ex(R, gamma, c, sps, n_sps, DSPARK_SCHED_EARLY_STOP, nullptr, ell, admitted,
+                            theta_best, ws, ws_bytes, stream);
 }
 
 dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,

@@ -17,8 +17,17 @@
 //      finds its place by one binary search in the partner run (keys are
 //      distinct);
 //   3. tau_fx(m) = R 2^50 + the exact integer prefix sum of the ranked a_fx;
-//   4. the first m with Theta(m) <= Theta(m-1) (exact comparison of
-//      tau_fx(m) * SPS(R+m) with tau_fx(m-1) * SPS(R+m-1)) gives A = m - 1;
+//   4. A, by mode:
+//      early stop  the first m with Theta(m) <= Theta(m-1) (exact comparison
+//                  of tau_fx(m) * SPS(R+m) with tau_fx(m-1) * SPS(R+m-1))
+//                  gives A = m - 1;
+//      whole walk  the smallest m with the largest Theta(m), m = 0..M: each
+//                  thread keeps the best of its ranked slots, then a wave
+//                  reduction and one pass over the wave winners, every
+//                  comparison exact (the production scheduler's capacity;
+//                  notes, "adapting Algorithm 1 to real hardware");
+//      capacity    A = min(max(K, 0), M) with K read from device memory (the
+//                  production scheduler's fill; notes, "the asynchronous fix");
 //   5. l_r = number of request r's slots ranked before position A.
 // Every step is integer or exact, so the result does not depend on the order
 // in which threads add things up.
@@ -98,13 +107,33 @@ __device__ int cmp_theta(uint64_t t1, double d1, uint64_t t2, double d2) {
   return cmp_products(t1, d1, t2, d2);
 }
 
+// A point of the ranked walk: admitting the first m slots gives tau_fx = t
+// and Theta = t * s (s = SPS(R + m)); m < 0 marks no point.
+struct WalkPoint {
+  uint64_t t;
+  double s;
+  int m;
+};
+
+// The better of two points: the larger Theta, the smaller m on equal Theta.
+__device__ __forceinline__ WalkPoint better(WalkPoint a, WalkPoint b) {
+  if (a.m < 0) return b;
+  if (b.m < 0) return a;
+  const int cmp = cmp_theta(a.t, a.s, b.t, b.s);
+  if (cmp != 0) return cmp > 0 ? a : b;
+  return a.m < b.m ? a : b;
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamma,
                                                                  const float* __restrict__ c,
                                                                  const double* __restrict__ sps,
+                                                                 int mode,
+                                                                 const int32_t* __restrict__ cap,
                                                                  int32_t* __restrict__ ell,
                                                                  int32_t* __restrict__ admitted,
                                                                  double* __restrict__ theta_best) {
   __shared__ uint64_t lds_keys[2 * kSchedMaxSlots];   // two buffers of n keys; reused for the scan afterwards
+  __shared__ WalkPoint wbest[kSchedThreads / kWave];
   const int tid = threadIdx.x;
   const int n = R * gamma;
 
@@ -208,22 +237,45 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
   uint64_t tau_prev = static_cast<uint64_t>(R) * kOne + excl;
   int my_first_drop = 0x7FFFFFFF;
   int my_count = 0;
+  // whole walk: this thread's best point (thread 0 also holds m = 0)
+  WalkPoint mine{static_cast<uint64_t>(R) * kOne, sps[R - 1], tid == 0 ? 0 : -1};
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     if (myk[t] >= cand_limit) break;
     ++my_count;
     const int m = tid * kPer + t + 1;               // admitting the m-th ranked slot
     const uint64_t tau = tau_prev + (kOne - (myk[t] >> 13));
-    if (my_first_drop == 0x7FFFFFFF &&
-        cmp_theta(tau, sps[R + m - 1], tau_prev, sps[R + m - 2]) <= 0)
-      my_first_drop = m;
+    const double s_m = sps[R + m - 1];
+    if (mode == DSPARK_SCHED_EARLY_STOP) {
+      if (my_first_drop == 0x7FFFFFFF && cmp_theta(tau, s_m, tau_prev, sps[R + m - 2]) <= 0) my_first_drop = m;
+    } else if (mode == DSPARK_SCHED_WHOLE_WALK) {
+      mine = better(mine, WalkPoint{tau, s_m, m});
+    }
     tau_prev = tau;
   }
   if (my_first_drop != 0x7FFFFFFF) atomicMin(&sh[0], my_first_drop);
   if (my_count) atomicAdd(&sh[1], my_count);
+  if (mode == DSPARK_SCHED_WHOLE_WALK) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      const WalkPoint other{__shfl_xor(mine.t, o), __shfl_xor(mine.s, o), __shfl_xor(mine.m, o)};
+      mine = better(mine, other);
+    }
+    if ((tid & (kWave - 1)) == 0) wbest[tid / kWave] = mine;
+  }
   __syncthreads();
   const int M = sh[1];
-  const int A = (sh[0] == 0x7FFFFFFF) ? M : sh[0] - 1;
+  int A;
+  if (mode == DSPARK_SCHED_WHOLE_WALK) {
+    WalkPoint b = wbest[0];
+#pragma unroll
+    for (int wv = 1; wv < kWaves; ++wv) b = better(b, wbest[wv]);
+    A = b.m;
+  } else if (mode == DSPARK_SCHED_CAPACITY) {
+    A = min(max(cap[0], 0), M);
+  } else {
+    A = (sh[0] == 0x7FFFFFFF) ? M : sh[0] - 1;
+  }
   // threshold key: the first ranked slot that is not admitted
   __syncthreads();
   uint64_t* thr = reinterpret_cast<uint64_t*>(sh + 4);
@@ -266,10 +318,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
 
 size_t schedule_workspace_bytes() { return 0; }
 
-hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int32_t* ell,
-                           int32_t* admitted, double* theta_best, hipStream_t s) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, R, gamma, c, sps, ell, admitted,
-                     theta_best);
+hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
+                           int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, R, gamma, c, sps, mode, cap, ell,
+                     admitted, theta_best);
   return hipGetLastError();
 }
 

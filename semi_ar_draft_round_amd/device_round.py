@@ -58,6 +58,15 @@ class DeviceRound:
     next_tok: torch.Tensor
     ws_sample: torch.Tensor
     ws_verify: torch.Tensor
+    # the production scheduler: this round's capacity, its fill, and the
+    # capacity its confidences set for two rounds later
+    cap: torch.Tensor
+    ell_p: torch.Tensor
+    admitted_p: torch.Tensor
+    theta_p: torch.Tensor
+    cap_next: torch.Tensor
+    ell_w: torch.Tensor
+    theta_w: torch.Tensor
 
 
 def to_device(inp, device="cuda:0") -> DeviceRound:
@@ -89,6 +98,13 @@ def to_device(inp, device="cuda:0") -> DeviceRound:
                               dtype=torch.uint8, device=dev),
         ws_verify=torch.empty(max(1, B.dspark_workspace_size(B.WS_VERIFY, R, gamma, V, r)),
                               dtype=torch.uint8, device=dev),
+        cap=torch.full((1,), R * gamma // 8, dtype=torch.int32, device=dev),
+        ell_p=torch.empty(R, dtype=torch.int32, device=dev),
+        admitted_p=torch.empty(1, dtype=torch.int32, device=dev),
+        theta_p=torch.empty(1, dtype=torch.float64, device=dev),
+        cap_next=torch.empty(1, dtype=torch.int32, device=dev),
+        ell_w=torch.empty(R, dtype=torch.int32, device=dev),
+        theta_w=torch.empty(1, dtype=torch.float64, device=dev),
     )
     return dr
 
@@ -103,6 +119,14 @@ def confidence(d: DeviceRound):
 
 def schedule(d: DeviceRound):
     B.dspark_schedule(d.c, d.sps, d.ell, d.admitted, d.theta_best)
+
+
+def schedule_production(d: DeviceRound):
+    """The asynchronous scheduler's two calls: fill this round's capacity
+    from the current ranking, then the whole-walk optimum of the current
+    confidences, which is the capacity two rounds later."""
+    B.dspark_schedule_ex(d.c, d.sps, B.SCHED_CAPACITY, d.cap, d.ell_p, d.admitted_p, d.theta_p)
+    B.dspark_schedule_ex(d.c, d.sps, B.SCHED_WHOLE_WALK, None, d.ell_w, d.cap_next, d.theta_w)
 
 
 def verify(d: DeviceRound):

@@ -111,6 +111,17 @@ def test_schedule_rejects_bad_arguments(lib):
     assert call(ptr=None) == EINVAL
 
 
+def test_schedule_ex_rejects_bad_arguments(lib):
+    def call(R=4, gamma=3, n_sps=16, mode=0, cap=FAKE, ptr=FAKE):
+        return lib.dspark_schedule_ex(R, gamma, ptr, ptr, n_sps, mode, cap, ptr, None, None, None, 0, None)
+    assert call(mode=3) == EINVAL               # unknown admission rule
+    assert call(mode=-1) == EINVAL
+    assert call(mode=2, cap=None) == EINVAL     # the capacity rule needs K
+    assert call(n_sps=15) == EINVAL
+    assert call(R=482, gamma=16, n_sps=10000) == EINVAL
+    assert call(ptr=None) == EINVAL
+
+
 def test_verify_rejects_bad_arguments(lib):
     def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
         args = [ptr] * 13
