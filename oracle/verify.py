@@ -24,6 +24,17 @@ Readings where the pages leave a choice:
   * if Z <= 0 (only when p_t and p_d coincide up to rounding) the draw falls
     back to p_t of the same row;
   * temperature 1 on both sides.
+
+Two more modes (SURVEY's verify modes; reading notes, the FAQ on greedy,
+temperature-0 decoding, and eq (8)-(8c) with the confidence-head paragraph):
+  * greedy verification: acceptance becomes an exact-match test of the draft
+    token against the target row's argmax; the prefix ends at the first
+    mismatch, and the next token is the argmax of the row there (the bonus
+    row when every admitted draft matched).  Reading: the argmax takes the
+    lowest token index among equal largest logits;
+  * the analytic acceptance c*_k = sum_v min(p_d^k(v), p_t^k(v)) of every
+    drafted position k (eq 8a; the confidence head's training label),
+    target row k against the drafter's distribution at position k.
 """
 
 from __future__ import annotations
@@ -120,3 +131,46 @@ def cdf_interval(res: np.ndarray, v: int):
     Z = cdf[-1]
     lo = cdf[v - 1] / Z if v > 0 else 0.0
     return lo, cdf[v] / Z
+
+
+def row_argmax(logits: np.ndarray) -> int:
+    """Lowest index among the largest entries."""
+    return int(np.argmax(logits))     # numpy returns the first maximum
+
+
+def verify_greedy(target, row0, x, ell) -> dict:
+    """Temperature-0 verification: n_r = the first i < l_r with
+    x_i != argmax(target row i) (l_r if none), next = argmax(target row n_r)."""
+    x = np.asarray(x)
+    R = x.shape[0]
+    n_acc = np.zeros(R, dtype=np.int64)
+    next_tok = np.zeros(R, dtype=np.int64)
+    for r in range(R):
+        L = int(ell[r])
+        n = L
+        for i in range(L):
+            if int(x[r, i]) != row_argmax(_target_row(target, row0, r, i)):
+                n = i
+                break
+        n_acc[r] = n
+        next_tok[r] = row_argmax(_target_row(target, row0, r, n))
+    return dict(n_acc=n_acc, next_tok=next_tok)
+
+
+def analytic_acceptance(target, row0, U, E, W2t, x0, x, lse=None) -> np.ndarray:
+    """c*[r, k] = sum_v min(p_d(v), p_t(v)) at every drafted position k, in
+    float64.  p_d is the drafter's softmax at position k (U_k plus the Markov
+    bias of x_{k-1}); its log-normaliser is computed here, or taken from
+    `lse` [R][gamma] when given (to check another implementation that is
+    handed the sampler's normalisers).  p_t is the softmax of target row k."""
+    R, gamma = np.asarray(x).shape
+    out = np.zeros((R, gamma), dtype=np.float64)
+    for r in range(R):
+        for k in range(gamma):
+            lt = np.asarray(_target_row(target, row0, r, k), dtype=np.float64)
+            pt = np.exp(lt - logsumexp(lt))
+            ld = draft_logits_at(U, E, W2t, x0, x, r, k).astype(np.float64)
+            nd = logsumexp(ld) if lse is None else float(lse[r, k])
+            pd = np.exp(ld - nd)
+            out[r, k] = float(np.minimum(pd, pt).sum())
+    return out
