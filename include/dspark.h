@@ -13,6 +13,8 @@
  *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
  *   dspark_schedule_ex    the same with the production admission rules
  *   dspark_verify         rejection-sampling verification + residual draw
+ *   dspark_verify_greedy  temperature-0 (exact-match) verification
+ *   dspark_acceptance     the analytic acceptance sum_v min(p_d, p_t) per position
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers to row-major arrays, 16-byte
@@ -66,7 +68,13 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 #define DSPARK_CHUNK 16
 
 /* Workspace selectors for dspark_workspace_size. */
-typedef enum { DSPARK_WS_SAMPLE = 0, DSPARK_WS_SCHEDULE = 2, DSPARK_WS_VERIFY = 3 } dspark_ws_kind;
+typedef enum {
+  DSPARK_WS_SAMPLE = 0,
+  DSPARK_WS_SCHEDULE = 2,
+  DSPARK_WS_VERIFY = 3,
+  DSPARK_WS_VERIFY_GREEDY = 4,
+  DSPARK_WS_ACCEPTANCE = 5
+} dspark_ws_kind;
 
 /*
  * dspark_markov_sample — the semi-autoregressive gamma-step sampling loop.
@@ -238,6 +246,56 @@ dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r,
                             const float* u_acc, const float* u_res,
                             int32_t* n_acc, int32_t* next_tok,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_verify_greedy — verification at temperature 0.
+ *
+ * Passage: notes, the FAQ on greedy (temperature-0) decoding: acceptance
+ * degenerates to an exact-match test of the draft token against the target's
+ * argmax token (the special case of the speculative-decoding framework).
+ * Reading: the argmax is the lowest token index among equal largest logits.
+ * n_acc[r] = the first i < ell[r] with x[r][i] != argmax(target row i), or
+ * ell[r] if every admitted draft matches; next_tok[r] = argmax of target row
+ * n_acc[r] (the bonus row when everything matched).  Bit-exact: only
+ * comparisons of the stored logits.
+ *
+ *   target, row0  as in dspark_verify
+ *   x       [R][gamma] i32 draft tokens (any value; one outside [0, V) never
+ *           matches)
+ *   ell     [R] i32 admitted lengths (read on the device)
+ *   n_acc   [R] i32 out; next_tok [R] i32 out
+ *   ws      workspace of dspark_workspace_size(DSPARK_WS_VERIFY_GREEDY, ...) bytes
+ *
+ * Limits: as dspark_markov_sample.
+ */
+dspark_status dspark_verify_greedy(dspark_dtype dt, int R, int gamma, int V, const void* target,
+                                   const int32_t* row0, const int32_t* x, const int32_t* ell,
+                                   int32_t* n_acc, int32_t* next_tok, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
+ * dspark_acceptance — the analytic acceptance of every drafted position.
+ *
+ * Passage: notes, eq (8) and its derivation (8a)-(8c), and the confidence-head
+ * paragraph (the head's training label is this closed form, not sampled
+ * accept/reject outcomes): c*[r][k] = sum_v min(p_d(v), p_t(v)) = 1 -
+ * 0.5 ||p_d - p_t||_1, with p_d the drafter's distribution at position k
+ * (U_k plus the Markov bias of x_{k-1}, normalised by lse[r][k]) and p_t the
+ * softmax of target row k.  One pass over the draft and target logits of all
+ * gamma positions (label generation and calibration checks).
+ *
+ *   target, row0  as in dspark_verify; rows 0 .. gamma-1 of every request are
+ *           read (row0[r] + k when packed)
+ *   U, W1, W2t, x0, x, lse  as in dspark_verify
+ *   c_star  [R][gamma] f32 out
+ *   ws      workspace of dspark_workspace_size(DSPARK_WS_ACCEPTANCE, ...) bytes
+ *
+ * Limits: as dspark_markov_sample.
+ */
+dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                                const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                                const int32_t* x0, const int32_t* x, const float* lse, float* c_star,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace a call needs (0 for an invalid shape).  Arguments that a
  * call does not take are ignored. */

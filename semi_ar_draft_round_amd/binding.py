@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 F32, BF16 = 0, 1
 CHUNK = 16   # tokens per chunk of the two-level Gumbel draw
-WS_SAMPLE, WS_SCHEDULE, WS_VERIFY = 0, 2, 3
+WS_SAMPLE, WS_SCHEDULE, WS_VERIFY, WS_VERIFY_GREEDY, WS_ACCEPTANCE = 0, 2, 3, 4, 5
 SCHED_EARLY_STOP, SCHED_WHOLE_WALK, SCHED_CAPACITY = 0, 1, 2
 
 _lib = None
@@ -35,6 +35,8 @@ _SIGNATURES = {
     "dspark_schedule_ex": [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_verify": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, _SZ, _P],
+    "dspark_verify_greedy": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_acceptance": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
     "dspark_status_string": [_I],
 }
@@ -242,3 +244,52 @@ def dspark_verify(target, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res, row0
                            ws.numel(), _stream())
     _raise("dspark_verify", st)
     return n_acc, next_tok
+
+
+def _target_check(target, row0, R, gamma, V, sdt, dev):
+    if row0 is None:
+        _check(target, "target", (R, gamma + 1, V), sdt, dev)
+    else:
+        _check(target, "target", (target.shape[0], V), sdt, dev)
+        _check(row0, "row0", (R,), (torch.int32,), dev)
+
+
+def dspark_verify_greedy(target, x, ell, row0=None, n_acc=None, next_tok=None, ws=None):
+    """n_acc [R], next_tok [R] int32: temperature-0 (exact-match) verification."""
+    lib = load_library()
+    R, gamma = x.shape
+    V = target.shape[-1]
+    dev = x.device
+    _target_check(target, row0, R, gamma, V, (torch.bfloat16, torch.float32), dev)
+    _check(x, "x", (R, gamma), (torch.int32,), dev)
+    _check(ell, "ell", (R,), (torch.int32,), dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev) if n_acc is None else n_acc
+    next_tok = torch.empty(R, dtype=torch.int32, device=dev) if next_tok is None else next_tok
+    ws = workspace(WS_VERIFY_GREEDY, R, gamma, V, 0, dev) if ws is None else ws
+    st = lib.dspark_verify_greedy(_dt(target), R, gamma, V, _ptr(target), _ptr(row0), _ptr(x), _ptr(ell),
+                                  _ptr(n_acc), _ptr(next_tok), _ptr(ws), ws.numel(), _stream())
+    _raise("dspark_verify_greedy", st)
+    return n_acc, next_tok
+
+
+def dspark_acceptance(target, U, W1, W2t, x0, x, lse, row0=None, c_star=None, ws=None):
+    """c_star [R][gamma] f32: sum_v min(p_d, p_t) at every drafted position."""
+    lib = load_library()
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    sdt = (U.dtype,)
+    _target_check(target, row0, R, gamma, V, sdt, dev)
+    _check(U, "U", (R, gamma, V), sdt, dev)
+    _check(W1, "W1", (V, r), sdt, dev)
+    _check(W2t, "W2t", (V, r), sdt, dev)
+    _check(x0, "x0", (R,), (torch.int32,), dev)
+    _check(x, "x", (R, gamma), (torch.int32,), dev)
+    _check(lse, "lse", (R, gamma), (torch.float32,), dev)
+    c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev) if c_star is None else c_star
+    ws = workspace(WS_ACCEPTANCE, R, gamma, V, r, dev) if ws is None else ws
+    st = lib.dspark_acceptance(_dt(U), R, gamma, V, r, _ptr(target), _ptr(row0), _ptr(U), _ptr(W1), _ptr(W2t),
+                               _ptr(x0), _ptr(x), _ptr(lse), _ptr(c_star), _ptr(ws), ws.numel(), _stream())
+    _raise("dspark_acceptance", st)
+    return c_star
+

@@ -23,6 +23,14 @@ size_t schedule_workspace_bytes();
 hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
                            int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s);
 // verify.hip
+size_t verify_greedy_workspace_bytes(int R, int gamma);
+size_t acceptance_workspace_bytes(int R, int gamma, int V);
+hipError_t verify_greedy_launch(dspark_dtype dt, int R, int gamma, int V, const void* target, const int32_t* row0,
+                                const int32_t* x, const int32_t* ell, int32_t* n_acc, int32_t* next_tok, void* ws,
+                                hipStream_t s);
+hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                             const int32_t* row0, const void* U, const void* W1, const void* W2t, const int32_t* x0,
+                             const int32_t* x, const float* lse, float* c_star, void* ws, hipStream_t s);
 size_t verify_workspace_bytes(int R, int gamma, int V);
 hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
                          const int32_t* row0, const void* U, const void* W1, const void* W2t,
@@ -112,6 +120,12 @@ size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r
     case DSPARK_WS_VERIFY:
       if (!draft_shape_ok(R, gamma, V)) return 0;
       return verify_workspace_bytes(R, gamma, V);
+    case DSPARK_WS_VERIFY_GREEDY:
+      if (!draft_shape_ok(R, gamma, V)) return 0;
+      return verify_greedy_workspace_bytes(R, gamma);
+    case DSPARK_WS_ACCEPTANCE:
+      if (!draft_shape_ok(R, gamma, V)) return 0;
+      return acceptance_workspace_bytes(R, gamma, V);
   }
   return 0;
 }
@@ -193,6 +207,38 @@ dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r, con
   if (st != DSPARK_OK) return st;
   if (verify_launch(dt, R, gamma, V, r, target, row0, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res,
                     n_acc, next_tok, ws, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_verify_greedy(dspark_dtype dt, int R, int gamma, int V, const void* target,
+                                   const int32_t* row0, const int32_t* x, const int32_t* ell, int32_t* n_acc,
+                                   int32_t* next_tok, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
+  if (!target || !x || !ell || !n_acc || !next_tok) return DSPARK_EINVAL;
+  if (!ws || ws_bytes < verify_greedy_workspace_bytes(R, gamma)) return DSPARK_EWORKSPACE;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (verify_greedy_launch(dt, R, gamma, V, target, row0, x, ell, n_acc, next_tok, ws,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                                const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                                const int32_t* x0, const int32_t* x, const float* lse, float* c_star, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
+  if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
+  if (!target || !U || !W1 || !W2t || !x0 || !x || !lse || !c_star) return DSPARK_EINVAL;
+  if (!ws || ws_bytes < acceptance_workspace_bytes(R, gamma, V)) return DSPARK_EWORKSPACE;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (acceptance_launch(dt, R, gamma, V, r, target, row0, U, W1, W2t, x0, x, lse, c_star, ws,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

@@ -77,7 +77,38 @@ constexpr int kLseThreads = 256;
 constexpr int kLseUnroll = 8;
 constexpr int kLseCompactR = 4096;
 
-template <typename Elt>
+// What a target-row part records, and which rows are needed:
+//   kPartLse     (max, sum exp) of rows 0..l_r, and the draft's target logit
+//   kPartArgmax  (largest logit, its lowest index) of rows 0..l_r (greedy)
+//   kPartLseAll  (max, sum exp) of rows 0..gamma-1 of every request (the
+//                analytic acceptance; ell is not read)
+enum PartMode { kPartLse = 0, kPartArgmax = 1, kPartLseAll = 2 };
+
+template <int MODE>
+__device__ __forceinline__ int needed_rows(const int32_t* ell, int r, int gamma) {
+  return MODE == kPartLseAll ? gamma : min(max(ell[r], 0), gamma) + 1;
+}
+
+// The larger logit, the lower index on equal logits.
+struct ArgMax {
+  float m;
+  int i;
+};
+__device__ __forceinline__ ArgMax argmax_combine(ArgMax a, ArgMax b) {
+  return (b.m > a.m || (b.m == a.m && b.i < a.i)) ? b : a;
+}
+__device__ __forceinline__ ArgMax block_reduce_argmax(ArgMax a, ArgMax* sh) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) a = argmax_combine(a, ArgMax{__shfl_xor(a.m, o), __shfl_xor(a.i, o)});
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sh[wave] = a;
+  __syncthreads();
+  ArgMax r = sh[0];
+  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) r = argmax_combine(r, sh[w]);
+  return r;
+}
+
+template <typename Elt, int MODE>
 __device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, int gamma, int V, int span,
                                                  const typename Elt::T* __restrict__ target,
                                                  const int32_t* __restrict__ row0, const int32_t* __restrict__ x,
@@ -88,6 +119,38 @@ __device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, in
   const typename Elt::T* t = target + row * V;
   const int v0 = sp * span;
   const int v1 = min(v0 + span, V);
+  if constexpr (MODE == kPartArgmax) {
+    // each thread visits its tokens in ascending order, so a strict > keeps
+    // the lowest index of its largest logit
+    ArgMax am{neg_inf(), 0x7FFFFFFF};
+    if ((V % N) == 0) {
+      for (int vb = v0 + static_cast<int>(threadIdx.x) * N; vb < v1; vb += kLseUnroll * N * kLseThreads) {
+        float e[kLseUnroll][N];
+#pragma unroll
+        for (int u = 0; u < kLseUnroll; ++u) {
+          const int v = vb + u * N * kLseThreads;
+          RowVec<Elt>::load(t + (v < v1 ? v : v0), e[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kLseUnroll; ++u) {
+          const int v = vb + u * N * kLseThreads;
+          if (v >= v1) break;
+#pragma unroll
+          for (int q = 0; q < N; ++q)
+            if (e[u][q] > am.m || am.i == 0x7FFFFFFF) am = ArgMax{e[u][q], v + q};
+        }
+      }
+    } else {
+      for (int v = v0 + static_cast<int>(threadIdx.x); v < v1; v += kLseThreads) {
+        const float e = Elt::load(t, v);
+        if (e > am.m || am.i == 0x7FFFFFFF) am = ArgMax{e, v};
+      }
+    }
+    am = block_reduce_argmax(am, reinterpret_cast<ArgMax*>(sh));
+    if (threadIdx.x == 0) part[ri * kLseSplits + sp] = make_float2(am.m, __int_as_float(am.i));
+    __syncthreads();   // sh is reused by the next item
+    return;
+  }
   Lse acc{neg_inf(), 0.f};
   if ((V % N) == 0) {
     for (int vb = v0 + static_cast<int>(threadIdx.x) * N; vb < v1; vb += kLseUnroll * N * kLseThreads) {
@@ -116,7 +179,7 @@ __device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, in
   acc = block_reduce_lse(acc, sh);
   if (threadIdx.x == 0) {
     part[ri * kLseSplits + sp] = make_float2(acc.M, acc.S);
-    if (sp == 0 && i < L) {
+    if (MODE == kPartLse && sp == 0 && i < L) {
       const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
       tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
     }
@@ -124,7 +187,7 @@ __device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, in
   __syncthreads();   // sh is reused by the next item
 }
 
-template <typename Elt>
+template <typename Elt, int MODE>
 __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gamma, int V,
                                                                   const typename Elt::T* __restrict__ target,
                                                                   const int32_t* __restrict__ row0,
@@ -141,7 +204,7 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
     const int per = ceil_div(R, kLseThreads);
     const int b0 = min(static_cast<int>(threadIdx.x) * per, R), b1 = min(b0 + per, R);
     int mine = 0;
-    for (int q = b0; q < b1; ++q) mine += min(max(ell[q], 0), gamma) + 1;
+    for (int q = b0; q < b1; ++q) mine += needed_rows<MODE>(ell, q, gamma);
     __shared__ int wtot[kLseThreads / kWave];
     int incl = mine;
 #pragma unroll
@@ -160,7 +223,7 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
     if (threadIdx.x == 0) pref[R] = total;
     for (int q = b0; q < b1; ++q) {
       pref[q] = run;
-      run += min(max(ell[q], 0), gamma) + 1;
+      run += needed_rows<MODE>(ell, q, gamma);
     }
     __syncthreads();
     const int64_t items = static_cast<int64_t>(pref[R]) * kLseSplits;
@@ -175,8 +238,8 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
         else
           hi = mid - 1;
       }
-      const int L = min(max(ell[lo], 0), gamma);
-      target_part_item<Elt>(lo, act - pref[lo], sp, L, gamma, V, span, target, row0, x, part, tx, sh);
+      const int L = needed_rows<MODE>(ell, lo, gamma) - 1;
+      target_part_item<Elt, MODE>(lo, act - pref[lo], sp, L, gamma, V, span, target, row0, x, part, tx, sh);
     }
   } else {
     const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
@@ -185,9 +248,9 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
       const int64_t ri = it / kLseSplits;
       const int r = static_cast<int>(ri / (gamma + 1));
       const int i = static_cast<int>(ri % (gamma + 1));
-      const int L = min(max(ell[r], 0), gamma);
+      const int L = needed_rows<MODE>(ell, r, gamma) - 1;
       if (i > L) continue;   // uniform across the work group
-      target_part_item<Elt>(r, i, sp, L, gamma, V, span, target, row0, x, part, tx, sh);
+      target_part_item<Elt, MODE>(r, i, sp, L, gamma, V, span, target, row0, x, part, tx, sh);
     }
   }
 }
@@ -234,6 +297,41 @@ __global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int
   if (lane == 0) n_acc[r] = first_fail;
 }
 
+// One wave per request, greedy verification: lane i merges the argmax parts
+// of target row i (rows 0..l_r); the first draft that differs from its row's
+// argmax ends the accepted prefix, and the argmax of the row where it ends
+// is the next token.
+__global__ __launch_bounds__(256) void verify_greedy_accept(int R, int gamma, const int32_t* __restrict__ ell,
+                                                            const int32_t* __restrict__ x,
+                                                            const float2* __restrict__ part,
+                                                            int32_t* __restrict__ n_acc, int32_t* __restrict__ next_tok) {
+  const int r = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= R) return;
+  const int L = min(max(ell[r], 0), gamma);
+  auto row_argmax = [&](int i) {
+    const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + i;
+    ArgMax a{neg_inf(), 0x7FFFFFFF};
+#pragma unroll
+    for (int sp = 0; sp < kLseSplits; ++sp) {
+      const float2 pv = part[ri * kLseSplits + sp];
+      a = argmax_combine(a, ArgMax{pv.x, __float_as_int(pv.y)});
+    }
+    return a.i;
+  };
+  int first_fail = L;
+  for (int i0 = 0; i0 < L; i0 += kWave) {   // gamma <= 64: at most one full pass
+    const int i = i0 + lane;
+    const bool fail = i < L && x[static_cast<int64_t>(r) * gamma + i] != row_argmax(i);
+    const unsigned long long b = __ballot(fail);
+    if (b != 0ull && first_fail == L) first_fail = i0 + __ffsll(static_cast<long long>(b)) - 1;
+  }
+  if (lane == 0) {
+    n_acc[r] = first_fail;
+    next_tok[r] = row_argmax(first_fail);
+  }
+}
+
 // ------------------------------------------------------- residual chunk masses
 
 // Row stride of the per-request chunk-mass arrays: ceil(V/16) rounded up to
@@ -270,6 +368,32 @@ __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, i
   return rr;
 }
 
+// Row rho = r gamma + k of the analytic acceptance: target row k of request
+// r against the drafter's distribution at position k (U row rho, the Markov
+// bias of x_{k-1}, the sampler's normaliser lse[rho]); the target
+// normaliser is merged from the row's parts.
+__device__ __forceinline__ ResidualRow acceptance_row(int rho, int gamma, int V, const int32_t* row0,
+                                                      const int32_t* x0, const int32_t* x, const float2* part,
+                                                      const float* lse) {
+  const int r = rho / gamma, k = rho % gamma;
+  const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + k;
+  ResidualRow rr;
+  rr.trow = row0 ? static_cast<int64_t>(row0[r]) + k : ri;
+  rr.urow = rho;
+  Lse acc{neg_inf(), 0.f};
+#pragma unroll
+  for (int sp = 0; sp < kLseSplits; ++sp) {
+    const float2 pv = part[ri * kLseSplits + sp];
+    acc = lse_combine(acc, Lse{pv.x, pv.y});
+  }
+  rr.lt = acc.M + logf(acc.S);
+  rr.ld = lse[rho];
+  rr.prev = token_or_none(k == 0 ? x0[r] : x[rho - 1], V);
+  rr.rej = true;
+  rr.live = true;
+  return rr;
+}
+
 // The residual row of every request, one sweep over the vocabulary in
 // 64-token tiles with the sampler's 32x32x16 layout: work group = 2 RQ waves
 // over 32 RQ requests, wave = (token half th, request quarter rq), lane (h, j)
@@ -281,25 +405,32 @@ __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, i
 // p_t (the bonus row) and skip nothing: their draft part is computed on U
 // row 0 and ignored.  W2t tiles go through registers into a double-buffered
 // LDS area one tile ahead; the lane's own logits are loaded two tiles ahead.
-template <int RQ, int KS16, bool VEC>
+//
+// ACC: the same sweep over the R gamma rows of the analytic acceptance
+// (acceptance_row); each lane adds up min(p_t, p_d) over its tokens, and the
+// request's four lanes leave one partial per work group in accp[rho][gx].
+template <int RQ, int KS16, bool VEC, bool ACC>
 __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     int R, int gamma, int V, const uint16_t* __restrict__ target, const int32_t* __restrict__ row0,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2t,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
-    float* __restrict__ csum, float* __restrict__ psum) {
+    float* __restrict__ csum, float* __restrict__ psum, const float2* __restrict__ part,
+    float* __restrict__ accp) {
   constexpr float kL2e = 1.4426950408889634f;
   constexpr int NROWS = 32 * RQ;
   constexpr int kW = wide_tile_bytes<KS16>();
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
+  __shared__ float accsh[ACC ? NROWS : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int th = wave & 1;
   const int rq = wave >> 1;
   const int j = lane & 31;
   const int h = lane >> 5;
+  const int nrows = ACC ? R * gamma : R;
   const int req = static_cast<int>(blockIdx.y) * NROWS + rq * 32 + j;
-  const bool live = req < R;
+  const bool live = req < nrows;
   const int lofs = 32 * th + 16 * h;
   const int nTiles = (V + kChunk - 1) / kChunk;
   const int nG = (V + kGChunk - 1) / kGChunk;
@@ -310,7 +441,9 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   const auto clampc = [&](int it) { return it < nT ? it : nT - 1; };
   const auto tile_of = [&](int it) { return static_cast<int>(blockIdx.x) + it * static_cast<int>(gridDim.x); };
 
-  const ResidualRow rr = residual_row(min(req, R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  const ResidualRow rr = ACC ? acceptance_row(min(req, nrows - 1), gamma, V, row0, x0, x, part, lse)
+                             : residual_row(min(req, R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  float mn = 0.f;   // ACC: the lane's sum of min(p_t, p_d)
   const uint16_t* trow = target + rr.trow * V;
   const uint16_t* urow = U + (rr.rej ? rr.urow : 0) * V;
   const float lt2 = rr.lt * kL2e;
@@ -371,13 +504,21 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     for (int q = 0; q < 16; ++q) {
       const float pt = __builtin_amdgcn_exp2f(fmaf(tv[q], kL2e, -lt2));
       const float pd = __builtin_amdgcn_exp2f(fmaf(acc[q] + acc2[q], kL2e, -ld2));
-      ps += pt;
-      cs += rr.rej ? fmaxf(0.f, pt - pd) : pt;
+      if constexpr (ACC) {
+        cs += fminf(pt, pd);
+      } else {
+        ps += pt;
+        cs += rr.rej ? fmaxf(0.f, pt - pd) : pt;
+      }
     }
-    const int c16 = 4 * tile_of(it) + 2 * th + h;
-    if (live && c16 < nG) {
-      csum[static_cast<int64_t>(req) * ldm + c16] = cs;
-      psum[static_cast<int64_t>(req) * ldm + c16] = ps;
+    if constexpr (ACC) {
+      mn += cs;
+    } else {
+      const int c16 = 4 * tile_of(it) + 2 * th + h;
+      if (live && c16 < nG) {
+        csum[static_cast<int64_t>(req) * ldm + c16] = cs;
+        psum[static_cast<int64_t>(req) * ldm + c16] = ps;
+      }
     }
     wide_store_w<KS16, RQ>(lds + ((it + 1) & 1) * kW, wr);
     wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(it + 2)) * kChunk);
@@ -389,6 +530,13 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     step(it + 1, odd);
   }
   if (it < nT) step(it, even);
+  if constexpr (ACC) {
+    const float t = mn + __shfl_xor(mn, 32);   // the request's two lanes of this token half
+    if (th == 1 && h == 0) accsh[rq * 32 + j] = t;
+    __syncthreads();
+    if (th == 0 && h == 0 && live)
+      accp[static_cast<int64_t>(req) * gridDim.x + blockIdx.x] = t + accsh[rq * 32 + j];
+  }
 }
 
 __global__ __launch_bounds__(64) void verify_residual_f32(
@@ -429,6 +577,46 @@ __global__ __launch_bounds__(64) void verify_residual_f32(
     csum[static_cast<int64_t>(req) * ldm + c16] = res;
     psum[static_cast<int64_t>(req) * ldm + c16] = pt;
   }
+}
+
+// fp32 storage, the analytic acceptance: one wave per (row rho, 64-token
+// tile), plain FMA bias; the wave's sum of min(p_t, p_d) is the partial
+// accp[rho][tile].
+__global__ __launch_bounds__(64) void verify_acceptance_f32(
+    int R, int gamma, int V, int r, const float* __restrict__ target, const int32_t* __restrict__ row0,
+    const float* __restrict__ U, const float* __restrict__ W1, const float* __restrict__ W2t,
+    const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
+    const float2* __restrict__ part, float* __restrict__ accp) {
+  const int rho = blockIdx.x;
+  const int tile = blockIdx.y;
+  const int lane = threadIdx.x;
+  const ResidualRow rr = acceptance_row(rho, gamma, V, row0, x0, x, part, lse);
+  const int v = tile * kChunk + lane;
+  float mn = 0.f;
+  if (v < V) {
+    const float pt = __expf(target[rr.trow * V + v] - rr.lt);
+    float b = 0.f;
+    if (rr.prev >= 0) {
+      const float* e = W1 + static_cast<int64_t>(rr.prev) * r;
+      const float* w = W2t + static_cast<int64_t>(v) * r;
+      for (int i = 0; i < r; ++i) b = fmaf(e[i], w[i], b);
+    }
+    mn = fminf(pt, __expf(U[rr.urow * V + v] + b - rr.ld));
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mn += __shfl_xor(mn, o);
+  if (lane == 0) accp[static_cast<int64_t>(rho) * gridDim.y + tile] = mn;
+}
+
+// c*[rho] = the sum of its partials, in order.
+__global__ __launch_bounds__(256) void acceptance_finish(int rows, int parts, const float* __restrict__ accp,
+                                                         float* __restrict__ c_star) {
+  const int rho = blockIdx.x * blockDim.x + threadIdx.x;
+  if (rho >= rows) return;
+  const float* p = accp + static_cast<int64_t>(rho) * parts;
+  float t = 0.f;
+  for (int b = 0; b < parts; ++b) t += p[b];
+  c_star[rho] = t;
 }
 
 // -------------------------------------------------------------------- select
@@ -626,39 +814,54 @@ static VerifyWs carve(void* ws, int R, int gamma, int V) {
 
 int compute_units();   // abi.hip
 
-template <int RQ, int KS16>
-static void launch_residual_wide(int R, int gamma, int V, const void* target, const int32_t* row0,
-                                 const void* U, const void* W1, const void* W2t, const int32_t* x0,
-                                 const int32_t* x, const float* lse, const int32_t* ell,
-                                 const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
-  const int nTiles = ceil_div(V, kChunk);
-  const int groups = ceil_div(R, 32 * RQ);
+// Arguments of one residual or acceptance sweep.
+struct SweepArgs {
+  int R, gamma, V;
+  const void *target, *U, *W1, *W2t;
+  const int32_t *row0, *x0, *x, *ell, *n_acc;
+  const float* lse;
+  const float* lse_t;
+  float *csum, *psum;
+  const float2* part;
+  float* accp;
+};
+
+// Launches the 32x32x16 sweep over `rows` rows (R residual rows, or R gamma
+// acceptance rows) and returns its work groups along the vocabulary.
+template <int RQ, int KS16, bool ACC>
+static int launch_residual_wide(const SweepArgs& a, int rows, hipStream_t s) {
+  const int nTiles = ceil_div(a.V, kChunk);
+  const int groups = ceil_div(rows, 32 * RQ);
   int gx = compute_units() / groups;
   gx = gx < 1 ? 1 : (gx > nTiles ? nTiles : gx);
   dim3 grid(gx, groups);
-  if (V % kGChunk == 0)
-    hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, true>), grid, dim3(wide_threads<RQ>()), 0, s, R, gamma, V,
-                       static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
-                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
-                       ell, n_acc, w.lse_t, w.csum, w.psum);
+  const auto b16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
+  if (a.V % kGChunk == 0)
+    hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, true, ACC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R,
+                       a.gamma, a.V, b16(a.target), a.row0, b16(a.U), b16(a.W1), b16(a.W2t), a.x0, a.x, a.lse,
+                       a.ell, a.n_acc, a.lse_t, a.csum, a.psum, a.part, a.accp);
   else
-    hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, false>), grid, dim3(wide_threads<RQ>()), 0, s, R, gamma, V,
-                       static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
-                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
-                       ell, n_acc, w.lse_t, w.csum, w.psum);
+    hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, false, ACC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R,
+                       a.gamma, a.V, b16(a.target), a.row0, b16(a.U), b16(a.W1), b16(a.W2t), a.x0, a.x, a.lse,
+                       a.ell, a.n_acc, a.lse_t, a.csum, a.psum, a.part, a.accp);
+  return gx;
 }
 
-template <int KS16>
-static void launch_residual_wide_ks(int R, int gamma, int V, const void* target, const int32_t* row0,
-                                    const void* U, const void* W1, const void* W2t, const int32_t* x0,
-                                    const int32_t* x, const float* lse, const int32_t* ell,
-                                    const int32_t* n_acc, const VerifyWs& w, hipStream_t s) {
-  if (R <= 32)
-    launch_residual_wide<1, KS16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
-  else if (R <= 64)
-    launch_residual_wide<2, KS16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
-  else
-    launch_residual_wide<4, KS16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s);
+template <int KS16, bool ACC>
+static int launch_residual_wide_ks(const SweepArgs& a, int rows, hipStream_t s) {
+  if (rows <= 32) return launch_residual_wide<1, KS16, ACC>(a, rows, s);
+  if (rows <= 64) return launch_residual_wide<2, KS16, ACC>(a, rows, s);
+  return launch_residual_wide<4, KS16, ACC>(a, rows, s);
+}
+
+template <bool ACC>
+static int launch_residual_wide_r(const SweepArgs& a, int r, int rows, hipStream_t s) {
+  switch (r / 32) {
+    case 1: return launch_residual_wide_ks<2, ACC>(a, rows, s);
+    case 2: return launch_residual_wide_ks<4, ACC>(a, rows, s);
+    case 4: return launch_residual_wide_ks<8, ACC>(a, rows, s);
+    default: return launch_residual_wide_ks<16, ACC>(a, rows, s);
+  }
 }
 
 hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
@@ -671,22 +874,19 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
   const int gridp = static_cast<int>(items < 4LL * compute_units() ? items : 4LL * compute_units());
   if (dt == DSPARK_BF16)
-    hipLaunchKernelGGL(verify_target_part<BF16>, dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
+    hipLaunchKernelGGL((verify_target_part<BF16, kPartLse>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
                        static_cast<const uint16_t*>(target), row0, x, ell, w.part, w.tx);
   else
-    hipLaunchKernelGGL(verify_target_part<F32>, dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
+    hipLaunchKernelGGL((verify_target_part<F32, kPartLse>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
                        static_cast<const float*>(target), row0, x, ell, w.part, w.tx);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(verify_accept, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, ell, w.part, w.tx, logit, lse,
                      u_acc, w.lse_t, n_acc);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (dt == DSPARK_BF16) {
-    switch (r / 32) {
-      case 1: launch_residual_wide_ks<2>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-      case 2: launch_residual_wide_ks<4>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-      case 4: launch_residual_wide_ks<8>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-      default: launch_residual_wide_ks<16>(R, gamma, V, target, row0, U, W1, W2t, x0, x, lse, ell, n_acc, w, s); break;
-    }
+    const SweepArgs a{R, gamma, V, target, U, W1, W2t, row0, x0, x, ell, n_acc, lse, w.lse_t, w.csum, w.psum,
+                      nullptr, nullptr};
+    launch_residual_wide_r<false>(a, r, R, s);
   } else {
     hipLaunchKernelGGL(verify_residual_f32, dim3(ceil_div(V, kChunk), R), dim3(64), 0, s, R, gamma, V, r,
                        static_cast<const float*>(target), row0, static_cast<const float*>(U),
@@ -704,6 +904,72 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                        static_cast<const float*>(target), row0, static_cast<const float*>(U),
                        static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, ell,
                        n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ greedy / acceptance
+
+size_t verify_greedy_workspace_bytes(int R, int gamma) {
+  return align256(sizeof(float2) * R * (gamma + 1) * kLseSplits);
+}
+
+size_t acceptance_workspace_bytes(int R, int gamma, int V) {
+  return align256(sizeof(float2) * R * (gamma + 1) * kLseSplits) +
+         align256(sizeof(float) * static_cast<size_t>(R) * gamma * ceil_div(V, kChunk));
+}
+
+static int part_grid(int R, int gamma) {
+  const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
+  return static_cast<int>(items < 4LL * compute_units() ? items : 4LL * compute_units());
+}
+
+hipError_t verify_greedy_launch(dspark_dtype dt, int R, int gamma, int V, const void* target, const int32_t* row0,
+                                const int32_t* x, const int32_t* ell, int32_t* n_acc, int32_t* next_tok, void* ws,
+                                hipStream_t s) {
+  float2* part = static_cast<float2*>(ws);
+  const int gridp = part_grid(R, gamma);
+  if (dt == DSPARK_BF16)
+    hipLaunchKernelGGL((verify_target_part<BF16, kPartArgmax>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, x, ell, part, nullptr);
+  else
+    hipLaunchKernelGGL((verify_target_part<F32, kPartArgmax>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
+                       static_cast<const float*>(target), row0, x, ell, part, nullptr);
+  hipError_t err;
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(verify_greedy_accept, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, ell, x, part, n_acc,
+                     next_tok);
+  return hipGetLastError();
+}
+
+hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                             const int32_t* row0, const void* U, const void* W1, const void* W2t, const int32_t* x0,
+                             const int32_t* x, const float* lse, float* c_star, void* ws, hipStream_t s) {
+  float2* part = static_cast<float2*>(ws);
+  float* accp = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         align256(sizeof(float2) * R * (gamma + 1) * kLseSplits));
+  const int gridp = part_grid(R, gamma);
+  if (dt == DSPARK_BF16)
+    hipLaunchKernelGGL((verify_target_part<BF16, kPartLseAll>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma,
+                       V, static_cast<const uint16_t*>(target), row0, nullptr, nullptr, part, nullptr);
+  else
+    hipLaunchKernelGGL((verify_target_part<F32, kPartLseAll>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma,
+                       V, static_cast<const float*>(target), row0, nullptr, nullptr, part, nullptr);
+  hipError_t err;
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int rows = R * gamma;
+  int parts;
+  if (dt == DSPARK_BF16) {
+    const SweepArgs a{R, gamma, V, target, U, W1, W2t, row0, x0, x, nullptr, nullptr, lse, nullptr, nullptr,
+                      nullptr, part, accp};
+    parts = launch_residual_wide_r<true>(a, r, rows, s);
+  } else {
+    parts = ceil_div(V, kChunk);
+    hipLaunchKernelGGL(verify_acceptance_f32, dim3(rows, parts), dim3(64), 0, s, R, gamma, V, r,
+                       static_cast<const float*>(target), row0, static_cast<const float*>(U),
+                       static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, part, accp);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(acceptance_finish, dim3(ceil_div(rows, 256)), dim3(256), 0, s, rows, parts, accp, c_star);
   return hipGetLastError();
 }
 

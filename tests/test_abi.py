@@ -122,6 +122,27 @@ def test_schedule_ex_rejects_bad_arguments(lib):
     assert call(ptr=None) == EINVAL
 
 
+def test_verify_greedy_rejects_bad_arguments(lib):
+    def call(dt=1, R=2, gamma=3, V=500, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.dspark_verify_greedy(dt, R, gamma, V, ptr, None, ptr, ptr, ptr, ptr, ws, ws_bytes, None)
+    assert call(dt=5) == EDTYPE
+    assert call(V=0) == EINVAL
+    assert call(gamma=65) == EINVAL
+    assert call(ptr=None) == EINVAL
+    assert call(ws_bytes=8) == EWORKSPACE
+
+
+def test_acceptance_rejects_bad_arguments(lib):
+    def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        args = [ptr] * 8
+        return lib.dspark_acceptance(dt, R, gamma, V, r, args[0], None, *args[1:], ws, ws_bytes, None)
+    assert call(dt=5) == EDTYPE
+    assert call(V=0) == EINVAL
+    assert call(r=48) == EDTYPE
+    assert call(ptr=None) == EINVAL
+    assert call(ws_bytes=8) == EWORKSPACE
+
+
 def test_verify_rejects_bad_arguments(lib):
     def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
         args = [ptr] * 13
