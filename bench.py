@@ -149,7 +149,8 @@ def main():
     graphs = {name: [capture(fn, d) for d in rounds]
               for name, fn in (("round", DR.run_round), ("sample", DR.sample),
                                ("confidence", DR.confidence), ("schedule", DR.schedule),
-                               ("verify", DR.verify), ("schedule_production", DR.schedule_production))}
+                               ("verify", DR.verify), ("schedule_production", DR.schedule_production),
+                               ("verify_greedy", DR.verify_greedy), ("acceptance", DR.acceptance))}
     torch.cuda.synchronize()
     log("[bench] graphs captured")
 
@@ -175,8 +176,13 @@ def main():
         log(f"[bench] {name}: {parts[name]:.1f} us")
     # the production (asynchronous) scheduler's two calls, timed on their
     # own: not part of the round above, which runs Algorithm 1
-    production_us = timed("schedule_production", max(args.steps, 10), 2) * 1e3
-    log(f"[bench] schedule_production: {production_us:.1f} us")
+    # the other modes, each timed on its own and outside the round: the
+    # production (asynchronous) scheduler's two calls, greedy verification of
+    # the round's drafts, and the analytic acceptance of all its positions
+    modes = {}
+    for name in ("schedule_production", "verify_greedy", "acceptance"):
+        modes[name] = timed(name, max(args.steps, 10), 2) * 1e3
+        log(f"[bench] {name}: {modes[name]:.1f} us")
 
     # outputs of the last replay of input set 0, as workload facts
     graphs["round"][0].replay()
@@ -203,7 +209,7 @@ def main():
                    "global_batch": w.R, "admitted": out["A"], "accepted": int(out["n_acc"].sum()),
                    "parallelism": "none (1 GPU)"},
         "parts_us": {k: round(v, 2) for k, v in parts.items()},
-        "schedule_production_us": round(production_us, 2),
+        "modes_us": {k: round(v, 2) for k, v in modes.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -67,6 +67,12 @@ class DeviceRound:
     cap_next: torch.Tensor
     ell_w: torch.Tensor
     theta_w: torch.Tensor
+    # greedy verification and the analytic acceptance
+    n_acc_g: torch.Tensor
+    next_tok_g: torch.Tensor
+    c_star: torch.Tensor
+    ws_greedy: torch.Tensor
+    ws_accept: torch.Tensor
 
 
 def to_device(inp, device="cuda:0") -> DeviceRound:
@@ -105,6 +111,13 @@ def to_device(inp, device="cuda:0") -> DeviceRound:
         cap_next=torch.empty(1, dtype=torch.int32, device=dev),
         ell_w=torch.empty(R, dtype=torch.int32, device=dev),
         theta_w=torch.empty(1, dtype=torch.float64, device=dev),
+        n_acc_g=torch.empty(R, dtype=torch.int32, device=dev),
+        next_tok_g=torch.empty(R, dtype=torch.int32, device=dev),
+        c_star=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+        ws_greedy=torch.empty(max(1, B.dspark_workspace_size(B.WS_VERIFY_GREEDY, R, gamma, V, r)),
+                              dtype=torch.uint8, device=dev),
+        ws_accept=torch.empty(max(1, B.dspark_workspace_size(B.WS_ACCEPTANCE, R, gamma, V, r)),
+                              dtype=torch.uint8, device=dev),
     )
     return dr
 
@@ -127,6 +140,16 @@ def schedule_production(d: DeviceRound):
     confidences, which is the capacity two rounds later."""
     B.dspark_schedule_ex(d.c, d.sps, B.SCHED_CAPACITY, d.cap, d.ell_p, d.admitted_p, d.theta_p)
     B.dspark_schedule_ex(d.c, d.sps, B.SCHED_WHOLE_WALK, None, d.ell_w, d.cap_next, d.theta_w)
+
+
+def verify_greedy(d: DeviceRound):
+    """Temperature-0 verification of the round's drafts and admitted lengths."""
+    B.dspark_verify_greedy(d.target, d.x, d.ell, n_acc=d.n_acc_g, next_tok=d.next_tok_g, ws=d.ws_greedy)
+
+
+def acceptance(d: DeviceRound):
+    """The analytic acceptance of every drafted position of the round."""
+    B.dspark_acceptance(d.target, d.U, d.W1, d.W2t, d.x0, d.x, d.lse, c_star=d.c_star, ws=d.ws_accept)
 
 
 def verify(d: DeviceRound):

@@ -3,12 +3,13 @@ ACC_TOL of the float64 oracle) through the C ABI: small rounds spanning
 several tiles and ragged tails, bf16 and fp32 storage, packed target rows,
 argmax ties, and full-size workloads on sampled requests.
 
-ACC_TOL: the kernel's target normaliser is an fp32 log-sum-exp (relative
-error of a few 2^-24 on |lse| ~ 12, so p_t within ~1e-5 relative), its
+ACC_TOL: the kernel's target normaliser is an fp32 log-sum-exp (a few
+2^-24 relative on |lse| ~ 12, so p_t within ~1e-6 relative), its
 exponentials are fp32, and the sum of up to 1.5e5 terms is accumulated in
-fp32 per lane and then across partials (~1e-5); c* <= 1, so 5e-5 absolute
-covers both with margin.  The drafter's normaliser is the sampler's own
-output, fed to both sides."""
+fp32, sixteen per lane per tile, then per lane over tiles and across
+partials (a few 1e-7 at these sizes); c* <= 1, so 1e-5 absolute leaves an
+order of magnitude over the largest error seen (6e-7).  The drafter's
+normaliser is the sampler's own output, fed to both sides."""
 
 import sys
 
@@ -22,7 +23,7 @@ from semi_ar_draft_round_amd import workloads as W
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-ACC_TOL = 5e-5
+ACC_TOL = 1e-5
 
 
 def say(*a):
