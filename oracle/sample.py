@@ -55,11 +55,17 @@ def markov_bias(E: np.ndarray, W2t: np.ndarray, prev: np.ndarray) -> np.ndarray:
 def sample_position(U_k: np.ndarray, E: np.ndarray, W2t: np.ndarray, prev: np.ndarray,
                     G_k: np.ndarray, g_k: np.ndarray) -> dict:
     """One position for every request.  U_k [R][V], G_k [R][nC], g_k [R][C]."""
+    return sample_with_bias(U_k, markov_bias(E, W2t, prev), G_k, g_k)
+
+
+def sample_with_bias(U_k: np.ndarray, B_k: np.ndarray, G_k: np.ndarray, g_k: np.ndarray) -> dict:
+    """One position for every request, given its bias B_k [R][V] (eq 4 with
+    any head's B_k)."""
     R, V = U_k.shape
     C = g_k.shape[1]
     nC = G_k.shape[1]
     assert nC == (V + C - 1) // C
-    l = U_k + markov_bias(E, W2t, prev)          # exponent of eq (4)
+    l = U_k + B_k                                # exponent of eq (4)
     lse = logsumexp(l, axis=1)                   # log of eq (4)'s denominator
     lpad = np.full((R, nC * C), -np.inf)
     lpad[:, :V] = l
