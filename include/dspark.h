@@ -9,6 +9,7 @@
  * sit between the backbone and the target model, as HIP kernels:
  *
  *   dspark_markov_sample  the sequential Markov-head sampling loop
+ *   dspark_rnn_sample     the same loop with the RNN head
  *   dspark_confidence     the confidence head (linear + sigmoid, temperature)
  *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
  *   dspark_schedule_ex    the same with the production admission rules
@@ -73,7 +74,8 @@ typedef enum {
   DSPARK_WS_SCHEDULE = 2,
   DSPARK_WS_VERIFY = 3,
   DSPARK_WS_VERIFY_GREEDY = 4,
-  DSPARK_WS_ACCEPTANCE = 5
+  DSPARK_WS_ACCEPTANCE = 5,
+  DSPARK_WS_RNN_SAMPLE = 6
 } dspark_ws_kind;
 
 /*
@@ -114,6 +116,37 @@ dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int
                                    const int32_t* x0, const float* G, const float* g,
                                    int32_t* x, float* lse, float* logit,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_rnn_sample — the gamma-step sampling loop with the RNN head.
+ *
+ * Passage: notes, "implementation two: the RNN head", eq (6); atlas, the two
+ * heads.  The head keeps a state s (s_0 = 0); position k forms
+ * z = [s_{k-1}; W1[x_{k-1}]; h_k] and one packed projection y = W z gives
+ * s_k = sigmoid(y_g) * s_{k-1} + (1 - sigmoid(y_g)) * tanh(y_c) and the
+ * bias B_k = tanh(y_o) W2; x_k is then drawn exactly as in
+ * dspark_markov_sample, with the r-vector o_k = tanh(y_o) in W1[x_{k-1}]'s
+ * place.  x_{-1} is the anchor x0 (-1: a W1 part of zeros).  With bf16
+ * storage z enters the projection in bf16 (the state rounded from fp32 to
+ * nearest, ties to even) with fp32 accumulation, the gates are fp32, and
+ * o_k is rounded the same way before the bias product; with fp32 storage
+ * everything is fp32.
+ *
+ *   U, W1, W2t, x0, G, g, x, lse, logit  as in dspark_markov_sample
+ *   Wrnn  [3r][2r + d] dt: rows 0..r-1 W_g, r..2r-1 W_c, 2r..3r-1 W_o; the
+ *         columns follow z (state, W1 row, hidden state)
+ *   h     [R][gamma][d] dt: the backbone's hidden states
+ *   s     [R][gamma][r] f32 out: the state after each position
+ *   o     [R][gamma][r] dt out: each position's bias vector o_k
+ *   ws    workspace of dspark_workspace_size(DSPARK_WS_RNN_SAMPLE, ...) bytes
+ *
+ * Limits: as dspark_markov_sample; d >= 1, and with bf16 storage d a
+ * multiple of 16.
+ */
+dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                const void* W1, const void* W2t, const void* Wrnn, const void* h,
+                                const int32_t* x0, const float* G, const float* g, int32_t* x, float* lse,
+                                float* logit, float* s, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_confidence — conditional survival of every drafted position.

@@ -68,9 +68,11 @@ def rnn_sample(U, E, W2t, W, h, x0, G, g, store: str, teacher: dict | None = Non
     arrays); G [R][gamma][nC], g [R][gamma][C].
 
     teacher: {"x": [R][gamma], "s": [R][gamma][r]} from another implementation;
-    position k then takes its previous token and previous state from there
-    (its own o_k and draw are still computed here), so that a near-tie or a
-    rounding-boundary case cannot cascade."""
+    position k then takes its previous token and previous state from there,
+    so that a near-tie cannot cascade.  With "o" [R][gamma][r] as well, the
+    draw at position k uses that bias vector (already in storage precision)
+    instead of this oracle's own rounded o_k, so that a case on a rounding
+    boundary is checked in the head and not again in the draw."""
     R, gamma, V = U.shape
     r = E.shape[1]
     x = np.zeros((R, gamma), dtype=np.int64)
@@ -88,7 +90,9 @@ def rnn_sample(U, E, W2t, W, h, x0, G, g, store: str, teacher: dict | None = Non
         s, o = rnn_step(W, s_prev, e_prev, h[:, k, :], store)
         S[:, k] = s
         O[:, k] = o
-        B = round_storage(o, store) @ W2t.T
+        o_used = (np.asarray(teacher["o"][:, k], dtype=np.float64) if teacher is not None and "o" in teacher
+                  else round_storage(o, store))
+        B = o_used @ W2t.T
         st = sample_with_bias(U[:, k, :], B, G[:, k, :], g[:, k, :])
         x[:, k] = st["token"]
         lse[:, k] = st["lse"]

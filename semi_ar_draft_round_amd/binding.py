@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 F32, BF16 = 0, 1
 CHUNK = 16   # tokens per chunk of the two-level Gumbel draw
-WS_SAMPLE, WS_SCHEDULE, WS_VERIFY, WS_VERIFY_GREEDY, WS_ACCEPTANCE = 0, 2, 3, 4, 5
+WS_SAMPLE, WS_SCHEDULE, WS_VERIFY, WS_VERIFY_GREEDY, WS_ACCEPTANCE, WS_RNN_SAMPLE = 0, 2, 3, 4, 5, 6
 SCHED_EARLY_STOP, SCHED_WHOLE_WALK, SCHED_CAPACITY = 0, 1, 2
 
 _lib = None
@@ -37,6 +37,8 @@ _SIGNATURES = {
                       _P, _SZ, _P],
     "dspark_verify_greedy": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_acceptance": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_rnn_sample": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _SZ, _P],
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
     "dspark_status_string": [_I],
 }
@@ -292,4 +294,35 @@ def dspark_acceptance(target, U, W1, W2t, x0, x, lse, row0=None, c_star=None, ws
                                _ptr(x0), _ptr(x), _ptr(lse), _ptr(c_star), _ptr(ws), ws.numel(), _stream())
     _raise("dspark_acceptance", st)
     return c_star
+
+
+def dspark_rnn_sample(U, W1, W2t, Wrnn, h, x0, G, g, x=None, lse=None, logit=None, s=None, o=None, ws=None):
+    """x [R][gamma] int32, lse and logit [R][gamma] f32, s [R][gamma][r] f32 (the
+    states) and o [R][gamma][r] (the bias vectors): sampling with the RNN head."""
+    lib = load_library()
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    d = h.shape[2]
+    dev = U.device
+    sdt = (U.dtype,)
+    nC = (V + CHUNK - 1) // CHUNK
+    _check(U, "U", (R, gamma, V), sdt, dev)
+    _check(W1, "W1", (V, r), sdt, dev)
+    _check(W2t, "W2t", (V, r), sdt, dev)
+    _check(Wrnn, "Wrnn", (3 * r, 2 * r + d), sdt, dev)
+    _check(h, "h", (R, gamma, d), sdt, dev)
+    _check(x0, "x0", (R,), (torch.int32,), dev)
+    _check(G, "G", (gamma, nC, R), (torch.float32,), dev)
+    _check(g, "g", (R, gamma, CHUNK), (torch.float32,), dev)
+    x = torch.empty((R, gamma), dtype=torch.int32, device=dev) if x is None else x
+    lse = torch.empty((R, gamma), dtype=torch.float32, device=dev) if lse is None else lse
+    logit = torch.empty((R, gamma), dtype=torch.float32, device=dev) if logit is None else logit
+    s = torch.empty((R, gamma, r), dtype=torch.float32, device=dev) if s is None else s
+    o = torch.empty((R, gamma, r), dtype=U.dtype, device=dev) if o is None else o
+    ws = workspace(WS_RNN_SAMPLE, R, gamma, V, r, dev) if ws is None else ws
+    st = lib.dspark_rnn_sample(_dt(U), R, gamma, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(Wrnn), _ptr(h),
+                               _ptr(x0), _ptr(G), _ptr(g), _ptr(x), _ptr(lse), _ptr(logit), _ptr(s), _ptr(o),
+                               _ptr(ws), ws.numel(), _stream())
+    _raise("dspark_rnn_sample", st)
+    return x, lse, logit, s, o
 

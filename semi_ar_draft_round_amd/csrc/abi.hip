@@ -6,14 +6,16 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "rnn_head.hpp"
 
 namespace dspark {
 // sample.hip
 size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V);
+size_t rnn_workspace_bytes(int R, int r);
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, const RnnHead* rnn);
 // confidence.hip
 hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
                              const void* w, const void* W1, const int32_t* x0, const int32_t* x,
@@ -105,6 +107,16 @@ const char* dspark_status_string(dspark_status s) {
   return "unknown status";
 }
 
+static size_t sample_ws_any(int R, int gamma, int V) {
+  const size_t a = sample_workspace_bytes(DSPARK_F32, R, gamma, V), b = sample_workspace_bytes(DSPARK_BF16, R, gamma, V);
+  return a > b ? a : b;
+}
+
+// The sampler's workspace (256-byte aligned), then the RNN projection partials.
+static size_t rnn_sample_workspace_bytes(int R, int gamma, int V, int r) {
+  return ((sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255)) + rnn_workspace_bytes(R, r);
+}
+
 size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r, int n_sps) {
   (void)r;
   (void)n_sps;
@@ -126,6 +138,9 @@ size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r
     case DSPARK_WS_ACCEPTANCE:
       if (!draft_shape_ok(R, gamma, V)) return 0;
       return acceptance_workspace_bytes(R, gamma, V);
+    case DSPARK_WS_RNN_SAMPLE:
+      if (!draft_shape_ok(R, gamma, V) || r < 1) return 0;
+      return rnn_sample_workspace_bytes(R, gamma, V, r);
   }
   return 0;
 }
@@ -142,7 +157,7 @@ dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
   if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws,
-                    static_cast<hipStream_t>(stream)) != hipSuccess)
+                    static_cast<hipStream_t>(stream), nullptr) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }
@@ -239,6 +254,27 @@ dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r,
   if (st != DSPARK_OK) return st;
   if (acceptance_launch(dt, R, gamma, V, r, target, row0, U, W1, W2t, x0, x, lse, c_star, ws,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                const void* W1, const void* W2t, const void* Wrnn, const void* h,
+                                const int32_t* x0, const float* G, const float* g, int32_t* x, float* lse,
+                                float* logit, float* s, void* o, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
+  if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
+  if (d < 1 || d > (1 << 20) || (dt == DSPARK_BF16 && d % 16 != 0)) return DSPARK_EINVAL;
+  if (!U || !W1 || !W2t || !Wrnn || !h || !x0 || !G || !g || !x || !lse || !logit || !s || !o)
+    return DSPARK_EINVAL;
+  if (!ws || ws_bytes < rnn_sample_workspace_bytes(R, gamma, V, r)) return DSPARK_EWORKSPACE;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  const size_t off = (sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255);
+  const RnnHead head{Wrnn, h, d, s, o, reinterpret_cast<float*>(static_cast<char*>(ws) + off)};
+  if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, static_cast<hipStream_t>(stream),
+                    &head) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

@@ -64,6 +64,19 @@ __device__ __forceinline__ void load_w1_frags(WFrags<NBW, KS>& e, const uint16_t
   }
 }
 
+// The same B fragments from one r-vector row per request group (a W1 row,
+// or the bias vector of another head); a null row gives zeros.
+template <int NBW, int KS>
+__device__ __forceinline__ void load_vec_frags(WFrags<NBW, KS>& e, const uint16_t* const (&rows)[NBW]) {
+  const int q = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      e.f[nb][ks] = rows[nb] ? load_bf16x8_global(rows[nb] + ks * 32 + q * 8) : bf16x8{};
+  }
+}
+
 // The W2t tile of one chunk staged in registers: the tile's 64 rows are one
 // contiguous block of 64 * r bf16, so thread t takes the 16-byte pieces
 // t, t + 256, ... of that block (fully coalesced); rows past V read row V-1

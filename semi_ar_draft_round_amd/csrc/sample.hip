@@ -19,14 +19,14 @@
 // drafted token.
 #include "bias_tile.hpp"
 #include "wide_tile.hpp"
+#include "sample_keys.hpp"
+#include "rnn_head.hpp"
 
 namespace dspark {
 
 // Upper bound on the work groups per position along the vocabulary (the
 // bf16 kernel runs one work group per compute unit); sizes the workspace.
 constexpr int kMaxSampleWGs = 1024;
-// Argmax key slots per (position, request); work group b uses slot b % 8.
-constexpr int kKeySlots = 8;
 
 template <int NBW>
 __host__ __device__ constexpr int sample_reqs_per_wg() { return kTileWaves * 16 * NBW; }
@@ -40,20 +40,6 @@ struct SampleWs {
 // the top counter and time-out flag, then kBarGroups group counters 128 bytes apart)
 constexpr int kBarWords = 256;
 constexpr int kBarGroups = 8;
-
-// Token drawn at position k-1 (or the anchor at k = 0).
-__device__ __forceinline__ int previous_token(const unsigned long long* keys, const int32_t* x0, int R,
-                                              int V, int k, int req) {
-  if (k == 0) return token_or_none(x0[req], V);
-  unsigned long long best = 0;
-  const unsigned long long* kp = keys + static_cast<int64_t>(k - 1) * kKeySlots * R + req;
-#pragma unroll
-  for (int s = 0; s < kKeySlots; ++s) {
-    const unsigned long long v = kp[static_cast<int64_t>(s) * R];
-    best = v > best ? v : best;
-  }
-  return token_or_none(key_token(best), V);
-}
 
 __global__ __launch_bounds__(256) void sample_init(unsigned long long* keys, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
@@ -139,7 +125,7 @@ template <int NBW, int KS, bool VEC>
 __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
     int R, int gamma, int V, int k, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
-    const float* __restrict__ g, SampleWs ws, int nPart) {
+    const float* __restrict__ g, SampleWs ws, int nPart, const uint16_t* __restrict__ bvec) {
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane and M-block column of four");
   constexpr int NROWS = sample_reqs_per_wg<NBW>();
   constexpr int kW = tile_bytes(KS);
@@ -188,7 +174,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
   // the previous tokens first: the W1 rows they select gate the first products
   int prev[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) prev[nb] = live[nb] ? previous_token(ws.keys, x0, R, V, k, req[nb]) : -1;
+  for (int nb = 0; nb < NBW; ++nb) prev[nb] = !bvec && live[nb] ? previous_token(ws.keys, x0, R, V, k, req[nb]) : -1;
   // in-chunk Gumbels: lane q brings offsets 4q .. 4q + 3 of its request
   f32x4 gq[NBW];
 #pragma unroll
@@ -199,7 +185,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
   load_lane(even, 0);
   load_lane(odd, clampc(1));
   WFrags<NBW, KS> e;
-  load_w1_frags<NBW, KS>(e, W1, prev);
+  // the bias vector of each request: its previous token's W1 row, or the
+  // given per-(request, position) vectors
+  const uint16_t* erow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+    erow[nb] = bvec ? bvec + rowk[nb] * (KS * 32)
+                    : (prev[nb] >= 0 ? W1 + static_cast<int64_t>(prev[nb]) * (KS * 32) : nullptr);
+  load_vec_frags<NBW, KS>(e, erow);
 
   LaneDraw dr[NBW];
   int bestSlot[NBW];   // which of the lane's two keep slots holds its best chunk
@@ -385,7 +378,7 @@ template <int RQ, int KS16, bool VEC>
 __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     int R, int gamma, int V, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
-    const float* __restrict__ g, SampleWs ws, int nPart) {
+    const float* __restrict__ g, SampleWs ws, int nPart, int kb, int ke, const uint16_t* __restrict__ bvec) {
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
   constexpr int T = wide_threads<RQ>();
   constexpr int NROWS = 32 * RQ;
@@ -415,14 +408,14 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
                       static_cast<int>(gridDim.x));
   // tile at sweep position p of position k (snake order over this group's pairs)
   const auto q_at = [&](int k, int p) { return (k & 1) ? nT - 1 - p : p; };
-  const auto tile_at = [&](int k, int p) {
-    const int q = q_at(k, p);
+  const auto tile_q = [&](int q) {
     return 2 * (static_cast<int>(blockIdx.x) + (q >> 1) * static_cast<int>(gridDim.x)) + (q & 1);
   };
+  const auto tile_at = [&](int k, int p) { return tile_q(q_at(k, p)); };
   // a sweep position past the last belongs to the next position (the last
-  // position repeats its last tile)
-  const auto next_k = [&](int k, int p) { return p < nT ? k : (k + 1 < gamma ? k + 1 : k); };
-  const auto next_p = [&](int k, int p) { return p < nT ? p : (k + 1 < gamma ? p - nT : nT - 1); };
+  // position of the launch repeats its last tile)
+  const auto next_k = [&](int k, int p) { return p < nT ? k : (k + 1 < ke ? k + 1 : k); };
+  const auto next_p = [&](int k, int p) { return p < nT ? p : (k + 1 < ke ? p - nT : nT - 1); };
   // the middle pair of the group's tiles stays in LDS (so that every
   // position starts on streamed tiles, whose loads are issued before the
   // grid barrier); the others stream through two slots, alternating with
@@ -450,11 +443,14 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
   auto load_gq = [&](int k) {
     return *reinterpret_cast<const f32x4*>(g + (static_cast<int64_t>(reqc) * gamma + k) * kGChunk + 8 * th + 4 * h);
   };
-  // B operand: k-step ks takes elements 16 ks + 8 h .. + 7 of the W1 row, or
-  // of a row of zeros when there is no previous token (bias 0)
+  // B operand: k-step ks takes elements 16 ks + 8 h .. + 7 of the W1 row of
+  // the previous token (a row of zeros when there is none: bias 0), or of
+  // the request's given bias vector of position k
   bf16x8 e[KS16];
-  auto load_e = [&](int prev) {
-    const uint16_t* w1row = (prev >= 0 ? W1 + static_cast<int64_t>(prev) * (KS16 * 16) : kZeroRow) + 8 * h;
+  auto load_e = [&](int prev, int k) {
+    const uint16_t* w1row =
+        (bvec ? bvec + (static_cast<int64_t>(reqc) * gamma + k) * (KS16 * 16)
+              : prev >= 0 ? W1 + static_cast<int64_t>(prev) * (KS16 * 16) : kZeroRow) + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS16; ++ks) e[ks] = load_bf16x8_global(w1row + 16 * ks);
   };
@@ -524,25 +520,26 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     advance(k, p);
   };
 
-  // position 0: its previous token is the anchor
-  const int x0v = x0[reqc];
+  // the first position of the launch: with W1 rows, its previous token is
+  // the anchor (kb = 0)
+  const int x0v = bvec ? -1 : x0[reqc];
   __builtin_amdgcn_sched_barrier(0);
-  f32x4 gq = load_gq(0);
+  f32x4 gq = load_gq(kb);
   static_assert(kResident == 2, "the resident tiles are one pair");
-  wide_load_w<KS16, RQ>(wr, W2t, V, tile_at(0, qr) * kChunk);
-  load_lane(even, 0, 0);
-  load_lane(odd, 0, 1);
-  load_e(live ? token_or_none(x0v, V) : -1);
+  wide_load_w<KS16, RQ>(wr, W2t, V, tile_q(qr) * kChunk);
+  load_lane(even, kb, 0);
+  load_lane(odd, kb, 1);
+  load_e(live ? token_or_none(x0v, V) : -1, kb);
   *reinterpret_cast<f32x4*>(&gsh[loc][8 * th + 4 * h]) = gq;
   wide_store_w<KS16, RQ>(lds + 2 * kW, wr);
-  wide_load_w<KS16, RQ>(wr, W2t, V, tile_at(0, qr + 1) * kChunk);
+  wide_load_w<KS16, RQ>(wr, W2t, V, tile_q(qr + 1) * kChunk);
   wide_store_w<KS16, RQ>(lds + 3 * kW, wr);
-  load_w(wr, 0, 0);
-  if (!resident(0, 0)) wide_store_w<KS16, RQ>(lds, wr);
-  load_w(wr, 0, 1);
+  load_w(wr, kb, 0);
+  if (!resident(kb, 0)) wide_store_w<KS16, RQ>(lds, wr);
+  load_w(wr, kb, 1);
   __syncthreads();
 
-  for (int k = 0; k < gamma; ++k) {
+  for (int k = kb; k < ke; ++k) {
     lane_draw_init(dr);
     products(k, 0, even, accP, GcP);
     v0P = tile_at(k, 0) * kChunk;
@@ -589,7 +586,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
         __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * kKeySlots + blockIdx.x % kKeySlots) * R + req,
                                key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    if (k + 1 == gamma) break;
+    if (k + 1 == ke) break;
 
     // next position: its in-chunk Gumbels are fetched before the barrier; its
     // logits and first two W2t tiles are already in flight
@@ -603,7 +600,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
                                                      __HIP_MEMORY_SCOPE_SYSTEM);
       best = v > best ? v : best;
     }
-    load_e(live ? token_or_none(key_token(best), V) : -1);
+    load_e(live ? token_or_none(key_token(best), V) : -1, k + 1);
     *reinterpret_cast<f32x4*>(&gsh[loc][8 * th + 4 * h]) = gq;
     __syncthreads();
   }
@@ -614,19 +611,19 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
 __global__ __launch_bounds__(64) void sample_step_f32(
     int R, int gamma, int V, int r, int k, const float* __restrict__ U, const float* __restrict__ W1,
     const float* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
-    const float* __restrict__ g, SampleWs ws, int nPart) {
+    const float* __restrict__ g, SampleWs ws, int nPart, const float* __restrict__ bvec) {
   const int tile = blockIdx.x;
   const int req = blockIdx.y;
   const int lane = threadIdx.x;
   const int nG = (V + kGChunk - 1) / kGChunk;
-  const int prev = previous_token(ws.keys, x0, R, V, k, req);
+  const int prev = bvec ? -1 : previous_token(ws.keys, x0, R, V, k, req);
   const int v = tile * kChunk + lane;
   const int64_t rowk = static_cast<int64_t>(req) * gamma + k;
   float val = neg_inf();
   if (v < V) {
     float b = 0.f;
-    if (prev >= 0) {
-      const float* e = W1 + static_cast<int64_t>(prev) * r;
+    if (bvec || prev >= 0) {
+      const float* e = bvec ? bvec + rowk * r : W1 + static_cast<int64_t>(prev) * r;
       const float* w = W2t + static_cast<int64_t>(v) * r;
       for (int i = 0; i < r; ++i) b = fmaf(e[i], w[i], b);
     }
@@ -668,7 +665,8 @@ __global__ __launch_bounds__(64) void sample_step_f32(
 }
 
 // Decode x, merge the log-sum-exp partials and recompute each drafted
-// token's logit U_k(x_k) + W1[x_{k-1}] . W2t[x_k]: one wave per (request, k).
+// token's logit U_k(x_k) + W1[x_{k-1}] . W2t[x_k] (or the given bias vector
+// of (request, k) in W1[x_{k-1}]'s place): one wave per (request, k).
 template <typename Elt>
 __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, int r,
                                                        const typename Elt::T* __restrict__ U,
@@ -676,7 +674,8 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
                                                        const typename Elt::T* __restrict__ W2t,
                                                        const int32_t* __restrict__ x0, SampleWs ws,
                                                        int nPart, int32_t* __restrict__ x,
-                                                       float* __restrict__ lse, float* __restrict__ logit) {
+                                                       float* __restrict__ lse, float* __restrict__ logit,
+                                                       const typename Elt::T* __restrict__ bvec) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= static_cast<int64_t>(R) * gamma) return;
@@ -692,7 +691,7 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   }
   const int drawn = previous_token(ws.keys, x0, R, V, k + 1, req);
   const int tok = drawn < 0 ? 0 : drawn;   // every position draws a token in [0, V)
-  const int prev = previous_token(ws.keys, x0, R, V, k, req);
+  const int prev = bvec ? -1 : previous_token(ws.keys, x0, R, V, k, req);
   Lse run{neg_inf(), 0.f};
   const float2* lp = ws.lsep + (static_cast<int64_t>(k) * R + req) * nPart;
   for (int p = lane; p < nPart; p += 64) {
@@ -701,9 +700,11 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   }
   run = wave_reduce_lse(run);
   float b = 0.f;
-  if (prev >= 0)
+  if (bvec || prev >= 0) {
+    const typename Elt::T* e = bvec ? bvec + row * r : W1 + static_cast<int64_t>(prev) * r;
     for (int i = lane; i < r; i += 64)
-      b = fmaf(Elt::load(W1, static_cast<int64_t>(prev) * r + i), Elt::load(W2t, static_cast<int64_t>(tok) * r + i), b);
+      b = fmaf(Elt::load(e, i), Elt::load(W2t, static_cast<int64_t>(tok) * r + i), b);
+  }
   b = wave_reduce_sum(b);
   if (lane == 0) {
     x[row] = tok;
@@ -767,61 +768,70 @@ static int bf16_grid_x(int R, int V) {
   return gx;
 }
 
+// Where each (request, position) takes its bias vector from: the previous
+// token's W1 row (the Markov head, bvec null) or bvec [R][gamma][r].
+struct SampleArgs {
+  int R, gamma, V;
+  const void *U, *W1, *W2t, *bvec;
+  const int32_t* x0;
+  const float *G, *g;
+};
+
 template <int NBW, int KS, bool VEC>
-static void launch_step_bf16(int R, int gamma, int V, int k, const void* U, const void* W1,
-                             const void* W2t, const int32_t* x0, const float* G, const float* g,
-                             const SampleWs& w, int gx, hipStream_t s) {
-  dim3 grid(gx, ceil_div(R, sample_reqs_per_wg<NBW>()));
-  hipLaunchKernelGGL((sample_step_bf16<NBW, KS, VEC>), grid, dim3(kTileThreads), 0, s, R, gamma, V, k,
-                     static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
-                     static_cast<const uint16_t*>(W2t), x0, G, g, w, gx);
+static void launch_step_bf16(const SampleArgs& a, int k, const SampleWs& w, int gx, hipStream_t s) {
+  dim3 grid(gx, ceil_div(a.R, sample_reqs_per_wg<NBW>()));
+  hipLaunchKernelGGL((sample_step_bf16<NBW, KS, VEC>), grid, dim3(kTileThreads), 0, s, a.R, a.gamma, a.V, k,
+                     static_cast<const uint16_t*>(a.U), static_cast<const uint16_t*>(a.W1),
+                     static_cast<const uint16_t*>(a.W2t), a.x0, a.G, a.g, w, gx,
+                     static_cast<const uint16_t*>(a.bvec));
 }
 
 template <int RQ, int KS16, bool VEC>
-static void launch_steps_wide(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
-                              const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
-                              hipStream_t s) {
-  dim3 grid(gx, ceil_div(R, 32 * RQ));
-  hipLaunchKernelGGL((sample_steps_wide<RQ, KS16, VEC>), grid, dim3(wide_threads<RQ>()), 0, s, R, gamma, V,
-                     static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
-                     static_cast<const uint16_t*>(W2t), x0, G, g, w, gx);
+static void launch_steps_wide(const SampleArgs& a, int kb, int ke, const SampleWs& w, int gx, hipStream_t s) {
+  dim3 grid(gx, ceil_div(a.R, 32 * RQ));
+  hipLaunchKernelGGL((sample_steps_wide<RQ, KS16, VEC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R, a.gamma, a.V,
+                     static_cast<const uint16_t*>(a.U), static_cast<const uint16_t*>(a.W1),
+                     static_cast<const uint16_t*>(a.W2t), a.x0, a.G, a.g, w, gx, kb, ke,
+                     static_cast<const uint16_t*>(a.bvec));
 }
 
 template <int KS16>
-static void launch_steps_wide_ks(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
-                                 const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
-                                 hipStream_t s) {
-  const bool vec = (V % kGChunk) == 0;
-  if (R <= 64) {
-    if (vec) launch_steps_wide<2, KS16, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
-    else launch_steps_wide<2, KS16, false>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
+static void launch_steps_wide_ks(const SampleArgs& a, int kb, int ke, const SampleWs& w, int gx, hipStream_t s) {
+  const bool vec = (a.V % kGChunk) == 0;
+  if (a.R <= 64) {
+    if (vec) launch_steps_wide<2, KS16, true>(a, kb, ke, w, gx, s);
+    else launch_steps_wide<2, KS16, false>(a, kb, ke, w, gx, s);
   } else {
-    if (vec) launch_steps_wide<4, KS16, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
-    else launch_steps_wide<4, KS16, false>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, s);
+    if (vec) launch_steps_wide<4, KS16, true>(a, kb, ke, w, gx, s);
+    else launch_steps_wide<4, KS16, false>(a, kb, ke, w, gx, s);
   }
 }
 
 template <int KS>
-static void launch_step_bf16_ks(int R, int gamma, int V, int k, const void* U, const void* W1,
-                                const void* W2t, const int32_t* x0, const float* G, const float* g,
-                                const SampleWs& w, int gx, hipStream_t s) {
+static void launch_step_bf16_ks(const SampleArgs& a, int k, const SampleWs& w, int gx, hipStream_t s) {
   // the vector path loads a lane's sixteen logits as two aligned 16-byte
   // pieces: rows must start on 16 bytes and hold whole Gumbel chunks
-  const bool vec = (V % kGChunk) == 0;
-  if (sample_nbw(R) == 1) {
-    if (vec) launch_step_bf16<1, KS, true>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, gx, s);
-    else launch_step_bf16<1, KS, false>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, gx, s);
+  const bool vec = (a.V % kGChunk) == 0;
+  if (sample_nbw(a.R) == 1) {
+    if (vec) launch_step_bf16<1, KS, true>(a, k, w, gx, s);
+    else launch_step_bf16<1, KS, false>(a, k, w, gx, s);
   } else {
-    if (vec) launch_step_bf16<2, KS, true>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, gx, s);
-    else launch_step_bf16<2, KS, false>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, gx, s);
+    if (vec) launch_step_bf16<2, KS, true>(a, k, w, gx, s);
+    else launch_step_bf16<2, KS, false>(a, k, w, gx, s);
   }
 }
+
+// rnn.hip: the RNN head's projection and gating for position k (reads the
+// keys of position k - 1 for the previous token)
+hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, int V, int r, int k,
+                           const void* W1, const int32_t* x0, const unsigned long long* keys, hipStream_t s);
 
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, const RnnHead* rnn) {
   const SampleWs w = carve(ws, R, gamma);
+  const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g};
   const int gxw = dt == DSPARK_BF16 && sample_wide(R) ? wide_grid_x(R, V) : 0;
   const int nPart = gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
   const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
@@ -829,41 +839,49 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                      dim3(256), 0, s, w.keys, nkeys);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (gxw > 0) {
-    switch (r / 32) {
-      case 1: launch_steps_wide_ks<2>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
-      case 2: launch_steps_wide_ks<4>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
-      case 4: launch_steps_wide_ks<8>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
-      default: launch_steps_wide_ks<16>(R, gamma, V, U, W1, W2t, x0, G, g, w, nPart, s); break;
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  for (int k = 0; k < gamma && gxw == 0; ++k) {
-    if (dt == DSPARK_BF16) {
-      {
-        switch (r / 32) {
-          case 1: launch_step_bf16_ks<1>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-          case 2: launch_step_bf16_ks<2>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-          case 4: launch_step_bf16_ks<4>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-          default: launch_step_bf16_ks<8>(R, gamma, V, k, U, W1, W2t, x0, G, g, w, nPart, s); break;
-        }
+  // the positions one launch covers: all of them with the Markov head (the
+  // persistent path meets at a grid barrier between positions), one at a
+  // time with the RNN head (its projection runs between positions)
+  const int span = rnn ? 1 : gamma;
+  for (int kb = 0; kb < gamma; kb += span) {
+    if (rnn && (err = rnn_step_launch(dt, *rnn, R, gamma, V, r, kb, W1, x0, w.keys, s)) != hipSuccess) return err;
+    if (gxw > 0) {
+      switch (r / 32) {
+        case 1: launch_steps_wide_ks<2>(a, kb, kb + span, w, nPart, s); break;
+        case 2: launch_steps_wide_ks<4>(a, kb, kb + span, w, nPart, s); break;
+        case 4: launch_steps_wide_ks<8>(a, kb, kb + span, w, nPart, s); break;
+        default: launch_steps_wide_ks<16>(a, kb, kb + span, w, nPart, s); break;
       }
-    } else {
-      hipLaunchKernelGGL(sample_step_f32, dim3(nPart, R), dim3(64), 0, s, R, gamma, V, r, k,
-                         static_cast<const float*>(U), static_cast<const float*>(W1),
-                         static_cast<const float*>(W2t), x0, G, g, w, nPart);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      continue;
     }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    for (int k = kb; k < kb + span; ++k) {
+      if (dt == DSPARK_BF16) {
+        switch (r / 32) {
+          case 1: launch_step_bf16_ks<1>(a, k, w, nPart, s); break;
+          case 2: launch_step_bf16_ks<2>(a, k, w, nPart, s); break;
+          case 4: launch_step_bf16_ks<4>(a, k, w, nPart, s); break;
+          default: launch_step_bf16_ks<8>(a, k, w, nPart, s); break;
+        }
+      } else {
+        hipLaunchKernelGGL(sample_step_f32, dim3(nPart, R), dim3(64), 0, s, R, gamma, V, r, k,
+                           static_cast<const float*>(U), static_cast<const float*>(W1),
+                           static_cast<const float*>(W2t), x0, G, g, w, nPart, static_cast<const float*>(a.bvec));
+      }
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
   }
   const int blocks = ceil_div(static_cast<int64_t>(R) * gamma, 4);
   if (dt == DSPARK_BF16)
     hipLaunchKernelGGL(sample_finalize<BF16>, dim3(blocks), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
-                       static_cast<const uint16_t*>(W2t), x0, w, nPart, x, lse, logit);
+                       static_cast<const uint16_t*>(W2t), x0, w, nPart, x, lse, logit,
+                       static_cast<const uint16_t*>(a.bvec));
   else
     hipLaunchKernelGGL(sample_finalize<F32>, dim3(blocks), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const float*>(U), static_cast<const float*>(W1),
-                       static_cast<const float*>(W2t), x0, w, nPart, x, lse, logit);
+                       static_cast<const float*>(W2t), x0, w, nPart, x, lse, logit,
+                       static_cast<const float*>(a.bvec));
   return hipGetLastError();
 }
 

@@ -229,3 +229,14 @@ def make_inputs(w: Workload, round_index: int = 0, with_target: bool = True) -> 
     u_acc = odd_uniform(rng, (R, gamma))
     u_res = odd_uniform(rng, (R,))
     return RoundInputs(w, U, E, W2t, w_conf, h, x0, target, sps, T, G, g, u_acc, u_res)
+
+
+def make_rnn_weights(w: Workload, gain: float = 1.0) -> np.ndarray:
+    """The RNN head's packed projection [3r][2r + d] (gate, candidate and
+    output rows; columns state, W1 row, hidden state), N(0, gain^2 / (2r + d)),
+    in the workload's storage type.  Seeded by the workload only."""
+    rng = np.random.default_rng([w.seed, 7])
+    K = 2 * w.r + w.d
+    W = rng.normal(0.0, gain / np.sqrt(K), size=(3 * w.r, K)).astype(np.float32)
+    return _store(W, w.dtype)
+

@@ -143,6 +143,19 @@ def test_acceptance_rejects_bad_arguments(lib):
     assert call(ws_bytes=8) == EWORKSPACE
 
 
+def test_rnn_sample_rejects_bad_arguments(lib):
+    def call(dt=1, R=2, gamma=3, V=500, r=64, d=32, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        args = [ptr] * 13
+        return lib.dspark_rnn_sample(dt, R, gamma, V, r, d, *args, ws, ws_bytes, None)
+    assert call(dt=5) == EDTYPE
+    assert call(r=48) == EDTYPE
+    assert call(d=24) == EINVAL                 # bf16 hidden size must be a multiple of 16
+    assert call(d=0) == EINVAL
+    assert call(V=0) == EINVAL
+    assert call(ptr=None) == EINVAL
+    assert call(ws_bytes=8) == EWORKSPACE
+
+
 def test_verify_rejects_bad_arguments(lib):
     def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
         args = [ptr] * 13

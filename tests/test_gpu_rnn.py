@@ -1,0 +1,142 @@
+"""GPU sampling with the RNN head (eq 6) through the C ABI, against the
+float64 oracle.
+
+Per position, the oracle is handed the GPU's previous token, previous state
+and bias vector:
+  * the head: s_k within S_TOL and o_k within one bf16 rounding plus O_TOL
+    of the oracle's values computed from the same z.  The projection sums
+    2r + d (up to 7680) products in fp32 on the GPU, about sqrt(K) 2^-24 of
+    the pre-activation's scale (< 1e-5; 3e-7 seen), and |s|, |o| < 1;
+  * the draw: the usual sampling rules (tokens within a perturbed-score gap
+    of 1e-4, lse 1e-5 relative, logit 1e-5 of max(1, |logit|)) with the
+    bias built from the GPU's bias vector.
+A GPU-only identity: with W1 entries +-1/2 and an output projection
+1.1015625 I on the W1 block (bf16-exact; tanh(0.55078) is within half a
+bf16 ulp of 0.5), o_k equals W1[x_{k-1}] exactly and the RNN path must
+reproduce the Markov path's outputs bit for bit."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle.common import as_f64
+from oracle import rnn as RN
+from oracle.sample import token_gaps
+from semi_ar_draft_round_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+S_TOL = 1e-5
+O_TOL = 1e-5
+TOK_GAP = 1e-4
+LSE_REL = 1e-5
+LOGIT_TOL = 1e-5
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from semi_ar_draft_round_amd import binding
+    binding.load_library()
+    return torch.device("cuda:0")
+
+
+def _run(inp, Wrnn, dev, E=None):
+    from semi_ar_draft_round_amd import binding as B
+    from semi_ar_draft_round_amd import device_round as DR
+    d = DR.to_device(inp, dev)
+    W1 = d.W1 if E is None else DR._dev_store(E, inp.w.dtype, dev)
+    out = B.dspark_rnn_sample(d.U, W1, d.W2t, DR._dev_store(Wrnn, inp.w.dtype, dev), d.h, d.x0, d.G, d.g)
+    torch.cuda.synchronize()
+    return d, W1, [t.cpu() for t in out]
+
+
+def _check(inp, Wrnn, got, idx):
+    w = inp.w
+    dt = w.dtype
+    x, lse, logit, s, o = got
+    x = x.numpy().astype(np.int64)
+    s = s.numpy().astype(np.float64)
+    o = (o.float().numpy() if dt == "bf16" else o.numpy()).astype(np.float64)
+    ref = RN.rnn_sample(as_f64(inp.U[idx], dt), as_f64(inp.E, dt), as_f64(inp.W2t, dt), as_f64(Wrnn, dt),
+                        as_f64(inp.h[idx], dt), inp.x0[idx].astype(np.int64), inp.G_by_request(idx),
+                        inp.g[idx].astype(np.float64), dt, teacher=dict(x=x[idx], s=s[idx], o=o[idx]))
+    ds = np.abs(ref["s"] - s[idx]).max()
+    assert ds <= S_TOL, ds
+    ulp = 2.0 ** -8 if dt == "bf16" else 2.0 ** -23
+    do = np.abs(ref["o"] - o[idx]) - ulp * np.abs(ref["o"])
+    assert do.max() <= O_TOL, do.max()
+    worst = 0.0
+    for k, st in enumerate(ref["steps"]):
+        tok = x[idx, k]
+        cg, ig = token_gaps(st, inp.g[idx, k].astype(np.float64), tok)
+        worst = max(worst, float(cg.max()), float(ig.max()))
+        assert np.all(cg <= TOK_GAP) and np.all(ig <= TOK_GAP), (k, cg.max(), ig.max())
+        l = lse.numpy()[idx, k].astype(np.float64)
+        assert np.all(np.abs(l - st["lse"]) <= LSE_REL * np.maximum(1.0, np.abs(st["lse"])))
+        want_logit = st["l"][np.arange(len(idx)), tok]
+        lg = logit.numpy()[idx, k].astype(np.float64)
+        assert np.all(np.abs(lg - want_logit) <= LOGIT_TOL * np.maximum(1.0, np.abs(want_logit)))
+    return dict(ds=ds, do=float(np.abs(ref["o"] - o[idx]).max()), gap=worst)
+
+
+CASES = [
+    W.custom("rnn_r20_g5_v1000_r32", R=20, gamma=5, V=1000, r=32, d=64, seed=41),
+    W.custom("rnn_r3_g4_v203_r32", R=3, gamma=4, V=203, r=32, d=48, seed=42),
+    W.custom("rnn_r70_g6_v4100_r64", R=70, gamma=6, V=4100, r=64, d=128, seed=43),
+    W.custom("rnn_r130_g4_v700_r128", R=130, gamma=4, V=700, r=128, d=256, seed=44),
+    W.custom("rnn_r9_g7_v333_f32", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=45),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_rnn_small(w, dev):
+    say(f"[rnn] {w.name}")
+    inp = W.make_inputs(w)
+    inp.x0[0] = -1                                   # no previous token at the first position
+    Wrnn = W.make_rnn_weights(w)
+    _, _, got = _run(inp, Wrnn, dev)
+    rep = _check(inp, Wrnn, got, np.arange(w.R))
+    say(f"  {rep}")
+
+
+def test_rnn_full_size_sampled(dev):
+    w = W.BY_NAME["heavy_r128_g16_v129280"]
+    say(f"[rnn] {w.name}: drawing inputs")
+    inp = W.make_inputs(w)
+    Wrnn = W.make_rnn_weights(w)
+    _, _, got = _run(inp, Wrnn, dev)
+    idx = np.array([0, 37, 127])
+    say(f"[rnn] {w.name}: oracle on requests {idx.tolist()}")
+    rep = _check(inp, Wrnn, got, idx)
+    say(f"  {rep}")
+    assert np.all((got[0].numpy() >= 0) & (got[0].numpy() < w.V))
+
+
+@pytest.mark.parametrize("name", ["rnn_r70_g6_v4100_r64", "rnn_r20_g5_v1000_r32"])
+def test_rnn_reduces_to_markov_bit_for_bit(name, dev):
+    from semi_ar_draft_round_amd import binding as B
+    from semi_ar_draft_round_amd import device_round as DR
+    w = next(c for c in CASES if c.name == name)
+    inp = W.make_inputs(w)
+    rng = np.random.default_rng(7)
+    E = np.where(rng.random((w.V, w.r)) < 0.5, -0.5, 0.5).astype(np.float32)
+    Wr = np.zeros((3 * w.r, 2 * w.r + w.d), dtype=np.float32)
+    Wr[: w.r] = rng.normal(0, 0.2, size=(w.r, 2 * w.r + w.d))
+    Wr[w.r:2 * w.r] = rng.normal(0, 0.2, size=(w.r, 2 * w.r + w.d))
+    Wr[2 * w.r:, w.r:2 * w.r] = np.eye(w.r) * 1.1015625
+    Wrnn = W.bf16_bits(Wr)
+    d, W1, got = _run(inp, Wrnn, dev, E=W.bf16_bits(E))
+    x, lse, logit, s, o = got
+    xm, lsem, logitm = B.dspark_markov_sample(d.U, W1, d.W2t, d.x0, d.G, d.g)
+    torch.cuda.synchronize()
+    assert torch.equal(x, xm.cpu()) and torch.equal(lse, lsem.cpu()) and torch.equal(logit, logitm.cpu())
+    prev = np.concatenate([inp.x0[:, None], x.numpy()[:, :-1]], axis=1)
+    assert np.array_equal(o.float().numpy(), E[prev])
