@@ -125,9 +125,10 @@ def main():
     t0 = time.perf_counter()
     inps = [W.make_inputs(w, round_index=i) for i in range(2)]
     log(f"[bench] inputs drawn in {time.perf_counter() - t0:.1f} s; copying to {dev}")
-    rounds = [DR.to_device(inps[0], dev)]
-    d1 = DR.to_device(inps[1], dev)
+    rounds = [DR.to_device(inps[0], dev, rnn=True)]
+    d1 = DR.to_device(inps[1], dev, rnn=True)
     d1.W1, d1.W2t, d1.w = rounds[0].W1, rounds[0].W2t, rounds[0].w   # weights are shared
+    d1.rnn["W"] = rounds[0].rnn["W"]
     rounds.append(d1)
     torch.cuda.synchronize()
 
@@ -150,7 +151,8 @@ def main():
               for name, fn in (("round", DR.run_round), ("sample", DR.sample),
                                ("confidence", DR.confidence), ("schedule", DR.schedule),
                                ("verify", DR.verify), ("schedule_production", DR.schedule_production),
-                               ("verify_greedy", DR.verify_greedy), ("acceptance", DR.acceptance))}
+                               ("verify_greedy", DR.verify_greedy), ("acceptance", DR.acceptance),
+                               ("rnn_sample", DR.rnn_sample))}
     torch.cuda.synchronize()
     log("[bench] graphs captured")
 
@@ -178,9 +180,10 @@ def main():
     # own: not part of the round above, which runs Algorithm 1
     # the other modes, each timed on its own and outside the round: the
     # production (asynchronous) scheduler's two calls, greedy verification of
-    # the round's drafts, and the analytic acceptance of all its positions
+    # the round's drafts, the analytic acceptance of all its positions, and
+    # the draft with the RNN head
     modes = {}
-    for name in ("schedule_production", "verify_greedy", "acceptance"):
+    for name in ("schedule_production", "verify_greedy", "acceptance", "rnn_sample"):
         modes[name] = timed(name, max(args.steps, 10), 2) * 1e3
         log(f"[bench] {name}: {modes[name]:.1f} us")
 

@@ -12,6 +12,7 @@
 // work groups; a second kernel adds the partials in order and applies the
 // gates in fp32.  fp32 storage: one thread per output with fp32 FMAs.
 #include "bias_tile.hpp"
+#include "wide_tile.hpp"
 #include "rnn_head.hpp"
 #include "sample_keys.hpp"
 
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(kRnnThreads) void rnn_proj_bf16(int R, int gamma, i
                                                              int per) {
   __shared__ float red[3][kRnnThreads / kWave][16][kWave];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int j = lane & 31;
   const int hh = lane >> 5;
   const int jb = blockIdx.x, ib = blockIdx.y, sp = blockIdx.z;
@@ -51,37 +52,58 @@ __global__ __launch_bounds__(kRnnThreads) void rnn_proj_bf16(int R, int gamma, i
   const int ic = min(i, R - 1);
   const int st1 = min(K / 16, (sp + 1) * per);
   const int prev = previous_token(keys, x0, R, V, k, ic);
-  const float* srow = k > 0 ? s + (static_cast<int64_t>(ic) * gamma + k - 1) * r : nullptr;
-  const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : nullptr;
+  const float* srow = s + (static_cast<int64_t>(ic) * gamma + (k > 0 ? k - 1 : 0)) * r;   // read when k > 0
+  const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
   const uint16_t* hrow = h + (static_cast<int64_t>(ic) * gamma + k) * d;
   const uint16_t* wrow[3];
 #pragma unroll
   for (int g = 0; g < 3; ++g) wrow[g] = W + static_cast<int64_t>(g * r + jb * 32 + j) * K;
   f32x16_r acc[3] = {};
-  for (int st = sp * per + wave; st < st1; st += kRnnThreads / kWave) {
-    const int kk = st * 16 + 8 * hh;   // the lane's first inner index; r and d are multiples of 16
-    bf16x8 b;
-    if (kk < r) {
-      if (srow) {
-        const float4 lo = *reinterpret_cast<const float4*>(srow + kk);
-        const float4 hi = *reinterpret_cast<const float4*>(srow + kk + 4);
-        const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t w[4];
+  constexpr int kW = kRnnThreads / kWave;   // waves; the wave takes every kW-th step of the range
+  constexpr int kU = 4;                     // steps whose operands are in flight together
+  // the wave's steps of [lo, hi) within this work group's range, kU at a time:
+  // every load of a batch is issued before its products; a step past the
+  // range reloads a valid one and multiplies a zero B operand
+  auto run = [&](int lo, int hi, auto&& zfrag) {
+    lo = max(lo, sp * per);
+    hi = min(hi, st1);
+    int st = sp * per + wave;
+    if (st < lo) st += ceil_div(lo - st, kW) * kW;
+    for (; st < hi; st += kU * kW) {
+      bf16x8 a[kU][3], bz[kU];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = bf16_bits_rne(f[2 * q]) | (bf16_bits_rne(f[2 * q + 1]) << 16);
-        b = __builtin_bit_cast(bf16x8, (uint4{w[0], w[1], w[2], w[3]}));
-      } else {
-        b = bf16x8{};
+      for (int u = 0; u < kU; ++u) {
+        const int su = st + u * kW < hi ? st + u * kW : st;
+        const int kk = su * 16 + 8 * hh;
+        bz[u] = zfrag(kk);
+#pragma unroll
+        for (int g = 0; g < 3; ++g) a[u][g] = load_bf16x8_global(wrow[g] + kk);
       }
-    } else if (kk < 2 * r) {
-      b = erow ? load_bf16x8_global(erow + kk - r) : bf16x8{};
-    } else {
-      b = load_bf16x8_global(hrow + kk - 2 * r);
-    }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int g = 0; g < 3; ++g)
-      acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_bf16x8_global(wrow[g] + kk), b, acc[g], 0, 0, 0);
-  }
+      for (int u = 0; u < kU; ++u) {
+        const bf16x8 bu = st + u * kW < hi ? bz[u] : bf16x8{};
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][g], bu, acc[g], 0, 0, 0);
+      }
+    }
+  };
+  // the hidden state first, then z's state part (zero at the first
+  // position; rounded from fp32 to bf16), then the previous token's W1 row
+  // (a row of zeros when there is none), whose address waits on the keys
+  run(2 * r / 16, K / 16, [&](int kk) { return load_bf16x8_global(hrow + kk - 2 * r); });
+  if (k > 0)
+    run(0, r / 16, [&](int kk) {
+      const float4 lo = *reinterpret_cast<const float4*>(srow + kk);
+      const float4 hi = *reinterpret_cast<const float4*>(srow + kk + 4);
+      const uint32_t w0 = bf16_bits_rne(lo.x) | (bf16_bits_rne(lo.y) << 16);
+      const uint32_t w1 = bf16_bits_rne(lo.z) | (bf16_bits_rne(lo.w) << 16);
+      const uint32_t w2 = bf16_bits_rne(hi.x) | (bf16_bits_rne(hi.y) << 16);
+      const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
+      return __builtin_bit_cast(bf16x8, (uint4{w0, w1, w2, w3}));
+    });
+  run(r / 16, 2 * r / 16, [&](int kk) { return load_bf16x8_global(erow + kk - r); });
 #pragma unroll
   for (int g = 0; g < 3; ++g)
 #pragma unroll

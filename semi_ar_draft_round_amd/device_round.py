@@ -73,9 +73,11 @@ class DeviceRound:
     c_star: torch.Tensor
     ws_greedy: torch.Tensor
     ws_accept: torch.Tensor
+    # sampling with the RNN head (allocated when asked for)
+    rnn: Optional[dict] = None
 
 
-def to_device(inp, device="cuda:0") -> DeviceRound:
+def to_device(inp, device="cuda:0", rnn: bool = False) -> DeviceRound:
     w = inp.w
     dev = torch.device(device)
     R, gamma, V, r, d = w.R, w.gamma, w.V, w.r, w.d
@@ -119,6 +121,18 @@ def to_device(inp, device="cuda:0") -> DeviceRound:
         ws_accept=torch.empty(max(1, B.dspark_workspace_size(B.WS_ACCEPTANCE, R, gamma, V, r)),
                               dtype=torch.uint8, device=dev),
     )
+    if rnn:
+        from .workloads import make_rnn_weights
+        dr.rnn = dict(
+            W=_dev_store(make_rnn_weights(w), w.dtype, dev),
+            x=torch.empty((R, gamma), dtype=torch.int32, device=dev),
+            lse=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            logit=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+            s=torch.empty((R, gamma, r), dtype=torch.float32, device=dev),
+            o=torch.empty((R, gamma, r), dtype=dr.U.dtype, device=dev),
+            ws=torch.empty(max(1, B.dspark_workspace_size(B.WS_RNN_SAMPLE, R, gamma, V, r)),
+                           dtype=torch.uint8, device=dev),
+        )
     return dr
 
 
@@ -140,6 +154,13 @@ def schedule_production(d: DeviceRound):
     confidences, which is the capacity two rounds later."""
     B.dspark_schedule_ex(d.c, d.sps, B.SCHED_CAPACITY, d.cap, d.ell_p, d.admitted_p, d.theta_p)
     B.dspark_schedule_ex(d.c, d.sps, B.SCHED_WHOLE_WALK, None, d.ell_w, d.cap_next, d.theta_w)
+
+
+def rnn_sample(d: DeviceRound):
+    """The round's draft with the RNN head instead of the Markov head."""
+    q = d.rnn
+    B.dspark_rnn_sample(d.U, d.W1, d.W2t, q["W"], d.h, d.x0, d.G, d.g, q["x"], q["lse"], q["logit"], q["s"],
+                        q["o"], q["ws"])
 
 
 def verify_greedy(d: DeviceRound):
