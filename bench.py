@@ -153,6 +153,13 @@ def main():
                                ("verify", DR.verify), ("schedule_production", DR.schedule_production),
                                ("verify_greedy", DR.verify_greedy), ("acceptance", DR.acceptance),
                                ("rnn_sample", DR.rnn_sample))}
+    # sequential temperature scaling on a held-out set of 65536 rollouts
+    # (gamma = 16, 61 temperatures, 15 bins), captured the same way
+    zs, ns = W.make_rollouts(65536, w.gamma, 2.0)
+    sts_in = (torch.tensor(zs, device=dev), torch.tensor(ns, device=dev), torch.tensor(W.sts_grid(), device=dev))
+    binding.dspark_sts_fit(*sts_in, 15)
+    torch.cuda.synchronize()
+    graphs["sts_fit"] = [capture(lambda _d: binding.dspark_sts_fit(*sts_in, 15), None)] * 2
     torch.cuda.synchronize()
     log("[bench] graphs captured")
 
@@ -180,10 +187,10 @@ def main():
     # own: not part of the round above, which runs Algorithm 1
     # the other modes, each timed on its own and outside the round: the
     # production (asynchronous) scheduler's two calls, greedy verification of
-    # the round's drafts, the analytic acceptance of all its positions, and
-    # the draft with the RNN head
+    # the round's drafts, the analytic acceptance of all its positions, the
+    # draft with the RNN head, and the calibration fit
     modes = {}
-    for name in ("schedule_production", "verify_greedy", "acceptance", "rnn_sample"):
+    for name in ("schedule_production", "verify_greedy", "acceptance", "rnn_sample", "sts_fit"):
         modes[name] = timed(name, max(args.steps, 10), 2) * 1e3
         log(f"[bench] {name}: {modes[name]:.1f} us")
 

@@ -16,6 +16,7 @@
  *   dspark_verify         rejection-sampling verification + residual draw
  *   dspark_verify_greedy  temperature-0 (exact-match) verification
  *   dspark_acceptance     the analytic acceptance sum_v min(p_d, p_t) per position
+ *   dspark_sts_fit        sequential temperature scaling with ECE and AUC
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers to row-major arrays, 16-byte
@@ -75,7 +76,8 @@ typedef enum {
   DSPARK_WS_VERIFY = 3,
   DSPARK_WS_VERIFY_GREEDY = 4,
   DSPARK_WS_ACCEPTANCE = 5,
-  DSPARK_WS_RNN_SAMPLE = 6
+  DSPARK_WS_RNN_SAMPLE = 6,
+  DSPARK_WS_STS = 7         /* R = rollouts N, V = grid size, r = bins */
 } dspark_ws_kind;
 
 /*
@@ -329,6 +331,38 @@ dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r,
                                 const int32_t* row0, const void* U, const void* W1, const void* W2t,
                                 const int32_t* x0, const int32_t* x, const float* lse, float* c_star,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_sts_fit — sequential temperature scaling of the confidence head
+ * on a held-out set, with its calibration metrics.
+ *
+ * Passage: notes, "sequential temperature scaling (STS)" and the
+ * per-position reliability table (ROC-AUC, ECE before and after STS);
+ * paper-breakdown, the confidence-head paragraph.  For k = 1..gamma in
+ * order, T_k is the grid temperature minimising the ECE of the cumulative
+ * product a_k = a_{k-1} * sigmoid(z_k / T_k) (a_0 = 1) against prefix
+ * survival y_k = [n_acc >= k], T_1..T_{k-1} fixed; ties go to the first
+ * grid entry.  ECE: n_bins equal-width bins of [0, 1], bin min(floor(p M),
+ * M - 1), ECE = (1/N) sum_b |sum_{n in b} (y_n - p_n)|.  Predictions are
+ * fp32 (sigmoid(x) = 1 / (1 + exp(-x))); the bin sums are exact 64-bit
+ * integers in units of 2^-32, so the fit is deterministic.  ece_before is
+ * the raw chain's (every T = 1).  auc[k] is the ROC-AUC of the raw logit
+ * z_k between accepted (n_acc >= k) and rejected (n_acc = k - 1) rollouts
+ * that reached position k, ties counted half (NaN without both classes);
+ * it is an exact pair count, O(N^2) work per position.
+ *
+ *   z       [N][gamma] f32: the confidence head's logits per rollout
+ *   n_acc   [N] i32: accepted prefix length of each rollout, 0..gamma
+ *   grid    [n_grid] f32: candidate temperatures (> 0)
+ *   T       [gamma] f32 out; ece_before, ece_after, auc [gamma] f64 out
+ *   ws      workspace of dspark_workspace_size(DSPARK_WS_STS, N, gamma,
+ *           n_grid, n_bins, 0) bytes
+ *
+ * Limits: 1 <= N <= 2^20, gamma <= 64, n_grid <= 256, n_bins <= 32.
+ */
+dspark_status dspark_sts_fit(int N, int gamma, const float* z, const int32_t* n_acc, const float* grid,
+                             int n_grid, int n_bins, float* T, double* ece_before, double* ece_after,
+                             double* auc, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace a call needs (0 for an invalid shape).  Arguments that a
  * call does not take are ignored. */

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libdspark.so")
 
 F32, BF16 = 0, 1
 CHUNK = 16   # tokens per chunk of the two-level Gumbel draw
-WS_SAMPLE, WS_SCHEDULE, WS_VERIFY, WS_VERIFY_GREEDY, WS_ACCEPTANCE, WS_RNN_SAMPLE = 0, 2, 3, 4, 5, 6
+WS_SAMPLE, WS_SCHEDULE, WS_VERIFY, WS_VERIFY_GREEDY, WS_ACCEPTANCE, WS_RNN_SAMPLE, WS_STS = 0, 2, 3, 4, 5, 6, 7
 SCHED_EARLY_STOP, SCHED_WHOLE_WALK, SCHED_CAPACITY = 0, 1, 2
 
 _lib = None
@@ -39,6 +39,7 @@ _SIGNATURES = {
     "dspark_acceptance": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_rnn_sample": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _SZ, _P],
+    "dspark_sts_fit": [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
     "dspark_status_string": [_I],
 }
@@ -325,4 +326,25 @@ def dspark_rnn_sample(U, W1, W2t, Wrnn, h, x0, G, g, x=None, lse=None, logit=Non
                                _ptr(ws), ws.numel(), _stream())
     _raise("dspark_rnn_sample", st)
     return x, lse, logit, s, o
+
+
+def dspark_sts_fit(z, n_acc, grid, n_bins=15, ws=None):
+    """Sequential temperature scaling on a held-out set: T [gamma] f32 and
+    ece_before, ece_after, auc [gamma] f64."""
+    lib = load_library()
+    N, gamma = z.shape
+    dev = z.device
+    G = grid.shape[0]
+    _check(z, "z", (N, gamma), (torch.float32,), dev)
+    _check(n_acc, "n_acc", (N,), (torch.int32,), dev)
+    _check(grid, "grid", (G,), (torch.float32,), dev)
+    T = torch.empty(gamma, dtype=torch.float32, device=dev)
+    e0 = torch.empty(gamma, dtype=torch.float64, device=dev)
+    e1 = torch.empty(gamma, dtype=torch.float64, device=dev)
+    auc = torch.empty(gamma, dtype=torch.float64, device=dev)
+    ws = workspace(WS_STS, N, gamma, G, n_bins, dev) if ws is None else ws
+    st = lib.dspark_sts_fit(N, gamma, _ptr(z), _ptr(n_acc), _ptr(grid), G, int(n_bins), _ptr(T), _ptr(e0), _ptr(e1),
+                            _ptr(auc), _ptr(ws), ws.numel(), _stream())
+    _raise("dspark_sts_fit", st)
+    return T, e0, e1, auc
 

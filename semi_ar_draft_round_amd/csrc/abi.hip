@@ -12,6 +12,11 @@ namespace dspark {
 // sample.hip
 size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V);
 size_t rnn_workspace_bytes(int R, int r);
+// sts.hip
+size_t sts_workspace_bytes(int N, int gamma, int G, int M);
+bool sts_shape_ok(int N, int gamma, int G, int M);
+hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, const float* grid, int G, int M,
+                      float* T, double* ece_before, double* ece_after, double* auc, void* ws, hipStream_t s);
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
@@ -141,6 +146,9 @@ size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r
     case DSPARK_WS_RNN_SAMPLE:
       if (!draft_shape_ok(R, gamma, V) || r < 1) return 0;
       return rnn_sample_workspace_bytes(R, gamma, V, r);
+    case DSPARK_WS_STS:
+      if (!sts_shape_ok(R, gamma, V, r)) return 0;
+      return sts_workspace_bytes(R, gamma, V, r);
   }
   return 0;
 }
@@ -275,6 +283,20 @@ dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r,
   const RnnHead head{Wrnn, h, d, s, o, reinterpret_cast<float*>(static_cast<char*>(ws) + off)};
   if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, static_cast<hipStream_t>(stream),
                     &head) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_sts_fit(int N, int gamma, const float* z, const int32_t* n_acc, const float* grid,
+                             int n_grid, int n_bins, float* T, double* ece_before, double* ece_after, double* auc,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!sts_shape_ok(N, gamma, n_grid, n_bins)) return DSPARK_EINVAL;
+  if (!z || !n_acc || !grid || !T || !ece_before || !ece_after || !auc) return DSPARK_EINVAL;
+  if (!ws || ws_bytes < sts_workspace_bytes(N, gamma, n_grid, n_bins)) return DSPARK_EWORKSPACE;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (sts_launch(N, gamma, z, n_acc, grid, n_grid, n_bins, T, ece_before, ece_after, auc, ws,
+                 static_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

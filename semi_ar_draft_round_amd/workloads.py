@@ -240,3 +240,27 @@ def make_rnn_weights(w: Workload, gain: float = 1.0) -> np.ndarray:
     W = rng.normal(0.0, gain / np.sqrt(K), size=(3 * w.r, K)).astype(np.float32)
     return _store(W, w.dtype)
 
+
+def make_rollouts(N: int, gamma: int, beta: float = 2.0, seed: int = 99):
+    """A synthetic held-out set for calibrating the confidence head: each
+    rollout's true conditional acceptance at position k is q ~ Beta(6, 2);
+    the head reports the logit z = beta * logit(q) (beta > 1: overconfident);
+    the rollout accepts position k with probability q_k until its first
+    rejection.  Returns z [N][gamma] float32 and n_acc [N] int32 (0..gamma)."""
+    rng = np.random.default_rng([seed, N, gamma])
+    q = rng.beta(6.0, 2.0, size=(N, gamma))
+    z = (np.log(q / (1.0 - q)) * beta).astype(np.float32)
+    acc = rng.random((N, gamma)) < q
+    n_acc = np.where(acc.all(axis=1), gamma, np.argmin(acc, axis=1)).astype(np.int32)
+    return z, n_acc
+
+
+def sts_grid(G: int = 61, lo: float = 0.25, hi: float = 8.0) -> np.ndarray:
+    """Log-spaced candidate temperatures, with T = 1 itself when the range
+    holds it at a grid point."""
+    g = np.exp(np.linspace(np.log(lo), np.log(hi), G)).astype(np.float32)
+    i = int(np.argmin(np.abs(np.log(g))))
+    if abs(np.log(g[i])) < 1e-6:
+        g[i] = 1.0
+    return g
+

@@ -156,6 +156,18 @@ def test_rnn_sample_rejects_bad_arguments(lib):
     assert call(ws_bytes=8) == EWORKSPACE
 
 
+def test_sts_fit_rejects_bad_arguments(lib):
+    def call(N=100, gamma=4, G=16, M=15, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.dspark_sts_fit(N, gamma, ptr, ptr, ptr, G, M, ptr, ptr, ptr, ptr, ws, ws_bytes, None)
+    assert call(N=0) == EINVAL
+    assert call(N=(1 << 20) + 1) == EINVAL
+    assert call(G=257) == EINVAL
+    assert call(M=33) == EINVAL
+    assert call(gamma=65) == EINVAL
+    assert call(ptr=None) == EINVAL
+    assert call(ws_bytes=8) == EWORKSPACE
+
+
 def test_verify_rejects_bad_arguments(lib):
     def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
         args = [ptr] * 13
