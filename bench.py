@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-requests", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip timing the other modes (the production scheduler, greedy verification, the "
+                         "analytic acceptance, the RNN-head draft, STS), e.g. for counter runs on the round")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB a few times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -190,7 +193,8 @@ def main():
     # the round's drafts, the analytic acceptance of all its positions, the
     # draft with the RNN head, and the calibration fit
     modes = {}
-    for name in ("schedule_production", "verify_greedy", "acceptance", "rnn_sample", "sts_fit"):
+    for name in () if args.no_modes else ("schedule_production", "verify_greedy", "acceptance", "rnn_sample",
+                                          "sts_fit"):
         modes[name] = timed(name, max(args.steps, 10), 2) * 1e3
         log(f"[bench] {name}: {modes[name]:.1f} us")
 

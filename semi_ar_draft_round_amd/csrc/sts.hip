@@ -130,38 +130,48 @@ __global__ __launch_bounds__(kStsThreads) void sts_update(int N, int gamma, int 
   a_raw[n] = a_raw[n] * sigmoid_f32(x);
 }
 
-// Pair counts for the AUC of position k: thread = one rollout i (counted
-// when accepted at k), tiles of rollouts j staged in LDS (counted when
-// rejected at k).  Both must have reached k (n_acc >= k, 0-based).
+// Pair counts for the AUC of position k.  Thread = one rollout i of
+// blockIdx.x's range (counted when accepted at k); blockIdx.y takes one
+// chunk of the rollouts j, staged through LDS a tile at a time with the
+// logit of a rollout that was not rejected at k replaced by NaN (it then
+// compares false both ways).  Both must have reached k (n_acc >= k, 0-based).
+constexpr int kStsAucChunks = 8;
+
 __global__ __launch_bounds__(kStsThreads) void sts_auc(int N, int gamma, int k, const float* __restrict__ z,
                                                        const int32_t* __restrict__ n_acc,
                                                        unsigned long long* __restrict__ pairs) {
-  __shared__ float sz[kStsThreads];
-  __shared__ int sneg[kStsThreads];
+  __shared__ __attribute__((aligned(16))) float sz[kStsThreads];
   __shared__ unsigned long long red[kStsThreads / kWave][3];
   const int i = blockIdx.x * kStsThreads + threadIdx.x;
   const bool pos = i < N && n_acc[i] >= k + 1;
   const float zi = i < N ? z[static_cast<int64_t>(i) * gamma + k] : 0.f;
-  unsigned long long cnt = 0;
-  unsigned long long negs = 0;
-  for (int j0 = 0; j0 < N; j0 += kStsThreads) {
+  const int per = ceil_div(ceil_div(N, kStsThreads), kStsAucChunks) * kStsThreads;
+  const int j_lo = blockIdx.y * per, j_hi = min(N, j_lo + per);
+  unsigned long long cnt = 0, negs = 0;
+  for (int j0 = j_lo; j0 < j_hi; j0 += kStsThreads) {
     const int j = j0 + threadIdx.x;
-    sneg[threadIdx.x] = j < N && n_acc[j] == k;
-    sz[threadIdx.x] = j < N ? z[static_cast<int64_t>(j) * gamma + k] : 0.f;
+    const bool neg = j < j_hi && n_acc[j] == k;
+    sz[threadIdx.x] = neg ? z[static_cast<int64_t>(j) * gamma + k] : __builtin_nanf("");
+    negs += (blockIdx.x == 0 && neg) ? 1ull : 0ull;
     __syncthreads();
     if (pos) {
       unsigned int c = 0;
-#pragma unroll 8
-      for (int q = 0; q < kStsThreads; ++q)
-        c += sneg[q] ? (zi > sz[q] ? 2u : (zi == sz[q] ? 1u : 0u)) : 0u;
+      const float4* s4 = reinterpret_cast<const float4*>(sz);
+#pragma unroll 4
+      for (int q = 0; q < kStsThreads / 4; ++q) {
+        const float4 v = s4[q];
+        c += (zi > v.x ? 2u : 0u) + (zi == v.x ? 1u : 0u);
+        c += (zi > v.y ? 2u : 0u) + (zi == v.y ? 1u : 0u);
+        c += (zi > v.z ? 2u : 0u) + (zi == v.z ? 1u : 0u);
+        c += (zi > v.w ? 2u : 0u) + (zi == v.w ? 1u : 0u);
+      }
       cnt += c;
     }
-    if (blockIdx.x == 0)
-      for (int q = 0; q < kStsThreads; ++q) negs += (threadIdx.x == 0 && sneg[q]) ? 1ull : 0ull;
     __syncthreads();
   }
-  // the block's totals: pair count, accepted rollouts, and (block 0) rejected ones
-  unsigned long long v[3] = {cnt, pos ? 1ull : 0ull, negs};
+  // the block's totals: pair count, accepted rollouts (first chunk only),
+  // rejected rollouts (first block column only)
+  unsigned long long v[3] = {cnt, (pos && blockIdx.y == 0) ? 1ull : 0ull, negs};
 #pragma unroll
   for (int e = 0; e < 3; ++e)
 #pragma unroll
@@ -225,7 +235,8 @@ hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, co
                        ece_after);
     hipLaunchKernelGGL(sts_update, dim3(blocksN), dim3(kStsThreads), 0, s, N, gamma, k, z, grid, w.best, w.a,
                        w.a_raw);
-    hipLaunchKernelGGL(sts_auc, dim3(blocksN), dim3(kStsThreads), 0, s, N, gamma, k, z, n_acc, w.pairs);
+    hipLaunchKernelGGL(sts_auc, dim3(blocksN, kStsAucChunks), dim3(kStsThreads), 0, s, N, gamma, k, z, n_acc,
+                       w.pairs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(sts_auc_finish, dim3(1), dim3(64), 0, s, gamma, w.pairs, auc);
