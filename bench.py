@@ -158,11 +158,13 @@ def main():
                                ("rnn_sample", DR.rnn_sample))}
     # sequential temperature scaling on a held-out set of 65536 rollouts
     # (gamma = 16, 61 temperatures, 15 bins), captured the same way
-    zs, ns = W.make_rollouts(65536, w.gamma, 2.0)
-    sts_in = (torch.tensor(zs, device=dev), torch.tensor(ns, device=dev), torch.tensor(W.sts_grid(), device=dev))
-    binding.dspark_sts_fit(*sts_in, 15)
-    torch.cuda.synchronize()
-    graphs["sts_fit"] = [capture(lambda _d: binding.dspark_sts_fit(*sts_in, 15), None)] * 2
+    if not args.no_modes:
+        zs, ns = W.make_rollouts(65536, w.gamma, 2.0)
+        sts_in = (torch.tensor(zs, device=dev), torch.tensor(ns, device=dev),
+                  torch.tensor(W.sts_grid(), device=dev))
+        binding.dspark_sts_fit(*sts_in, 15)
+        torch.cuda.synchronize()
+        graphs["sts_fit"] = [capture(lambda _d: binding.dspark_sts_fit(*sts_in, 15), None)] * 2
     torch.cuda.synchronize()
     log("[bench] graphs captured")
 
