@@ -14,6 +14,7 @@
  *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
  *   dspark_schedule_ex    the same with the production admission rules
  *   dspark_verify         rejection-sampling verification + residual draw
+ *   dspark_verify_ex      the same with the RNN head's bias vectors
  *   dspark_verify_greedy  temperature-0 (exact-match) verification
  *   dspark_acceptance     the analytic acceptance sum_v min(p_d, p_t) per position
  *   dspark_sts_fit        sequential temperature scaling with ECE and AUC
@@ -322,6 +323,8 @@ dspark_status dspark_verify_greedy(dspark_dtype dt, int R, int gamma, int V, con
  *   target, row0  as in dspark_verify; rows 0 .. gamma-1 of every request are
  *           read (row0[r] + k when packed)
  *   U, W1, W2t, x0, x, lse  as in dspark_verify
+ *   bvec    [R][gamma][r] dt or NULL: the drafter's bias vectors (the `o`
+ *           output of dspark_rnn_sample) in W1[x_{k-1}]'s place
  *   c_star  [R][gamma] f32 out
  *   ws      workspace of dspark_workspace_size(DSPARK_WS_ACCEPTANCE, ...) bytes
  *
@@ -329,8 +332,8 @@ dspark_status dspark_verify_greedy(dspark_dtype dt, int R, int gamma, int V, con
  */
 dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
                                 const int32_t* row0, const void* U, const void* W1, const void* W2t,
-                                const int32_t* x0, const int32_t* x, const float* lse, float* c_star,
-                                void* ws, size_t ws_bytes, void* stream);
+                                const void* bvec, const int32_t* x0, const int32_t* x, const float* lse,
+                                float* c_star, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_sts_fit — sequential temperature scaling of the confidence head
@@ -363,6 +366,23 @@ dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r,
 dspark_status dspark_sts_fit(int N, int gamma, const float* z, const int32_t* n_acc, const float* grid,
                              int n_grid, int n_bins, float* T, double* ece_before, double* ece_after,
                              double* auc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_verify_ex — dspark_verify for a drafter whose bias vector is not a
+ * W1 row (the RNN head).
+ *
+ * Passage: as dspark_verify, with eq (6)'s bias B_k = o_k W2: p_d at the
+ * first rejected position n is rebuilt from U_n and the bias vector o_n,
+ * bvec[r][n], instead of W1[x_{n-1}].  bvec NULL is dspark_verify.
+ *
+ *   bvec    [R][gamma][r] dt or NULL: the `o` output of dspark_rnn_sample
+ *   every other argument as in dspark_verify
+ */
+dspark_status dspark_verify_ex(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                               const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                               const void* bvec, const int32_t* x0, const int32_t* x, const float* lse,
+                               const float* logit, const int32_t* ell, const float* u_acc, const float* u_res,
+                               int32_t* n_acc, int32_t* next_tok, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace a call needs (0 for an invalid shape).  Arguments that a
  * call does not take are ignored. */

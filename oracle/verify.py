@@ -52,13 +52,17 @@ def _target_row(target: np.ndarray, row0, r: int, i: int) -> np.ndarray:
 
 
 def draft_logits_at(U: np.ndarray, E: np.ndarray, W2t: np.ndarray, x0: np.ndarray,
-                    x: np.ndarray, r: int, i: int) -> np.ndarray:
-    """U_i + B_i for request r at draft position i (eq 4's exponent)."""
+                    x: np.ndarray, r: int, i: int, bvec=None) -> np.ndarray:
+    """U_i + B_i for request r at draft position i (eq 4's exponent).  With
+    bvec [R][gamma][r] (another head's bias vectors, e.g. the RNN head's
+    o_i), B_i = bvec[r, i] W2 instead of the Markov head's W1[x_{i-1}] W2."""
+    if bvec is not None:
+        return U[r, i] + W2t @ np.asarray(bvec[r, i], dtype=np.float64)
     prev = int(x0[r]) if i == 0 else int(x[r, i - 1])
     return U[r, i] + markov_bias(E, W2t, np.array([prev]))[0]
 
 
-def accept_log_ratios(target, row0, U, E, W2t, x0, x, ell):
+def accept_log_ratios(target, row0, U, E, W2t, x0, x, ell, bvec=None):
     """For each request, ln p_t(x_i) - ln p_d(x_i) for i < l_r (a list of arrays)."""
     R = U.shape[0]
     out = []
@@ -66,7 +70,7 @@ def accept_log_ratios(target, row0, U, E, W2t, x0, x, ell):
         vals = []
         for i in range(int(ell[r])):
             lt = _target_row(target, row0, r, i)
-            ld = draft_logits_at(U, E, W2t, x0, x, r, i)
+            ld = draft_logits_at(U, E, W2t, x0, x, r, i, bvec)
             xi = int(x[r, i])
             vals.append((lt[xi] - logsumexp(lt)) - (ld[xi] - logsumexp(ld)))
         out.append(np.array(vals))
@@ -82,13 +86,13 @@ def first_rejection(log_ratio: np.ndarray, u: np.ndarray) -> int:
     return int(log_ratio.shape[0])
 
 
-def residual(target, row0, U, E, W2t, x0, x, r: int, n: int, ell_r: int) -> np.ndarray:
+def residual(target, row0, U, E, W2t, x0, x, r: int, n: int, ell_r: int, bvec=None) -> np.ndarray:
     """The distribution (unnormalised) the next token is drawn from."""
     lt = _target_row(target, row0, r, n)
     pt = np.exp(lt - logsumexp(lt))
     if n >= ell_r:
         return pt                                   # bonus row: p_t itself
-    ld = draft_logits_at(U, E, W2t, x0, x, r, n)
+    ld = draft_logits_at(U, E, W2t, x0, x, r, n, bvec)
     pd = np.exp(ld - logsumexp(ld))
     res = np.maximum(0.0, pt - pd)
     if not (res.sum() > 0.0):
@@ -104,13 +108,13 @@ def inverse_cdf(res: np.ndarray, u: float) -> int:
     return min(v, res.shape[0] - 1)
 
 
-def verify(target, row0, U, E, W2t, x0, x, ell, u_acc, u_res, n_teacher=None) -> dict:
+def verify(target, row0, U, E, W2t, x0, x, ell, u_acc, u_res, n_teacher=None, bvec=None) -> dict:
     """Accepted lengths n_acc [R] and next tokens next_tok [R].
 
     n_teacher: when given, the residual draw uses these accepted lengths instead
     of the oracle's own (to check another implementation past a near-tie)."""
     R = U.shape[0]
-    logr = accept_log_ratios(target, row0, U, E, W2t, x0, x, ell)
+    logr = accept_log_ratios(target, row0, U, E, W2t, x0, x, ell, bvec)
     n_acc = np.zeros(R, dtype=np.int64)
     next_tok = np.zeros(R, dtype=np.int64)
     margins = []
@@ -120,7 +124,7 @@ def verify(target, row0, U, E, W2t, x0, x, ell, u_acc, u_res, n_teacher=None) ->
         if logr[r].shape[0]:
             margins.append(np.abs(np.log(u_acc[r, :logr[r].shape[0]].astype(np.float64)) - logr[r]))
         n_use = n if n_teacher is None else int(n_teacher[r])
-        res = residual(target, row0, U, E, W2t, x0, x, r, n_use, int(ell[r]))
+        res = residual(target, row0, U, E, W2t, x0, x, r, n_use, int(ell[r]), bvec)
         next_tok[r] = inverse_cdf(res, u_res[r])
     return dict(n_acc=n_acc, next_tok=next_tok, log_ratio=logr, margins=margins)
 
@@ -157,7 +161,7 @@ def verify_greedy(target, row0, x, ell) -> dict:
     return dict(n_acc=n_acc, next_tok=next_tok)
 
 
-def analytic_acceptance(target, row0, U, E, W2t, x0, x, lse=None) -> np.ndarray:
+def analytic_acceptance(target, row0, U, E, W2t, x0, x, lse=None, bvec=None) -> np.ndarray:
     """c*[r, k] = sum_v min(p_d(v), p_t(v)) at every drafted position k, in
     float64.  p_d is the drafter's softmax at position k (U_k plus the Markov
     bias of x_{k-1}); its log-normaliser is computed here, or taken from
@@ -169,7 +173,7 @@ def analytic_acceptance(target, row0, U, E, W2t, x0, x, lse=None) -> np.ndarray:
         for k in range(gamma):
             lt = np.asarray(_target_row(target, row0, r, k), dtype=np.float64)
             pt = np.exp(lt - logsumexp(lt))
-            ld = draft_logits_at(U, E, W2t, x0, x, r, k).astype(np.float64)
+            ld = draft_logits_at(U, E, W2t, x0, x, r, k, bvec).astype(np.float64)
             nd = logsumexp(ld) if lse is None else float(lse[r, k])
             pd = np.exp(ld - nd)
             out[r, k] = float(np.minimum(pd, pt).sum())

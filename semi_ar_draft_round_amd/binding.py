@@ -36,7 +36,9 @@ _SIGNATURES = {
     "dspark_verify": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, _SZ, _P],
     "dspark_verify_greedy": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
-    "dspark_acceptance": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_acceptance": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_verify_ex": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                         _SZ, _P],
     "dspark_rnn_sample": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _SZ, _P],
     "dspark_sts_fit": [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
@@ -216,8 +218,9 @@ def dspark_schedule_ex(c, sps, mode, cap=None, ell=None, admitted=None, theta_be
 
 
 def dspark_verify(target, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res, row0=None,
-                  n_acc=None, next_tok=None, ws=None):
-    """n_acc [R], next_tok [R] int32: rejection sampling with residual draw."""
+                  n_acc=None, next_tok=None, ws=None, bvec=None):
+    """n_acc [R], next_tok [R] int32: rejection sampling with residual draw.
+    bvec: the RNN head's bias vectors [R][gamma][r] (dspark_verify_ex)."""
     lib = load_library()
     R, gamma, V = U.shape
     r = W1.shape[1]
@@ -241,11 +244,19 @@ def dspark_verify(target, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res, row0
     n_acc = torch.empty(R, dtype=torch.int32, device=dev) if n_acc is None else n_acc
     next_tok = torch.empty(R, dtype=torch.int32, device=dev) if next_tok is None else next_tok
     ws = workspace(WS_VERIFY, R, gamma, V, r, dev) if ws is None else ws
-    st = lib.dspark_verify(_dt(U), R, gamma, V, r, _ptr(target), _ptr(row0), _ptr(U), _ptr(W1),
-                           _ptr(W2t), _ptr(x0), _ptr(x), _ptr(lse), _ptr(logit), _ptr(ell),
-                           _ptr(u_acc), _ptr(u_res), _ptr(n_acc), _ptr(next_tok), _ptr(ws),
-                           ws.numel(), _stream())
-    _raise("dspark_verify", st)
+    if bvec is None:
+        st = lib.dspark_verify(_dt(U), R, gamma, V, r, _ptr(target), _ptr(row0), _ptr(U), _ptr(W1),
+                               _ptr(W2t), _ptr(x0), _ptr(x), _ptr(lse), _ptr(logit), _ptr(ell),
+                               _ptr(u_acc), _ptr(u_res), _ptr(n_acc), _ptr(next_tok), _ptr(ws),
+                               ws.numel(), _stream())
+        _raise("dspark_verify", st)
+    else:
+        _check(bvec, "bvec", (R, gamma, r), sdt, dev)
+        st = lib.dspark_verify_ex(_dt(U), R, gamma, V, r, _ptr(target), _ptr(row0), _ptr(U), _ptr(W1),
+                                  _ptr(W2t), _ptr(bvec), _ptr(x0), _ptr(x), _ptr(lse), _ptr(logit), _ptr(ell),
+                                  _ptr(u_acc), _ptr(u_res), _ptr(n_acc), _ptr(next_tok), _ptr(ws),
+                                  ws.numel(), _stream())
+        _raise("dspark_verify_ex", st)
     return n_acc, next_tok
 
 
@@ -275,7 +286,7 @@ def dspark_verify_greedy(target, x, ell, row0=None, n_acc=None, next_tok=None, w
     return n_acc, next_tok
 
 
-def dspark_acceptance(target, U, W1, W2t, x0, x, lse, row0=None, c_star=None, ws=None):
+def dspark_acceptance(target, U, W1, W2t, x0, x, lse, row0=None, c_star=None, ws=None, bvec=None):
     """c_star [R][gamma] f32: sum_v min(p_d, p_t) at every drafted position."""
     lib = load_library()
     R, gamma, V = U.shape
@@ -291,8 +302,11 @@ def dspark_acceptance(target, U, W1, W2t, x0, x, lse, row0=None, c_star=None, ws
     _check(lse, "lse", (R, gamma), (torch.float32,), dev)
     c_star = torch.empty((R, gamma), dtype=torch.float32, device=dev) if c_star is None else c_star
     ws = workspace(WS_ACCEPTANCE, R, gamma, V, r, dev) if ws is None else ws
+    if bvec is not None:
+        _check(bvec, "bvec", (R, gamma, r), sdt, dev)
     st = lib.dspark_acceptance(_dt(U), R, gamma, V, r, _ptr(target), _ptr(row0), _ptr(U), _ptr(W1), _ptr(W2t),
-                               _ptr(x0), _ptr(x), _ptr(lse), _ptr(c_star), _ptr(ws), ws.numel(), _stream())
+                               _ptr(bvec), _ptr(x0), _ptr(x), _ptr(lse), _ptr(c_star), _ptr(ws), ws.numel(),
+                               _stream())
     _raise("dspark_acceptance", st)
     return c_star
 

@@ -37,13 +37,14 @@ hipError_t verify_greedy_launch(dspark_dtype dt, int R, int gamma, int V, const 
                                 hipStream_t s);
 hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
                              const int32_t* row0, const void* U, const void* W1, const void* W2t, const int32_t* x0,
-                             const int32_t* x, const float* lse, float* c_star, void* ws, hipStream_t s);
+                             const int32_t* x, const float* lse, float* c_star, void* ws, hipStream_t s,
+                             const void* bvec);
 size_t verify_workspace_bytes(int R, int gamma, int V);
 hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
                          const int32_t* row0, const void* U, const void* W1, const void* W2t,
                          const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
                          const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
-                         int32_t* next_tok, void* ws, hipStream_t s);
+                         int32_t* next_tok, void* ws, hipStream_t s, const void* bvec);
 
 namespace {
 
@@ -213,11 +214,11 @@ dspark_status dspark_schedule(int R, int gamma, const float* c, const double* sp
                             theta_best, ws, ws_bytes, stream);
 }
 
-dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
-                            const int32_t* row0, const void* U, const void* W1, const void* W2t,
-                            const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
-                            const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
-                            int32_t* next_tok, void* ws, size_t ws_bytes, void* stream) {
+dspark_status dspark_verify_ex(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                               const int32_t* row0, const void* U, const void* W1, const void* W2t, const void* bvec,
+                               const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
+                               const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
+                               int32_t* next_tok, void* ws, size_t ws_bytes, void* stream) {
   if (!dtype_ok(dt)) return DSPARK_EDTYPE;
   if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
   if (static_cast<int64_t>(R) * (gamma + 1) > 0x7FFFFFFF) return DSPARK_EINVAL;
@@ -229,9 +230,18 @@ dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r, con
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
   if (verify_launch(dt, R, gamma, V, r, target, row0, U, W1, W2t, x0, x, lse, logit, ell, u_acc, u_res,
-                    n_acc, next_tok, ws, static_cast<hipStream_t>(stream)) != hipSuccess)
+                    n_acc, next_tok, ws, static_cast<hipStream_t>(stream), bvec) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
+}
+
+dspark_status dspark_verify(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
+                            const int32_t* row0, const void* U, const void* W1, const void* W2t,
+                            const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
+                            const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
+                            int32_t* next_tok, void* ws, size_t ws_bytes, void* stream) {
+  return dspark_verify_ex(dt, R, gamma, V, r, target, row0, U, W1, W2t, nullptr, x0, x, lse, logit, ell, u_acc,
+                          u_res, n_acc, next_tok, ws, ws_bytes, stream);
 }
 
 dspark_status dspark_verify_greedy(dspark_dtype dt, int R, int gamma, int V, const void* target,
@@ -251,8 +261,8 @@ dspark_status dspark_verify_greedy(dspark_dtype dt, int R, int gamma, int V, con
 
 dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
                                 const int32_t* row0, const void* U, const void* W1, const void* W2t,
-                                const int32_t* x0, const int32_t* x, const float* lse, float* c_star, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                const void* bvec, const int32_t* x0, const int32_t* x, const float* lse,
+                                float* c_star, void* ws, size_t ws_bytes, void* stream) {
   if (!dtype_ok(dt)) return DSPARK_EDTYPE;
   if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
   if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
@@ -261,7 +271,7 @@ dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r,
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
   if (acceptance_launch(dt, R, gamma, V, r, target, row0, U, W1, W2t, x0, x, lse, c_star, ws,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
+                        static_cast<hipStream_t>(stream), bvec) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

@@ -345,14 +345,17 @@ struct ResidualRow {
   int64_t urow;     // draft row index (request * gamma + n), valid when rej
   float lt, ld;     // target and draft log-normalisers of that row
   int prev;         // previous token for the Markov bias, -1 if none / not needed
+  int64_t brow;     // row of the bias-vector table (W1: the previous token; or the given
+                    // per-(request, position) vectors: the draft row), -1 for bias 0
   bool rej, live;
 };
 
 __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, int V, const int32_t* row0,
                                                     const int32_t* x0, const int32_t* x,
                                                     const int32_t* ell, const int32_t* n_acc,
-                                                    const float* lse_t, const float* lse) {
-  ResidualRow rr{0, 0, 0.f, 0.f, -1, false, false};
+                                                    const float* lse_t, const float* lse,
+                                                    bool hasb) {
+  ResidualRow rr{0, 0, 0.f, 0.f, -1, -1, false, false};
   if (req >= R) return rr;
   rr.live = true;
   const int L = min(max(ell[req], 0), gamma);
@@ -364,6 +367,7 @@ __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, i
   if (rr.rej) {
     rr.ld = lse[rr.urow];
     rr.prev = token_or_none((n == 0) ? x0[req] : x[static_cast<int64_t>(req) * gamma + n - 1], V);
+    rr.brow = hasb ? rr.urow : rr.prev;
   }
   return rr;
 }
@@ -374,7 +378,7 @@ __device__ __forceinline__ ResidualRow residual_row(int req, int R, int gamma, i
 // normaliser is merged from the row's parts.
 __device__ __forceinline__ ResidualRow acceptance_row(int rho, int gamma, int V, const int32_t* row0,
                                                       const int32_t* x0, const int32_t* x, const float2* part,
-                                                      const float* lse) {
+                                                      const float* lse, bool hasb) {
   const int r = rho / gamma, k = rho % gamma;
   const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + k;
   ResidualRow rr;
@@ -389,6 +393,7 @@ __device__ __forceinline__ ResidualRow acceptance_row(int rho, int gamma, int V,
   rr.lt = acc.M + logf(acc.S);
   rr.ld = lse[rho];
   rr.prev = token_or_none(k == 0 ? x0[r] : x[rho - 1], V);
+  rr.brow = hasb ? rho : rr.prev;
   rr.rej = true;
   rr.live = true;
   return rr;
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
     float* __restrict__ csum, float* __restrict__ psum, const float2* __restrict__ part,
-    float* __restrict__ accp) {
+    float* __restrict__ accp, const uint16_t* __restrict__ bvec) {
   constexpr float kL2e = 1.4426950408889634f;
   constexpr int NROWS = 32 * RQ;
   constexpr int kW = wide_tile_bytes<KS16>();
@@ -441,8 +446,8 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   const auto clampc = [&](int it) { return it < nT ? it : nT - 1; };
   const auto tile_of = [&](int it) { return static_cast<int>(blockIdx.x) + it * static_cast<int>(gridDim.x); };
 
-  const ResidualRow rr = ACC ? acceptance_row(min(req, nrows - 1), gamma, V, row0, x0, x, part, lse)
-                             : residual_row(min(req, R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  const ResidualRow rr = ACC ? acceptance_row(min(req, nrows - 1), gamma, V, row0, x0, x, part, lse, bvec)
+                             : residual_row(min(req, R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse, bvec);
   float mn = 0.f;   // ACC: the lane's sum of min(p_t, p_d)
   const uint16_t* trow = target + rr.trow * V;
   const uint16_t* urow = U + (rr.rej ? rr.urow : 0) * V;
@@ -463,7 +468,8 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   load_lane(even, 0);
   load_lane(odd, 1);
   bf16x8 e[KS16];
-  const uint16_t* w1row = (rr.rej && rr.prev >= 0 ? W1 + static_cast<int64_t>(rr.prev) * (KS16 * 16) : kZeroRow) + 8 * h;
+  const uint16_t* btab = bvec ? bvec : W1;
+  const uint16_t* w1row = (rr.rej && rr.brow >= 0 ? btab + rr.brow * (KS16 * 16) : kZeroRow) + 8 * h;
 #pragma unroll
   for (int ks = 0; ks < KS16; ++ks) e[ks] = load_bf16x8_global(w1row + 16 * ks);
   wide_store_w<KS16, RQ>(lds, wr);
@@ -544,11 +550,11 @@ __global__ __launch_bounds__(64) void verify_residual_f32(
     const float* __restrict__ U, const float* __restrict__ W1, const float* __restrict__ W2t,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
-    float* __restrict__ csum, float* __restrict__ psum) {
+    float* __restrict__ csum, float* __restrict__ psum, const float* __restrict__ bvec) {
   const int tile = blockIdx.x;
   const int req = blockIdx.y;
   const int lane = threadIdx.x;
-  const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
+  const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse, bvec);
   const int v = tile * kChunk + lane;
   float res = 0.f, pt = 0.f;
   if (v < V) {
@@ -556,8 +562,8 @@ __global__ __launch_bounds__(64) void verify_residual_f32(
     res = pt;
     if (rr.rej) {
       float b = 0.f;
-      if (rr.prev >= 0) {
-        const float* e = W1 + static_cast<int64_t>(rr.prev) * r;
+      if (rr.brow >= 0) {
+        const float* e = (bvec ? bvec : W1) + rr.brow * r;
         const float* w = W2t + static_cast<int64_t>(v) * r;
         for (int i = 0; i < r; ++i) b = fmaf(e[i], w[i], b);
       }
@@ -586,18 +592,18 @@ __global__ __launch_bounds__(64) void verify_acceptance_f32(
     int R, int gamma, int V, int r, const float* __restrict__ target, const int32_t* __restrict__ row0,
     const float* __restrict__ U, const float* __restrict__ W1, const float* __restrict__ W2t,
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
-    const float2* __restrict__ part, float* __restrict__ accp) {
+    const float2* __restrict__ part, float* __restrict__ accp, const float* __restrict__ bvec) {
   const int rho = blockIdx.x;
   const int tile = blockIdx.y;
   const int lane = threadIdx.x;
-  const ResidualRow rr = acceptance_row(rho, gamma, V, row0, x0, x, part, lse);
+  const ResidualRow rr = acceptance_row(rho, gamma, V, row0, x0, x, part, lse, bvec);
   const int v = tile * kChunk + lane;
   float mn = 0.f;
   if (v < V) {
     const float pt = __expf(target[rr.trow * V + v] - rr.lt);
     float b = 0.f;
-    if (rr.prev >= 0) {
-      const float* e = W1 + static_cast<int64_t>(rr.prev) * r;
+    if (rr.brow >= 0) {
+      const float* e = (bvec ? bvec : W1) + rr.brow * r;
       const float* w = W2t + static_cast<int64_t>(v) * r;
       for (int i = 0; i < r; ++i) b = fmaf(e[i], w[i], b);
     }
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(256) void verify_select(
     const int32_t* __restrict__ x0, const int32_t* __restrict__ x, const float* __restrict__ lse,
     const int32_t* __restrict__ ell, const int32_t* __restrict__ n_acc, const float* __restrict__ lse_t,
     const float* __restrict__ u_res, const float* __restrict__ csum, const float* __restrict__ psum,
-    int32_t* __restrict__ next_tok) {
+    int32_t* __restrict__ next_tok, const typename Elt::T* __restrict__ bvec) {
   constexpr int kT = 256;
   constexpr int kSelVec = 12;
   __shared__ float wsum[kT / kWave];
@@ -648,10 +654,10 @@ __global__ __launch_bounds__(256) void verify_select(
   const int tid = threadIdx.x;
   const int nG = (V + kGChunk - 1) / kGChunk;
   const int ldm = mass_stride(V);
-  const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse);
-  // the previous token's W1 row, for the bias of the chunk's tokens
-  if (rr.rej && rr.prev >= 0)
-    for (int i = tid; i < r; i += kT) e_row[i] = Elt::load(W1, static_cast<int64_t>(rr.prev) * r + i);
+  const ResidualRow rr = residual_row(req, R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse, bvec);
+  // the previous token's W1 row (or the given bias vector), for the bias of the chunk's tokens
+  if (rr.rej && rr.brow >= 0)
+    for (int i = tid; i < r; i += kT) e_row[i] = Elt::load(bvec ? bvec : W1, rr.brow * r + i);
   const int seg4 = (ldm / 4 + kT - 1) / kT;    // vectors per thread
   const int lo = tid * seg4 * 4;
   const int hi = min(nG, lo + seg4 * 4);
@@ -746,7 +752,7 @@ __global__ __launch_bounds__(256) void verify_select(
       tl = Elt::load(target, rr.trow * V + v);
       if (!use_pt) ul = Elt::load(U, rr.urow * V + v);
     }
-    if (!use_pt && rr.prev >= 0) {
+    if (!use_pt && rr.brow >= 0) {
       const typename Elt::T* w = W2t + static_cast<int64_t>(v) * r;
 #pragma unroll 16
       for (int i = sl; i < r; i += kGChunk) b = fmaf(e_row[i], Elt::load(w, i), b);
@@ -824,6 +830,7 @@ struct SweepArgs {
   float *csum, *psum;
   const float2* part;
   float* accp;
+  const void* bvec;   // per-(request, position) bias vectors in W1[x_prev]'s place, or null
 };
 
 // Launches the 32x32x16 sweep over `rows` rows (R residual rows, or R gamma
@@ -839,11 +846,11 @@ static int launch_residual_wide(const SweepArgs& a, int rows, hipStream_t s) {
   if (a.V % kGChunk == 0)
     hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, true, ACC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R,
                        a.gamma, a.V, b16(a.target), a.row0, b16(a.U), b16(a.W1), b16(a.W2t), a.x0, a.x, a.lse,
-                       a.ell, a.n_acc, a.lse_t, a.csum, a.psum, a.part, a.accp);
+                       a.ell, a.n_acc, a.lse_t, a.csum, a.psum, a.part, a.accp, b16(a.bvec));
   else
     hipLaunchKernelGGL((verify_residual_wide<RQ, KS16, false, ACC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R,
                        a.gamma, a.V, b16(a.target), a.row0, b16(a.U), b16(a.W1), b16(a.W2t), a.x0, a.x, a.lse,
-                       a.ell, a.n_acc, a.lse_t, a.csum, a.psum, a.part, a.accp);
+                       a.ell, a.n_acc, a.lse_t, a.csum, a.psum, a.part, a.accp, b16(a.bvec));
   return gx;
 }
 
@@ -868,7 +875,7 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                          const int32_t* row0, const void* U, const void* W1, const void* W2t,
                          const int32_t* x0, const int32_t* x, const float* lse, const float* logit,
                          const int32_t* ell, const float* u_acc, const float* u_res, int32_t* n_acc,
-                         int32_t* next_tok, void* ws, hipStream_t s) {
+                         int32_t* next_tok, void* ws, hipStream_t s, const void* bvec) {
   const VerifyWs w = carve(ws, R, gamma, V);
   hipError_t err;
   const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
@@ -885,25 +892,25 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (dt == DSPARK_BF16) {
     const SweepArgs a{R, gamma, V, target, U, W1, W2t, row0, x0, x, ell, n_acc, lse, w.lse_t, w.csum, w.psum,
-                      nullptr, nullptr};
+                      nullptr, nullptr, bvec};
     launch_residual_wide_r<false>(a, r, R, s);
   } else {
     hipLaunchKernelGGL(verify_residual_f32, dim3(ceil_div(V, kChunk), R), dim3(64), 0, s, R, gamma, V, r,
                        static_cast<const float*>(target), row0, static_cast<const float*>(U),
                        static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, ell,
-                       n_acc, w.lse_t, w.csum, w.psum);
+                       n_acc, w.lse_t, w.csum, w.psum, static_cast<const float*>(bvec));
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (dt == DSPARK_BF16)
     hipLaunchKernelGGL(verify_select<BF16>, dim3(R), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const uint16_t*>(target), row0, static_cast<const uint16_t*>(U),
                        static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W2t), x0, x, lse,
-                       ell, n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok);
+                       ell, n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok, static_cast<const uint16_t*>(bvec));
   else
     hipLaunchKernelGGL(verify_select<F32>, dim3(R), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const float*>(target), row0, static_cast<const float*>(U),
                        static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, ell,
-                       n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok);
+                       n_acc, w.lse_t, u_res, w.csum, w.psum, next_tok, static_cast<const float*>(bvec));
   return hipGetLastError();
 }
 
@@ -943,7 +950,8 @@ hipError_t verify_greedy_launch(dspark_dtype dt, int R, int gamma, int V, const 
 
 hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* target,
                              const int32_t* row0, const void* U, const void* W1, const void* W2t, const int32_t* x0,
-                             const int32_t* x, const float* lse, float* c_star, void* ws, hipStream_t s) {
+                             const int32_t* x, const float* lse, float* c_star, void* ws, hipStream_t s,
+                             const void* bvec) {
   float2* part = static_cast<float2*>(ws);
   float* accp = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                          align256(sizeof(float2) * R * (gamma + 1) * kLseSplits));
@@ -960,13 +968,14 @@ hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, co
   int parts;
   if (dt == DSPARK_BF16) {
     const SweepArgs a{R, gamma, V, target, U, W1, W2t, row0, x0, x, nullptr, nullptr, lse, nullptr, nullptr,
-                      nullptr, part, accp};
+                      nullptr, part, accp, bvec};
     parts = launch_residual_wide_r<true>(a, r, rows, s);
   } else {
     parts = ceil_div(V, kChunk);
     hipLaunchKernelGGL(verify_acceptance_f32, dim3(rows, parts), dim3(64), 0, s, R, gamma, V, r,
                        static_cast<const float*>(target), row0, static_cast<const float*>(U),
-                       static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, part, accp);
+                       static_cast<const float*>(W1), static_cast<const float*>(W2t), x0, x, lse, part, accp,
+                       static_cast<const float*>(bvec));
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(acceptance_finish, dim3(ceil_div(rows, 256)), dim3(256), 0, s, rows, parts, accp, c_star);

@@ -134,8 +134,9 @@ def test_verify_greedy_rejects_bad_arguments(lib):
 
 def test_acceptance_rejects_bad_arguments(lib):
     def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
-        args = [ptr] * 8
-        return lib.dspark_acceptance(dt, R, gamma, V, r, args[0], None, *args[1:], ws, ws_bytes, None)
+        a = [ptr] * 8
+        return lib.dspark_acceptance(dt, R, gamma, V, r, a[0], None, a[1], a[2], a[3], None, *a[4:], ws, ws_bytes,
+                                     None)
     assert call(dt=5) == EDTYPE
     assert call(V=0) == EINVAL
     assert call(r=48) == EDTYPE
@@ -164,6 +165,18 @@ def test_sts_fit_rejects_bad_arguments(lib):
     assert call(G=257) == EINVAL
     assert call(M=33) == EINVAL
     assert call(gamma=65) == EINVAL
+    assert call(ptr=None) == EINVAL
+    assert call(ws_bytes=8) == EWORKSPACE
+
+
+def test_verify_ex_rejects_bad_arguments(lib):
+    def call(dt=1, R=2, gamma=3, V=500, r=64, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        a = [ptr] * 13
+        return lib.dspark_verify_ex(dt, R, gamma, V, r, a[0], None, a[1], a[2], a[3], ptr, *a[4:], ws, ws_bytes,
+                                    None)
+    assert call(dt=5) == EDTYPE
+    assert call(V=0) == EINVAL
+    assert call(r=48) == EDTYPE
     assert call(ptr=None) == EINVAL
     assert call(ws_bytes=8) == EWORKSPACE
 

@@ -140,3 +140,75 @@ def test_rnn_reduces_to_markov_bit_for_bit(name, dev):
     assert torch.equal(x, xm.cpu()) and torch.equal(lse, lsem.cpu()) and torch.equal(logit, logitm.cpu())
     prev = np.concatenate([inp.x0[:, None], x.numpy()[:, :-1]], axis=1)
     assert np.array_equal(o.float().numpy(), E[prev])
+
+
+ACC_TIE = 1e-5
+CDF_TOL = 1e-4
+
+
+@pytest.mark.parametrize("w", [CASES[0], CASES[2], CASES[3], CASES[4]], ids=lambda w: w.name)
+def test_verify_with_rnn_bias_vectors(w, dev):
+    """An RNN-head draft verified with its own bias vectors (dspark_verify_ex)
+    against the oracle's verifier given the same vectors: accepted lengths
+    exact except near-ties, next tokens inside the CDF interval of u_res."""
+    from semi_ar_draft_round_amd import binding as B
+    from oracle import verify as OV
+    say(f"[rnn verify] {w.name}")
+    inp = W.make_inputs(w)
+    Wrnn = W.make_rnn_weights(w)
+    d, W1, got = _run(inp, Wrnn, dev)
+    x, lse, logit, s, o = got
+    rng = np.random.default_rng(w.seed)
+    ell = rng.integers(0, w.gamma + 1, size=w.R).astype(np.int32)
+    n_acc, next_tok = B.dspark_verify(d.target, d.U, W1, d.W2t, d.x0, x.to(dev), lse.to(dev), logit.to(dev),
+                                      torch.tensor(ell, device=dev), d.u_acc, d.u_res, bvec=o.to(dev))
+    c_star = B.dspark_acceptance(d.target, d.U, W1, d.W2t, d.x0, x.to(dev), lse.to(dev), bvec=o.to(dev))
+    torch.cuda.synchronize()
+    dt = w.dtype
+    tgt, U = as_f64(inp.target, dt), as_f64(inp.U, dt)
+    E, W2t = as_f64(inp.E, dt), as_f64(inp.W2t, dt)
+    bv = (o.float().numpy() if dt == "bf16" else o.numpy()).astype(np.float64)
+    xs = x.numpy().astype(np.int64)
+    logr = OV.accept_log_ratios(tgt, None, U, E, W2t, inp.x0.astype(np.int64), xs, ell, bvec=bv)
+    ng_all = n_acc.cpu().numpy()
+    nt_all = next_tok.cpu().numpy()
+    for i in range(w.R):
+        lr = logr[i]
+        lu = np.log(inp.u_acc[i, :len(lr)].astype(np.float64))
+        ng = int(ng_all[i])
+        assert 0 <= ng <= ell[i]
+        for p in range(min(ng + 1, len(lr))):
+            if bool(lu[p] < lr[p]) != (p < ng):
+                assert abs(lu[p] - lr[p]) <= ACC_TIE, (i, p)
+        res = OV.residual(tgt, None, U, E, W2t, inp.x0.astype(np.int64), xs, i, ng, int(ell[i]), bvec=bv)
+        tok = int(nt_all[i])
+        if tok != OV.inverse_cdf(res, float(inp.u_res[i])):
+            lo, hi = OV.cdf_interval(res, tok)
+            assert lo - CDF_TOL <= float(inp.u_res[i]) <= hi + CDF_TOL, (i, tok)
+    ref = OV.analytic_acceptance(tgt, None, U, E, W2t, inp.x0.astype(np.int64), xs,
+                                 lse.numpy().astype(np.float64), bvec=bv)
+    assert np.abs(c_star.cpu().numpy() - ref).max() <= 1e-5
+
+
+def test_verify_ex_with_w1_rows_is_verify(dev):
+    """Bias vectors that are exactly the previous tokens' W1 rows (the
+    reduction weights) make dspark_verify_ex reproduce dspark_verify bit for
+    bit, and likewise the analytic acceptance."""
+    from semi_ar_draft_round_amd import binding as B
+    w = next(c for c in CASES if c.name == "rnn_r70_g6_v4100_r64")
+    inp = W.make_inputs(w)
+    rng = np.random.default_rng(7)
+    E = np.where(rng.random((w.V, w.r)) < 0.5, -0.5, 0.5).astype(np.float32)
+    Wr = np.zeros((3 * w.r, 2 * w.r + w.d), dtype=np.float32)
+    Wr[2 * w.r:, w.r:2 * w.r] = np.eye(w.r) * 1.1015625
+    d, W1, got = _run(inp, W.bf16_bits(Wr), dev, E=W.bf16_bits(E))
+    x, lse, logit, s, o = [t.to(dev) for t in got]
+    ell = torch.tensor(rng.integers(0, w.gamma + 1, size=w.R).astype(np.int32), device=dev)
+    a = B.dspark_verify(d.target, d.U, W1, d.W2t, d.x0, x, lse, logit, ell, d.u_acc, d.u_res)
+    a = [t.clone() for t in a]
+    b = B.dspark_verify(d.target, d.U, W1, d.W2t, d.x0, x, lse, logit, ell, d.u_acc, d.u_res, bvec=o)
+    ca = B.dspark_acceptance(d.target, d.U, W1, d.W2t, d.x0, x, lse).clone()
+    cb = B.dspark_acceptance(d.target, d.U, W1, d.W2t, d.x0, x, lse, bvec=o)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.equal(ca, cb)

@@ -113,3 +113,25 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(RN.round_storage(x, "bf16"), ref)
     np.testing.assert_array_equal(RN.round_storage(cases, "bf16"),
                                   torch.from_numpy(cases.astype(np.float32)).to(torch.bfloat16).double().numpy())
+
+
+def test_verify_with_bias_vectors_matches_the_markov_rows():
+    """The verifier's p_d from explicit bias vectors equals the Markov head's
+    when the vectors are the W1 rows of the previous tokens."""
+    from oracle import verify as Vf
+    rng = np.random.default_rng(8)
+    R, gamma, V, r = 4, 5, 60, 8
+    U = rng.normal(0, 2.0, size=(R, gamma, V))
+    E = rng.normal(0, 0.5, size=(V, r))
+    W2t = rng.normal(0, 0.4, size=(V, r))
+    x0 = rng.integers(0, V, size=R)
+    x = rng.integers(0, V, size=(R, gamma))
+    target = rng.normal(0, 2.0, size=(R, gamma + 1, V))
+    ell = rng.integers(0, gamma + 1, size=R)
+    u_acc, u_res = rng.random((R, gamma)), rng.random(R)
+    bvec = E[np.concatenate([x0[:, None], x[:, :-1]], axis=1)]
+    a = Vf.verify(target, None, U, E, W2t, x0, x, ell, u_acc, u_res)
+    b = Vf.verify(target, None, U, E, W2t, x0, x, ell, u_acc, u_res, bvec=bvec)
+    assert a["n_acc"].tolist() == b["n_acc"].tolist() and a["next_tok"].tolist() == b["next_tok"].tolist()
+    np.testing.assert_allclose(Vf.analytic_acceptance(target, None, U, E, W2t, x0, x, bvec=bvec),
+                               Vf.analytic_acceptance(target, None, U, E, W2t, x0, x), atol=1e-12)
