@@ -7,7 +7,9 @@
 // One wave per (request, position): a dot product of length d over the
 // hidden state plus one of length r over the previous token's W1 row, both
 // with 16-byte loads and fp32 accumulation, then a wave reduction.  The
-// kernel streams h once, so it is bound by HBM bandwidth.
+// kernel streams h once, so it is bound by HBM bandwidth: a lane issues the
+// loads of up to kConfBatch pieces of the row (and of w) before it uses any,
+// so a row costs one round trip to memory rather than one per piece.
 #include "common.hpp"
 
 namespace dspark {
@@ -35,6 +37,10 @@ struct Vec16<BF16> {
     }
   }
 };
+
+// Sixteen-byte pieces per lane whose loads are in flight together (a bf16
+// row of up to 8192 elements in one batch).
+constexpr int kConfBatch = 16;
 
 template <typename Elt>
 __device__ __forceinline__ float dot_stride(const typename Elt::T* a, const typename Elt::T* b, int n,
@@ -65,8 +71,32 @@ __global__ __launch_bounds__(256) void confidence_kernel(int R, int gamma, int d
   if (row >= static_cast<int64_t>(R) * gamma) return;
   const int req = static_cast<int>(row / gamma);
   const int k = static_cast<int>(row % gamma);
-  const int prev = token_or_none((k == 0) ? x0[req] : x[row - 1], V);
-  float acc = dot_stride<Elt>(h + row * d, w, d, lane);
+  const int prev_raw = (k == 0) ? x0[req] : x[row - 1];
+  constexpr int N = Vec16<Elt>::N;
+  const typename Elt::T* hrow = h + row * d;
+  float acc = 0.f;
+  for (int i0 = lane * N; i0 < d; i0 += 64 * N * kConfBatch) {
+    uint4 hv[kConfBatch], wv[kConfBatch];
+#pragma unroll
+    for (int b = 0; b < kConfBatch; ++b) {
+      const int i = i0 + b * 64 * N;
+      if (i < d) {
+        hv[b] = *reinterpret_cast<const uint4*>(hrow + i);
+        wv[b] = *reinterpret_cast<const uint4*>(w + i);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kConfBatch; ++b) {
+      if (i0 + b * 64 * N < d) {
+        float va[N], vb[N];
+        Vec16<Elt>::load(reinterpret_cast<const typename Elt::T*>(&hv[b]), va);
+        Vec16<Elt>::load(reinterpret_cast<const typename Elt::T*>(&wv[b]), vb);
+#pragma unroll
+        for (int t = 0; t < N; ++t) acc = fmaf(va[t], vb[t], acc);
+      }
+    }
+  }
+  const int prev = token_or_none(prev_raw, V);
   if (prev >= 0) acc += dot_stride<Elt>(W1 + static_cast<int64_t>(prev) * r, w + d, r, lane);
   const float zz = wave_reduce_sum(acc);
   if (lane == 0) {
