@@ -9,10 +9,10 @@
 // Four launches:
 //   verify_target_part  the needed target rows (rows 0..l_r of request r),
 //                       each split into parts along the vocabulary: (max,
-//                       sum) parts of the log-normaliser, and the target
-//                       logit of the drafted token on rows below l_r;
+//                       sum) parts of the log-normaliser;
 //   verify_accept       one wave per request: the parts merged into each
-//                       row's log-normaliser, then the first i with
+//                       row's log-normaliser, the target logit of each
+//                       drafted token gathered, then the first i with
 //                       ln u_acc >= ln p_t(x_i) - ln p_d(x_i) -> n_acc;
 //   verify_residual_*   the residual row of every request in one pass over
 //                       the vocabulary: p_d is rebuilt from U and the Markov
@@ -70,15 +70,16 @@ __device__ __forceinline__ Lse block_reduce_lse(Lse a, Lse* sh) {
 // prefix of the needed-row counts (for up to kLseCompactR requests) and
 // deals the needed (row, part) items out evenly: item a goes to work group
 // a mod gridDim.  Larger batches walk every (row, part) item and skip the
-// unneeded ones.  Each thread keeps kLseUnroll 16-byte loads in flight; part
-// 0 of a draft row also fetches the target logit of the drafted token.
+// unneeded ones.  Each thread keeps kLseUnroll 16-byte loads in flight, and
+// every item costs the same (the drafted tokens' target logits are gathered
+// by verify_accept, so no item waits on a dependent load).
 constexpr int kLseSplits = 8;
 constexpr int kLseThreads = 256;
 constexpr int kLseUnroll = 8;
 constexpr int kLseCompactR = 4096;
 
 // What a target-row part records, and which rows are needed:
-//   kPartLse     (max, sum exp) of rows 0..l_r, and the draft's target logit
+//   kPartLse     (max, sum exp) of rows 0..l_r
 //   kPartArgmax  (largest logit, its lowest index) of rows 0..l_r (greedy)
 //   kPartLseAll  (max, sum exp) of rows 0..gamma-1 of every request (the
 //                analytic acceptance; ell is not read)
@@ -109,10 +110,10 @@ __device__ __forceinline__ ArgMax block_reduce_argmax(ArgMax a, ArgMax* sh) {
 }
 
 template <typename Elt, int MODE>
-__device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, int gamma, int V, int span,
+__device__ __forceinline__ void target_part_item(int r, int i, int sp, int gamma, int V, int span,
                                                  const typename Elt::T* __restrict__ target,
-                                                 const int32_t* __restrict__ row0, const int32_t* __restrict__ x,
-                                                 float2* __restrict__ part, float* __restrict__ tx, Lse* sh) {
+                                                 const int32_t* __restrict__ row0, float2* __restrict__ part,
+                                                 Lse* sh) {
   constexpr int N = RowVec<Elt>::N;
   const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + i;
   const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + i : ri;
@@ -177,13 +178,7 @@ __device__ __forceinline__ void target_part_item(int r, int i, int sp, int L, in
       acc = lse_combine(acc, Lse{Elt::load(t, v), 1.f});
   }
   acc = block_reduce_lse(acc, sh);
-  if (threadIdx.x == 0) {
-    part[ri * kLseSplits + sp] = make_float2(acc.M, acc.S);
-    if (MODE == kPartLse && sp == 0 && i < L) {
-      const int xi = token_or_none(x[static_cast<int64_t>(r) * gamma + i], V);
-      tx[static_cast<int64_t>(r) * gamma + i] = xi < 0 ? neg_inf() : Elt::load(t, xi);
-    }
-  }
+  if (threadIdx.x == 0) part[ri * kLseSplits + sp] = make_float2(acc.M, acc.S);
   __syncthreads();   // sh is reused by the next item
 }
 
@@ -191,9 +186,8 @@ template <typename Elt, int MODE>
 __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gamma, int V,
                                                                   const typename Elt::T* __restrict__ target,
                                                                   const int32_t* __restrict__ row0,
-                                                                  const int32_t* __restrict__ x,
                                                                   const int32_t* __restrict__ ell,
-                                                                  float2* __restrict__ part, float* __restrict__ tx) {
+                                                                  float2* __restrict__ part) {
   __shared__ Lse sh[kLseThreads / kWave];
   __shared__ int pref[kLseCompactR + 1];   // pref[r] = needed rows of requests < r
   constexpr int N = RowVec<Elt>::N;
@@ -238,8 +232,7 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
         else
           hi = mid - 1;
       }
-      const int L = needed_rows<MODE>(ell, lo, gamma) - 1;
-      target_part_item<Elt, MODE>(lo, act - pref[lo], sp, L, gamma, V, span, target, row0, x, part, tx, sh);
+      target_part_item<Elt, MODE>(lo, act - pref[lo], sp, gamma, V, span, target, row0, part, sh);
     }
   } else {
     const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
@@ -250,7 +243,7 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
       const int i = static_cast<int>(ri % (gamma + 1));
       const int L = needed_rows<MODE>(ell, r, gamma) - 1;
       if (i > L) continue;   // uniform across the work group
-      target_part_item<Elt, MODE>(r, i, sp, L, gamma, V, span, target, row0, x, part, tx, sh);
+      target_part_item<Elt, MODE>(r, i, sp, gamma, V, span, target, row0, part, sh);
     }
   }
 }
@@ -258,11 +251,16 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
 // ------------------------------------------------------------------- accept
 
 // One wave per request: lane i merges the parts of target row i into its
-// log-normaliser (rows 0..l_r), evaluates the accept test of draft i, and the
-// first failing draft, found by a ballot, ends the accepted prefix.
-__global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int32_t* __restrict__ ell,
+// log-normaliser (rows 0..l_r), gathers the target logit of draft i (its
+// token is read before l_r is known, so the two loads overlap the part
+// loads), evaluates the accept test of draft i, and the first failing draft,
+// found by a ballot, ends the accepted prefix.
+template <typename Elt>
+__global__ __launch_bounds__(256) void verify_accept(int R, int gamma, int V, const typename Elt::T* __restrict__ target,
+                                                     const int32_t* __restrict__ row0,
+                                                     const int32_t* __restrict__ x,
+                                                     const int32_t* __restrict__ ell,
                                                      const float2* __restrict__ part,
-                                                     const float* __restrict__ tx,
                                                      const float* __restrict__ logit,
                                                      const float* __restrict__ lse,
                                                      const float* __restrict__ u_acc,
@@ -270,12 +268,20 @@ __global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int
   const int r = blockIdx.x * 4 + static_cast<int>(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= R) return;
+  const int64_t rbase = row0 ? static_cast<int64_t>(row0[r]) : static_cast<int64_t>(r) * (gamma + 1);
+  // draft i = lane (a draft row below l_r <= gamma <= 64 is always in the first pass)
+  const int xr = lane < gamma ? x[static_cast<int64_t>(r) * gamma + lane] : -1;
   const int L = min(max(ell[r], 0), gamma);
   int first_fail = L;
   for (int i0 = 0; i0 <= L; i0 += kWave) {   // gamma <= 64: at most two passes
     const int i = i0 + lane;
     bool fail = false;
     if (i <= L) {
+      float txv = neg_inf();
+      if (i < L) {
+        const int xi = token_or_none(xr, V);
+        if (xi >= 0) txv = Elt::load(target + (rbase + i) * V, xi);
+      }
       const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + i;
       Lse acc{neg_inf(), 0.f};
 #pragma unroll
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256) void verify_accept(int R, int gamma, const int
       lse_t[ri] = lt;
       if (i < L) {
         const int64_t o = static_cast<int64_t>(r) * gamma + i;
-        const float log_ratio = (tx[o] - lt) - (logit[o] - lse[o]);
+        const float log_ratio = (txv - lt) - (logit[o] - lse[o]);
         fail = !(logf(u_acc[o]) < log_ratio);
       }
     }
@@ -789,7 +795,6 @@ __global__ __launch_bounds__(256) void verify_select(
 struct VerifyWs {
   float* lse_t;   // [R][gamma+1]
   float2* part;   // [R][gamma+1][kLseSplits] (max, sum) parts of the target log-normalisers
-  float* tx;      // [R][gamma]
   float* csum;    // [R][mass_stride(V)] residual mass of each 16-token chunk
   float* psum;    // [R][mass_stride(V)] p_t mass of each 16-token chunk
 };
@@ -799,7 +804,7 @@ static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 size_t verify_workspace_bytes(int R, int gamma, int V) {
   const size_t nC = static_cast<size_t>(mass_stride(V));
   return align256(sizeof(float) * R * (gamma + 1)) + align256(sizeof(float2) * R * (gamma + 1) * kLseSplits) +
-         align256(sizeof(float) * R * gamma) + 2 * align256(sizeof(float) * R * nC);
+         2 * align256(sizeof(float) * R * nC);
 }
 
 static VerifyWs carve(void* ws, int R, int gamma, int V) {
@@ -810,8 +815,6 @@ static VerifyWs carve(void* ws, int R, int gamma, int V) {
   p += align256(sizeof(float) * R * (gamma + 1));
   w.part = reinterpret_cast<float2*>(p);
   p += align256(sizeof(float2) * R * (gamma + 1) * kLseSplits);
-  w.tx = reinterpret_cast<float*>(p);
-  p += align256(sizeof(float) * R * gamma);
   w.csum = reinterpret_cast<float*>(p);
   p += align256(sizeof(float) * R * nC);
   w.psum = reinterpret_cast<float*>(p);
@@ -880,15 +883,19 @@ hipError_t verify_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   hipError_t err;
   const int64_t items = static_cast<int64_t>(R) * (gamma + 1) * kLseSplits;
   const int gridp = static_cast<int>(items < 4LL * compute_units() ? items : 4LL * compute_units());
-  if (dt == DSPARK_BF16)
+  if (dt == DSPARK_BF16) {
     hipLaunchKernelGGL((verify_target_part<BF16, kPartLse>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
-                       static_cast<const uint16_t*>(target), row0, x, ell, w.part, w.tx);
-  else
+                       static_cast<const uint16_t*>(target), row0, ell, w.part);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(verify_accept<BF16>, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, x, ell, w.part, logit, lse, u_acc, w.lse_t, n_acc);
+  } else {
     hipLaunchKernelGGL((verify_target_part<F32, kPartLse>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
-                       static_cast<const float*>(target), row0, x, ell, w.part, w.tx);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(verify_accept, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, ell, w.part, w.tx, logit, lse,
-                     u_acc, w.lse_t, n_acc);
+                       static_cast<const float*>(target), row0, ell, w.part);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(verify_accept<F32>, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, V,
+                       static_cast<const float*>(target), row0, x, ell, w.part, logit, lse, u_acc, w.lse_t, n_acc);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (dt == DSPARK_BF16) {
     const SweepArgs a{R, gamma, V, target, U, W1, W2t, row0, x0, x, ell, n_acc, lse, w.lse_t, w.csum, w.psum,
@@ -937,10 +944,10 @@ hipError_t verify_greedy_launch(dspark_dtype dt, int R, int gamma, int V, const 
   const int gridp = part_grid(R, gamma);
   if (dt == DSPARK_BF16)
     hipLaunchKernelGGL((verify_target_part<BF16, kPartArgmax>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
-                       static_cast<const uint16_t*>(target), row0, x, ell, part, nullptr);
+                       static_cast<const uint16_t*>(target), row0, ell, part);
   else
     hipLaunchKernelGGL((verify_target_part<F32, kPartArgmax>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma, V,
-                       static_cast<const float*>(target), row0, x, ell, part, nullptr);
+                       static_cast<const float*>(target), row0, ell, part);
   hipError_t err;
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(verify_greedy_accept, dim3(ceil_div(R, 4)), dim3(256), 0, s, R, gamma, ell, x, part, n_acc,
@@ -958,10 +965,10 @@ hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, co
   const int gridp = part_grid(R, gamma);
   if (dt == DSPARK_BF16)
     hipLaunchKernelGGL((verify_target_part<BF16, kPartLseAll>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma,
-                       V, static_cast<const uint16_t*>(target), row0, nullptr, nullptr, part, nullptr);
+                       V, static_cast<const uint16_t*>(target), row0, nullptr, part);
   else
     hipLaunchKernelGGL((verify_target_part<F32, kPartLseAll>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma,
-                       V, static_cast<const float*>(target), row0, nullptr, nullptr, part, nullptr);
+                       V, static_cast<const float*>(target), row0, nullptr, part);
   hipError_t err;
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int rows = R * gamma;
