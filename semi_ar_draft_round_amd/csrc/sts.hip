@@ -11,11 +11,18 @@
 // fixed point (units of 2^-32, int64) into LDS bins, then into global ones
 // -- integer sums, so the result does not depend on the order of addition;
 // sts_select turns the sums into ECEs and takes the first minimum; sts_update
-// advances both chains; sts_auc counts, over every (accepted, rejected)
-// pair of rollouts that reached the position, 2 for a higher logit of the
-// accepted one and 1 for a tie (exact 64-bit integer counts).  The AUC is
-// taken on the logits: the sigmoid is strictly increasing, so the order is
-// the same, without the ties that rounding the sigmoid to fp32 would add.
+// advances both chains.
+//
+// The AUC of position k counts, over every (accepted, rejected) pair of
+// rollouts that reached k, 2 for a higher logit of the accepted one and 1 for
+// a tie (exact 64-bit integer counts).  It is taken on the logits: the
+// sigmoid is strictly increasing, so the order is the same, without the ties
+// that rounding the sigmoid to fp32 would add.  A rollout is rejected at
+// exactly one position (k = n_acc), so the rejected logits of all positions
+// form one set of at most N keys (k, logit); sts_auc_sort sorts it in chunks
+// and sts_auc_count ranks every accepted logit in each chunk's segment for
+// its position (2 below + equal = lower bound + upper bound): O(N log N)
+// work per call instead of one test per pair.
 #include "common.hpp"
 
 namespace dspark {
@@ -31,6 +38,8 @@ struct StsWs {
   long long* bins;          // [(G + 1) * M] sums of y - p, 2^-32 units; row G is the raw chain
   int* best;                // [1] index of the chosen temperature
   unsigned long long* pairs;  // [gamma][3]: 2 * (wins) + ties, accepted count, rejected count
+  unsigned long long* sorted; // [ceil(N / kAucChunk) * kAucChunk] chunk-sorted rejected keys
+  int* seg;                   // [ceil(N / kAucChunk)][gamma + 1] segment starts
 };
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + expf(-x)); }
@@ -130,59 +139,184 @@ __global__ __launch_bounds__(kStsThreads) void sts_update(int N, int gamma, int 
   a_raw[n] = a_raw[n] * sigmoid_f32(x);
 }
 
-// Pair counts for the AUC of position k.  Thread = one rollout i of
-// blockIdx.x's range (counted when accepted at k); blockIdx.y takes one
-// chunk of the rollouts j, staged through LDS a tile at a time with the
-// logit of a rollout that was not rejected at k replaced by NaN (it then
-// compares false both ways).  Both must have reached k (n_acc >= k, 0-based).
-constexpr int kStsAucChunks = 8;
+// ------------------------------------------------------------------ AUC
 
-__global__ __launch_bounds__(kStsThreads) void sts_auc(int N, int gamma, int k, const float* __restrict__ z,
-                                                       const int32_t* __restrict__ n_acc,
-                                                       unsigned long long* __restrict__ pairs) {
-  __shared__ __attribute__((aligned(16))) float sz[kStsThreads];
-  __shared__ unsigned long long red[kStsThreads / kWave][3];
-  const int i = blockIdx.x * kStsThreads + threadIdx.x;
-  const bool pos = i < N && n_acc[i] >= k + 1;
-  const float zi = i < N ? z[static_cast<int64_t>(i) * gamma + k] : 0.f;
-  const int per = ceil_div(ceil_div(N, kStsThreads), kStsAucChunks) * kStsThreads;
-  const int j_lo = blockIdx.y * per, j_hi = min(N, j_lo + per);
-  unsigned long long cnt = 0, negs = 0;
-  for (int j0 = j_lo; j0 < j_hi; j0 += kStsThreads) {
-    const int j = j0 + threadIdx.x;
-    const bool neg = j < j_hi && n_acc[j] == k;
-    sz[threadIdx.x] = neg ? z[static_cast<int64_t>(j) * gamma + k] : __builtin_nanf("");
-    negs += (blockIdx.x == 0 && neg) ? 1ull : 0ull;
-    __syncthreads();
-    if (pos) {
-      unsigned int c = 0;
-      const float4* s4 = reinterpret_cast<const float4*>(sz);
-#pragma unroll 4
-      for (int q = 0; q < kStsThreads / 4; ++q) {
-        const float4 v = s4[q];
-        c += (zi > v.x ? 2u : 0u) + (zi == v.x ? 1u : 0u);
-        c += (zi > v.y ? 2u : 0u) + (zi == v.y ? 1u : 0u);
-        c += (zi > v.z ? 2u : 0u) + (zi == v.z ? 1u : 0u);
-        c += (zi > v.w ? 2u : 0u) + (zi == v.w ? 1u : 0u);
-      }
-      cnt += c;
-    }
-    __syncthreads();
-  }
-  // the block's totals: pair count, accepted rollouts (first chunk only),
-  // rejected rollouts (first block column only)
-  unsigned long long v[3] = {cnt, (pos && blockIdx.y == 0) ? 1ull : 0ull, negs};
+constexpr int kAucThreads = 1024;
+constexpr int kAucE = 8;                               // keys per thread in the chunk sort
+constexpr int kAucChunk = kAucThreads * kAucE;         // rollouts per sorted chunk (8192)
+constexpr int kAucQuery = 2048;                        // rollouts ranked per counting work group
+
+// The logit's order-preserving unsigned image (-0 taken as +0, so the two
+// compare equal as floats do); NaN never reaches it.
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  const uint32_t u = __float_as_uint(x == 0.f ? 0.f : x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Ascending bitonic sort of keys[0 .. n_pad) in LDS by kAucThreads threads
+// (n_pad = kAucThreads E).  Lane l of wave w holds elements w 64 E + l E +
+// (0 .. E-1): a partner less than E away is in the same lane, one less than
+// 64 E away in the same wave (a shuffle), any other in another wave (through
+// keys[] and keys[n_pad ..], alternating, one barrier per such stage).
+template <int E>
+__device__ void auc_bitonic(unsigned long long* keys) {
+  constexpr int n_pad = kAucThreads * E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int base = (threadIdx.x / kWave) * kWave * E + lane * E;
+  const auto cx = [](unsigned long long a, unsigned long long o, int i, int j, int k) {
+    const bool asc = (i & k) == 0, lower = (i & j) == 0;
+    return (lower == asc) ? (a < o ? a : o) : (a < o ? o : a);
+  };
+  unsigned long long v[E];
 #pragma unroll
-  for (int e = 0; e < 3; ++e)
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v[e] += __shfl_xor(v[e], o);
-  if ((threadIdx.x & 63) == 0)
-    for (int e = 0; e < 3; ++e) red[threadIdx.x >> 6][e] = v[e];
+  for (int e = 0; e < E; ++e) v[e] = keys[base + e];
   __syncthreads();
-  if (threadIdx.x < 3) {
-    unsigned long long t = 0;
-    for (int w = 0; w < kStsThreads / kWave; ++w) t += red[w][threadIdx.x];
-    if (t) atomicAdd(pairs + 3 * k + threadIdx.x, t);
+  int buf = 0;
+  for (int k = 2; k <= n_pad; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kWave * E) {
+        unsigned long long* b = keys + buf * n_pad;
+#pragma unroll
+        for (int e = 0; e < E; ++e) b[base + e] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = cx(v[e], b[(base + e) ^ j], base + e, j, k);
+        buf ^= 1;
+      } else if (j >= E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = cx(v[e], __shfl_xor(v[e], j / E), base + e, j, k);
+      } else {
+        unsigned long long w[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          unsigned long long o = v[e ^ 1];
+          if constexpr (E > 2) {
+            if (j == 2) o = v[e ^ 2];
+          }
+          if constexpr (E > 4) {
+            if (j == 4) o = v[e ^ 4];
+          }
+          w[e] = cx(v[e], o, base + e, j, k);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = w[e];
+      }
+    }
+  }
+  __syncthreads();   // the last LDS stage's reads are done
+#pragma unroll
+  for (int e = 0; e < E; ++e) keys[base + e] = v[e];
+  __syncthreads();
+}
+
+// First index in s[lo, hi) whose key is not below (UPPER: not at or below) key.
+template <bool UPPER>
+__device__ __forceinline__ int auc_bound(const unsigned long long* s, int lo, int hi, unsigned long long key) {
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const bool left = UPPER ? s[mid] <= key : s[mid] < key;
+    if (left)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Chunk c of the rollouts: the rejected logit of each rollout, as the key
+// (k << 32) | logit_key (k = n_acc < gamma; rollouts accepted everywhere, or
+// with a NaN logit, which compares false both ways, get ~0 and sort last),
+// sorted; seg[c][k] = the first sorted index of position k (k = 0..gamma).
+__global__ __launch_bounds__(kAucThreads) void sts_auc_sort(int N, int gamma, const float* __restrict__ z,
+                                                           const int32_t* __restrict__ n_acc,
+                                                           unsigned long long* __restrict__ sorted,
+                                                           int* __restrict__ seg) {
+  __shared__ unsigned long long sk[2 * kAucChunk];
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kAucChunk;
+  for (int i = threadIdx.x; i < kAucChunk; i += kAucThreads) {
+    const int64_t n = n0 + i;
+    unsigned long long key = ~0ull;
+    if (n < N) {
+      const int a = n_acc[n];
+      if (a >= 0 && a < gamma) {
+        const float x = z[n * gamma + a];
+        if (x == x) key = (static_cast<unsigned long long>(a) << 32) | logit_key(x);
+      }
+    }
+    sk[i] = key;
+  }
+  __syncthreads();
+  auc_bitonic<kAucE>(sk);
+  for (int i = threadIdx.x; i < kAucChunk; i += kAucThreads) sorted[n0 + i] = sk[i];
+  if (static_cast<int>(threadIdx.x) <= gamma)
+    seg[static_cast<int64_t>(blockIdx.x) * (gamma + 1) + threadIdx.x] =
+        auc_bound<false>(sk, 0, kAucChunk, static_cast<unsigned long long>(threadIdx.x) << 32);
+}
+
+// Work group (q, c): sorted chunk c in LDS, ranked against by the rollouts
+// q kAucQuery .. + kAucQuery - 1.  For every position k, each rollout
+// accepted at k (n_acc >= k + 1) with a logit that is not NaN adds lower +
+// upper bound of its key in chunk c's segment for k; the work group's sums
+// go to pairs[3k] once per wave.  The column c = 0 also counts the accepted
+// (pairs[3k + 1]) and rejected (pairs[3k + 2]) rollouts, NaN logits
+// included.
+__global__ __launch_bounds__(kAucThreads) void sts_auc_count(int N, int gamma, const float* __restrict__ z,
+                                                            const int32_t* __restrict__ n_acc,
+                                                            const unsigned long long* __restrict__ sorted,
+                                                            const int* __restrict__ seg,
+                                                            unsigned long long* __restrict__ pairs) {
+  __shared__ unsigned long long sk[kAucChunk];
+  __shared__ int sseg[65];
+  __shared__ unsigned long long acc[64][3];
+  const int c = blockIdx.y;
+  const int nk = seg[static_cast<int64_t>(c) * (gamma + 1) + gamma];   // keys of this chunk below ~0
+  for (int i = threadIdx.x; i < nk; i += kAucThreads) sk[i] = sorted[static_cast<int64_t>(c) * kAucChunk + i];
+  if (static_cast<int>(threadIdx.x) <= gamma) sseg[threadIdx.x] = seg[static_cast<int64_t>(c) * (gamma + 1) + threadIdx.x];
+  for (int i = threadIdx.x; i < 3 * 64; i += kAucThreads) (&acc[0][0])[i] = 0ull;
+  __syncthreads();
+  constexpr int kPerThread = kAucQuery / kAucThreads;
+  int a[kPerThread];
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * kAucQuery;
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int64_t n = q0 + u * kAucThreads + threadIdx.x;
+    a[u] = n < N ? n_acc[n] : -1;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int k = 0; k < gamma; ++k) {
+    unsigned long long cnt = 0;
+    const int lo = sseg[k], hi = sseg[k + 1];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      if (a[u] >= k + 1 && hi > lo) {
+        const float x = z[(q0 + u * kAucThreads + threadIdx.x) * gamma + k];
+        if (x == x) {
+          const unsigned long long key = (static_cast<unsigned long long>(k) << 32) | logit_key(x);
+          cnt += static_cast<unsigned long long>(auc_bound<false>(sk, lo, hi, key) - lo) +
+                 static_cast<unsigned long long>(auc_bound<true>(sk, lo, hi, key) - lo);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0 && cnt) atomicAdd(&acc[k][0], cnt);
+    if (c == 0) {
+      int np = 0, nn = 0;
+#pragma unroll
+      for (int u = 0; u < kPerThread; ++u) {
+        np += __popcll(__ballot(a[u] >= k + 1));
+        nn += __popcll(__ballot(a[u] == k));
+      }
+      if (lane == 0) {
+        if (np) atomicAdd(&acc[k][1], static_cast<unsigned long long>(np));
+        if (nn) atomicAdd(&acc[k][2], static_cast<unsigned long long>(nn));
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 3 * gamma; i += kAucThreads) {
+    const unsigned long long v = (&acc[0][0])[i];
+    if (v) atomicAdd(pairs + i, v);
   }
 }
 
@@ -197,9 +331,13 @@ __global__ __launch_bounds__(64) void sts_auc_finish(int gamma, const unsigned l
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
+static int auc_chunks(int N) { return ceil_div(N, kAucChunk); }
+
 size_t sts_workspace_bytes(int N, int gamma, int G, int M) {
   return 2 * align256(sizeof(float) * N) + align256(sizeof(long long) * (G + 1) * M) + align256(sizeof(int)) +
-         align256(sizeof(unsigned long long) * 3 * gamma);
+         align256(sizeof(unsigned long long) * 3 * gamma) +
+         align256(sizeof(unsigned long long) * static_cast<size_t>(auc_chunks(N)) * kAucChunk) +
+         align256(sizeof(int) * static_cast<size_t>(auc_chunks(N)) * (gamma + 1));
 }
 
 bool sts_shape_ok(int N, int gamma, int G, int M) {
@@ -220,12 +358,22 @@ hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, co
   w.best = reinterpret_cast<int*>(p);
   p += align256(sizeof(int));
   w.pairs = reinterpret_cast<unsigned long long*>(p);
+  p += align256(sizeof(unsigned long long) * 3 * gamma);
+  w.sorted = reinterpret_cast<unsigned long long*>(p);
+  p += align256(sizeof(unsigned long long) * static_cast<size_t>(auc_chunks(N)) * kAucChunk);
+  w.seg = reinterpret_cast<int*>(p);
   const int blocksN = ceil_div(N, kStsThreads);
   const int nbins = (G + 1) * M;
   hipLaunchKernelGGL(sts_init, dim3(ceil_div(N > 3 * gamma ? N : 3 * gamma, kStsThreads)), dim3(kStsThreads), 0, s, N,
                      gamma, w.a, w.a_raw, w.pairs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // the AUC needs only the logits and n_acc: both passes run once, up front
+  hipLaunchKernelGGL(sts_auc_sort, dim3(auc_chunks(N)), dim3(kAucThreads), 0, s, N, gamma, z, n_acc, w.sorted,
+                     w.seg);
+  hipLaunchKernelGGL(sts_auc_count, dim3(ceil_div(N, kAucQuery), auc_chunks(N)), dim3(kAucThreads), 0, s, N, gamma,
+                     z, n_acc, w.sorted, w.seg, w.pairs);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int blocksB = blocksN < 1024 ? blocksN : 1024;
   for (int k = 0; k < gamma; ++k) {
     hipLaunchKernelGGL(sts_clear, dim3(ceil_div(nbins, kStsThreads)), dim3(kStsThreads), 0, s, nbins, w.bins);
@@ -235,8 +383,6 @@ hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, co
                        ece_after);
     hipLaunchKernelGGL(sts_update, dim3(blocksN), dim3(kStsThreads), 0, s, N, gamma, k, z, grid, w.best, w.a,
                        w.a_raw);
-    hipLaunchKernelGGL(sts_auc, dim3(blocksN, kStsAucChunks), dim3(kStsThreads), 0, s, N, gamma, k, z, n_acc,
-                       w.pairs);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   hipLaunchKernelGGL(sts_auc_finish, dim3(1), dim3(64), 0, s, gamma, w.pairs, auc);

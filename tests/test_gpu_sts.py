@@ -88,3 +88,22 @@ def test_sts_position_never_reached(dev):
     ref = OS.sts_fit(z, n_acc, grid, 15, teacher_T=T)
     assert np.isnan(auc[1]) and np.isnan(auc[2]) and np.isnan(auc[0])   # no accepted draft anywhere
     assert np.all(np.abs(e1 - ref["ece_after"]) <= 2.5 / N + 1e-6)
+
+
+@pytest.mark.parametrize("N", [8192, 8193, 20000])
+def test_sts_auc_ties_and_signed_zeros(N, dev):
+    """Logits on a coarse grid (most pairs tie) with many exact -0.0 and
+    +0.0, at rollout counts on and just past a sort-chunk boundary: the AUC
+    is the oracle's pair count exactly (ties count one half, -0 equals +0)."""
+    gamma = 5
+    rng = np.random.default_rng(N)
+    z = (np.round(rng.normal(size=(N, gamma)) * 2) / 4).astype(np.float32)
+    zero = rng.random(size=(N, gamma)) < 0.2
+    z[zero] = np.where(rng.random(size=int(zero.sum())) < 0.5, np.float32(-0.0), np.float32(0.0))
+    n_acc = rng.integers(0, gamma + 1, size=N).astype(np.int32)
+    say(f"[sts ties] N={N} gamma={gamma}")
+    _, _, _, auc = _run(z, n_acc, W.sts_grid(), 15, dev)
+    for k in range(gamma):
+        reach = n_acc >= k
+        ref = OS.auc_pairs(z[reach, k], (n_acc >= k + 1)[reach])
+        assert abs(auc[k] - ref) <= 1e-12, (k, auc[k], ref)
