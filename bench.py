@@ -35,6 +35,7 @@ def source_hash() -> str:
     h = hashlib.sha256()
     for rel in ("semi_ar_draft_round_amd/csrc/sample.hip", "semi_ar_draft_round_amd/csrc/bias_tile.hpp",
                 "semi_ar_draft_round_amd/csrc/wide_tile.hpp", "semi_ar_draft_round_amd/csrc/common.hpp",
+                "semi_ar_draft_round_amd/csrc/sample_keys.hpp", "semi_ar_draft_round_amd/csrc/rnn_head.hpp",
                 "include/dspark.h"):
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(rel.encode() + fh.read())

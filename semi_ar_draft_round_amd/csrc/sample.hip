@@ -12,7 +12,7 @@
 // Gumbel-max (score LSE_c + G_c), keeping the best chunk's logits for the
 // in-chunk draw (argmax of l_v + g_{v mod 16}), which is made once at the end
 // of the sweep.  Each work group then merges its draw into the request's key
-// with one 64-bit atomic max (eight key slots per request spread the
+// with one 64-bit atomic max (four key slots per request spread the
 // contention) and stores its log-sum-exp partial.  The next position's
 // launch reads the keys back as its previous tokens.  sample_finalize decodes
 // x, merges the log-sum-exp partials and recomputes the logit of each
