@@ -25,7 +25,7 @@ Readings where the pages leave a choice:
     back to p_t of the same row;
   * temperature 1 on both sides.
 
-Two more modes (SURVEY's verify modes; reading notes, the FAQ on greedy,
+Two more modes (reading notes, the FAQ on greedy,
 temperature-0 decoding, and eq (8)-(8c) with the confidence-head paragraph):
   * greedy verification: acceptance becomes an exact-match test of the draft
     token against the target row's argmax; the prefix ends at the first
