@@ -350,7 +350,8 @@ __device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int rou
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      // no sleep between polls: the next load goes out as soon as this one
+      // returns (a sleep of one measured about 2 % slower per launch)
     }
     *flag = ok;
   }
@@ -681,16 +682,10 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   if (row >= static_cast<int64_t>(R) * gamma) return;
   const int req = static_cast<int>(row / gamma);
   const int k = static_cast<int>(row % gamma);
-  if (ws.bar[1] != 0u) {   // the persistent launch timed out at a grid barrier: no valid draw
-    if (lane == 0) {
-      x[row] = -1;
-      lse[row] = __builtin_nanf("");
-      logit[row] = __builtin_nanf("");
-    }
-    return;
-  }
+  // the time-out flag, the keys and the partials are loaded together; only
+  // the rows of the bias dot wait on the keys
+  const unsigned int timed_out = ws.bar[1];
   const int drawn = previous_token(ws.keys, x0, R, V, k + 1, req);
-  const int tok = drawn < 0 ? 0 : drawn;   // every position draws a token in [0, V)
   const int prev = bvec ? -1 : previous_token(ws.keys, x0, R, V, k, req);
   Lse run{neg_inf(), 0.f};
   const float2* lp = ws.lsep + (static_cast<int64_t>(k) * R + req) * nPart;
@@ -698,6 +693,15 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
     const float2 v = lp[p];
     run = lse_combine(run, Lse{v.x, v.y});
   }
+  if (timed_out != 0u) {   // the persistent launch timed out at a grid barrier: no valid draw
+    if (lane == 0) {
+      x[row] = -1;
+      lse[row] = __builtin_nanf("");
+      logit[row] = __builtin_nanf("");
+    }
+    return;
+  }
+  const int tok = drawn < 0 ? 0 : drawn;   // every position draws a token in [0, V)
   run = wave_reduce_lse(run);
   float b = 0.f;
   if (bvec || prev >= 0) {
