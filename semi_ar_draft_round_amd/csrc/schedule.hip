@@ -253,8 +253,18 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
     }
     tau_prev = tau;
   }
-  if (my_first_drop != 0x7FFFFFFF) atomicMin(&sh[0], my_first_drop);
-  if (my_count) atomicAdd(&sh[1], my_count);
+  // one LDS atomic per wave (the first drop and the candidate count reduced
+  // in the wave first)
+  int wave_drop = my_first_drop, wave_count = my_count;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    wave_drop = min(wave_drop, __shfl_xor(wave_drop, o));
+    wave_count += __shfl_xor(wave_count, o);
+  }
+  if ((tid & (kWave - 1)) == 0) {
+    if (wave_drop != 0x7FFFFFFF) atomicMin(&sh[0], wave_drop);
+    if (wave_count) atomicAdd(&sh[1], wave_count);
+  }
   if (mode == DSPARK_SCHED_WHOLE_WALK) {
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) {
