@@ -180,8 +180,10 @@ def dspark_confidence(h, w, W1, x0, x, T=None, c=None, z=None, want_z=True):
     return c, z
 
 
-def dspark_schedule(c, sps, ell=None, admitted=None, theta_best=None):
-    """ell [R] int32, admitted [1] int32, theta_best [1] float64 (Algorithm 1)."""
+def dspark_schedule(c, sps, ell=None, admitted=None, theta_best=None, ws=None):
+    """ell [R] int32, admitted [1] int32, theta_best [1] float64 (Algorithm 1).
+    ws: uint8 workspace of dspark_workspace_size(WS_SCHEDULE, R, gamma, 0) bytes
+    (a cached one when None)."""
     lib = load_library()
     R, gamma = c.shape
     dev = c.device
@@ -190,17 +192,18 @@ def dspark_schedule(c, sps, ell=None, admitted=None, theta_best=None):
     ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
     admitted = torch.empty(1, dtype=torch.int32, device=dev) if admitted is None else admitted
     theta_best = torch.empty(1, dtype=torch.float64, device=dev) if theta_best is None else theta_best
+    ws = workspace(WS_SCHEDULE, R, gamma, 0, 0, dev) if ws is None else ws
     st = lib.dspark_schedule(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), _ptr(ell), _ptr(admitted),
-                             _ptr(theta_best), None, 0, _stream())
+                             _ptr(theta_best), _ptr(ws), ws.numel(), _stream())
     _raise("dspark_schedule", st)
     return ell, admitted, theta_best
 
 
-def dspark_schedule_ex(c, sps, mode, cap=None, ell=None, admitted=None, theta_best=None):
+def dspark_schedule_ex(c, sps, mode, cap=None, ell=None, admitted=None, theta_best=None, ws=None):
     """The scheduler with an admission rule (SCHED_EARLY_STOP, SCHED_WHOLE_WALK
     or SCHED_CAPACITY; the last reads the capacity from the int32 [1] device
     tensor `cap`).  Returns ell [R] int32, admitted [1] int32, theta_best [1]
-    float64."""
+    float64.  ws as for dspark_schedule."""
     lib = load_library()
     R, gamma = c.shape
     dev = c.device
@@ -211,8 +214,9 @@ def dspark_schedule_ex(c, sps, mode, cap=None, ell=None, admitted=None, theta_be
     ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
     admitted = torch.empty(1, dtype=torch.int32, device=dev) if admitted is None else admitted
     theta_best = torch.empty(1, dtype=torch.float64, device=dev) if theta_best is None else theta_best
+    ws = workspace(WS_SCHEDULE, R, gamma, 0, 0, dev) if ws is None else ws
     st = lib.dspark_schedule_ex(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), int(mode), _ptr(cap), _ptr(ell),
-                                _ptr(admitted), _ptr(theta_best), None, 0, _stream())
+                                _ptr(admitted), _ptr(theta_best), _ptr(ws), ws.numel(), _stream())
     _raise("dspark_schedule_ex", st)
     return ell, admitted, theta_best
 

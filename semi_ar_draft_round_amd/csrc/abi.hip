@@ -26,9 +26,9 @@ hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, in
                              const void* w, const void* W1, const int32_t* x0, const int32_t* x,
                              const float* T, float* c, float* z, hipStream_t s);
 // schedule.hip
-size_t schedule_workspace_bytes();
+size_t schedule_workspace_bytes(int R, int gamma);
 hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
-                           int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s);
+                           int32_t* ell, int32_t* admitted, double* theta_best, void* ws, hipStream_t s);
 // verify.hip
 size_t verify_greedy_workspace_bytes(int R, int gamma);
 size_t acceptance_workspace_bytes(int R, int gamma, int V);
@@ -134,7 +134,8 @@ size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r
                  ? sample_workspace_bytes(DSPARK_F32, R, gamma, V)
                  : sample_workspace_bytes(DSPARK_BF16, R, gamma, V);
     case DSPARK_WS_SCHEDULE:
-      return schedule_workspace_bytes();
+      if (R < 1 || gamma < 1 || gamma > kMaxGamma || static_cast<int64_t>(R) * (1 + gamma) > kMaxSchedSlots) return 0;
+      return schedule_workspace_bytes(R, gamma);
     case DSPARK_WS_VERIFY:
       if (!draft_shape_ok(R, gamma, V)) return 0;
       return verify_workspace_bytes(R, gamma, V);
@@ -190,8 +191,6 @@ dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r,
 dspark_status dspark_schedule_ex(int R, int gamma, const float* c, const double* sps, int n_sps, int mode,
                                  const int32_t* cap, int32_t* ell, int32_t* admitted, double* theta_best,
                                  void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (R < 1 || gamma < 1 || gamma > kMaxGamma) return DSPARK_EINVAL;
   if (static_cast<int64_t>(R) * (1 + gamma) > kMaxSchedSlots) return DSPARK_EINVAL;
   if (n_sps < R * (1 + gamma)) return DSPARK_EINVAL;
@@ -199,9 +198,10 @@ dspark_status dspark_schedule_ex(int R, int gamma, const float* c, const double*
   if (mode != DSPARK_SCHED_EARLY_STOP && mode != DSPARK_SCHED_WHOLE_WALK && mode != DSPARK_SCHED_CAPACITY)
     return DSPARK_EINVAL;
   if (mode == DSPARK_SCHED_CAPACITY && !cap) return DSPARK_EINVAL;
+  if (!ws || ws_bytes < schedule_workspace_bytes(R, gamma)) return DSPARK_EWORKSPACE;
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
-  if (schedule_launch(R, gamma, c, sps, mode, cap, ell, admitted, theta_best, static_cast<hipStream_t>(stream)) !=
+  if (schedule_launch(R, gamma, c, sps, mode, cap, ell, admitted, theta_best, ws, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;

@@ -4,18 +4,21 @@
 // Algorithm 1 steps 1-6, Lemma 1 (prefix closure of the ranked pool) and the
 // causal early stop; caijizhuo summary, sections 三 and 四 (admit).
 //
-// One work group of 1024 threads, all data in LDS:
+// Two launches.  schedule_rank, many work groups:
 //   1. survival a_{r,j} as the fp64 left-to-right product of the fp32
 //      confidences, quantised to a_fx = floor(a * 2^50) (one thread per
-//      request);
+//      request; every work group computes all of them);
 //   2. ranking: each slot gets a 64-bit key ((2^50 - a_fx) << 13) | (r*gamma + j)
 //      so that ascending keys are descending a_fx, then ascending request,
 //      then ascending position; slots with a_fx = 0 sort after every
 //      candidate.  Survival never increases along a request, so each
-//      request's keys already form a sorted run, and the ranking is a merge
-//      of R runs: ceil(log2 R) levels of pairwise merges in which every key
-//      finds its place by one binary search in the partner run (keys are
-//      distinct);
+//      request's keys form a sorted run, and (keys being distinct) a key's
+//      rank is its position in its own run plus, for every other run, the
+//      number of that run's keys below it: one fixed-depth binary descent
+//      per run, the runs of each key dealt out over sixteen threads, four
+//      descents in lockstep.  The key is stored at its rank in the workspace.
+// schedule_kernel, one work group of 1024 threads, everything in LDS and
+// registers:
 //   3. tau_fx(m) = R 2^50 + the exact integer prefix sum of the ranked a_fx;
 //   4. A, by mode:
 //      early stop  the first m with Theta(m) <= Theta(m-1) (exact comparison
@@ -124,77 +127,82 @@ __device__ __forceinline__ WalkPoint better(WalkPoint a, WalkPoint b) {
   return a.m < b.m ? a : b;
 }
 
+// The key of slot (req, j) for j = 0 .. gamma-1 (one thread per request),
+// from the confidences staged in LDS.
+__device__ __forceinline__ void slot_keys(int req, int gamma, const float* cl, uint64_t* keys) {
+  double s = 1.0;
+  for (int j = 0; j < gamma; ++j) {
+    s = s * static_cast<double>(cl[req * gamma + j]);
+    const uint64_t afx = static_cast<uint64_t>(floor(s * static_cast<double>(kOne)));
+    keys[req * gamma + j] = ((kOne - afx) << 13) | static_cast<uint64_t>(req * gamma + j);
+  }
+}
+
+constexpr int kRankThreads = 512;
+constexpr int kRankKeys = 32;                              // keys ranked per work group
+constexpr int kRankParts = kRankThreads / kRankKeys;       // threads sharing a key's runs (16)
+constexpr int kRankBatch = 4;                              // runs searched in lockstep per thread
+
+__global__ __launch_bounds__(kRankThreads) void schedule_rank(int R, int gamma, const float* __restrict__ c,
+                                                              uint64_t* __restrict__ ranked) {
+  __shared__ uint64_t keys[kSchedMaxSlots];
+  __shared__ float cl[kSchedMaxSlots];
+  __shared__ int below[kRankKeys];
+  const int tid = threadIdx.x;
+  const int n = R * gamma;
+  for (int i = tid; i < n; i += kRankThreads) cl[i] = c[i];   // one coalesced pass
+  if (tid < kRankKeys) below[tid] = 0;
+  __syncthreads();
+  for (int req = tid; req < R; req += kRankThreads) slot_keys(req, gamma, cl, keys);
+  __syncthreads();
+  const int kl = tid % kRankKeys;
+  const int i = blockIdx.x * kRankKeys + kl;
+  if (i < n) {
+    const uint64_t key = keys[i];
+    const int own = i / gamma;
+    int top = 1;   // highest power of two <= gamma: a fixed-depth descent
+    while ((top << 1) <= gamma) top <<= 1;
+    int cnt = 0;
+    for (int run0 = tid / kRankKeys; run0 < R; run0 += kRankBatch * kRankParts) {
+      int pos[kRankBatch];
+#pragma unroll
+      for (int b = 0; b < kRankBatch; ++b) pos[b] = 0;
+      // pos[b] becomes the number of keys of run run0 + b kRankParts below `key`
+      for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+        for (int b = 0; b < kRankBatch; ++b) {
+          const int run = run0 + b * kRankParts;
+          const int q = pos[b] + step;
+          if (run < R && q <= gamma && keys[run * gamma + q - 1] < key) pos[b] = q;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kRankBatch; ++b) {
+        const int run = run0 + b * kRankParts;
+        if (run < R && run != own) cnt += pos[b];
+      }
+    }
+    atomicAdd(&below[kl], cnt);
+  }
+  __syncthreads();
+  if (tid < kRankKeys && i < n) ranked[below[tid] + i % gamma] = keys[i];
+}
+
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamma,
-                                                                 const float* __restrict__ c,
                                                                  const double* __restrict__ sps,
                                                                  int mode,
                                                                  const int32_t* __restrict__ cap,
+                                                                 const uint64_t* __restrict__ ranked,
                                                                  int32_t* __restrict__ ell,
                                                                  int32_t* __restrict__ admitted,
                                                                  double* __restrict__ theta_best) {
-  __shared__ uint64_t lds_keys[2 * kSchedMaxSlots];   // two buffers of n keys; reused for the scan afterwards
+  __shared__ uint64_t lds_small[32];   // wave totals, then scalars
   __shared__ WalkPoint wbest[kSchedThreads / kWave];
   const int tid = threadIdx.x;
   const int n = R * gamma;
 
-  // 1-2: the confidences go to LDS in one coalesced pass (through the
-  // second key buffer, free until the first merge), then one thread per
-  // request walks its positions in order and writes the keys
-  uint64_t* keys = lds_keys;
-  uint64_t* other = lds_keys + n;
-  float* cl = reinterpret_cast<float*>(other);
-  for (int i = tid; i < n; i += kSchedThreads) cl[i] = c[i];
+  uint64_t* keys = lds_small;
   for (int req = tid; req < R; req += kSchedThreads) ell[req] = 0;
-  __syncthreads();
-  for (int req = tid; req < R; req += kSchedThreads) {
-    double s = 1.0;
-    for (int j = 0; j < gamma; ++j) {
-      s = s * static_cast<double>(cl[req * gamma + j]);
-      const uint64_t afx = static_cast<uint64_t>(floor(s * static_cast<double>(kOne)));
-      keys[req * gamma + j] = ((kOne - afx) << 13) | static_cast<uint64_t>(req * gamma + j);
-    }
-  }
-  __syncthreads();
-
-  // merge levels: runs of length L = gamma 2^l are merged in pairs; a key's
-  // place in its partner run is a fixed-depth binary descent, two keys per
-  // thread side by side
-  for (int L = gamma; L < n; L <<= 1) {
-    int top = 1;
-    while ((top << 1) <= L) top <<= 1;   // highest power of two <= L
-    for (int i0 = tid; i0 < n; i0 += 2 * kSchedThreads) {
-      int idx[2], part0[2], plen[2], pos[2], dst[2];
-      uint64_t key[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = i0 + e * kSchedThreads;
-        const int ii = i < n ? i : n - 1;
-        const int run = ii / L;
-        const int a0 = (run & ~1) * L;               // start of the merged pair
-        part0[e] = (run & 1) ? a0 : a0 + L;          // start of the partner run
-        const int rest = n - part0[e];
-        plen[e] = (run & 1) ? L : (rest < L ? (rest > 0 ? rest : 0) : L);
-        idx[e] = i;
-        key[e] = keys[ii];
-        dst[e] = a0 + (ii - run * L);
-        pos[e] = 0;
-      }
-      for (int step = top; step > 0; step >>= 1) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int q = pos[e] + step;
-          if (q <= plen[e] && keys[part0[e] + q - 1] < key[e]) pos[e] = q;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        if (idx[e] < n) other[dst[e] + pos[e]] = key[e];
-    }
-    __syncthreads();
-    uint64_t* t = keys;
-    keys = other;
-    other = t;
-  }
   const int P = n;   // ranked keys: keys[0 .. n)
 
   // 3: thread t owns ranked positions [t*8, t*8+8)
@@ -205,10 +213,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int p = tid * kPer + t;
-    myk[t] = (p < P) ? keys[p] : ~0ull;
+    myk[t] = (p < P) ? ranked[p] : ~0ull;
     if (myk[t] < cand_limit) local += kOne - (myk[t] >> 13);
   }
-  __syncthreads();                     // keys now live in registers
+  __syncthreads();                     // ell is cleared before any slot is admitted
   // exclusive prefix of the per-thread sums: a scan inside each wave, then
   // one pass over the wave totals
   uint64_t incl = local;
@@ -326,11 +334,19 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
   }
 }
 
-size_t schedule_workspace_bytes() { return 0; }
+// The ranked slot keys.
+size_t schedule_workspace_bytes(int R, int gamma) {
+  return (sizeof(uint64_t) * static_cast<size_t>(R) * gamma + 255) & ~static_cast<size_t>(255);
+}
 
 hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
-                           int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, R, gamma, c, sps, mode, cap, ell,
+                           int32_t* ell, int32_t* admitted, double* theta_best, void* ws, hipStream_t s) {
+  uint64_t* ranked = static_cast<uint64_t*>(ws);
+  hipLaunchKernelGGL(schedule_rank, dim3(ceil_div(R * gamma, kRankKeys)), dim3(kRankThreads), 0, s, R, gamma, c,
+                     ranked);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, R, gamma, sps, mode, cap, ranked, ell,
                      admitted, theta_best);
   return hipGetLastError();
 }

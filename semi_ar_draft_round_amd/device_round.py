@@ -57,6 +57,7 @@ class DeviceRound:
     n_acc: torch.Tensor
     next_tok: torch.Tensor
     ws_sample: torch.Tensor
+    ws_sched: torch.Tensor
     ws_verify: torch.Tensor
     # the production scheduler: this round's capacity, its fill, and the
     # capacity its confidences set for two rounds later
@@ -104,6 +105,8 @@ def to_device(inp, device="cuda:0", rnn: bool = False) -> DeviceRound:
         next_tok=torch.empty(R, dtype=torch.int32, device=dev),
         ws_sample=torch.empty(max(1, B.dspark_workspace_size(B.WS_SAMPLE, R, gamma, V, r)),
                               dtype=torch.uint8, device=dev),
+        ws_sched=torch.empty(max(1, B.dspark_workspace_size(B.WS_SCHEDULE, R, gamma, V, r)),
+                             dtype=torch.uint8, device=dev),
         ws_verify=torch.empty(max(1, B.dspark_workspace_size(B.WS_VERIFY, R, gamma, V, r)),
                               dtype=torch.uint8, device=dev),
         cap=torch.full((1,), R * gamma // 8, dtype=torch.int32, device=dev),
@@ -145,15 +148,15 @@ def confidence(d: DeviceRound):
 
 
 def schedule(d: DeviceRound):
-    B.dspark_schedule(d.c, d.sps, d.ell, d.admitted, d.theta_best)
+    B.dspark_schedule(d.c, d.sps, d.ell, d.admitted, d.theta_best, ws=d.ws_sched)
 
 
 def schedule_production(d: DeviceRound):
     """The asynchronous scheduler's two calls: fill this round's capacity
     from the current ranking, then the whole-walk optimum of the current
     confidences, which is the capacity two rounds later."""
-    B.dspark_schedule_ex(d.c, d.sps, B.SCHED_CAPACITY, d.cap, d.ell_p, d.admitted_p, d.theta_p)
-    B.dspark_schedule_ex(d.c, d.sps, B.SCHED_WHOLE_WALK, None, d.ell_w, d.cap_next, d.theta_w)
+    B.dspark_schedule_ex(d.c, d.sps, B.SCHED_CAPACITY, d.cap, d.ell_p, d.admitted_p, d.theta_p, ws=d.ws_sched)
+    B.dspark_schedule_ex(d.c, d.sps, B.SCHED_WHOLE_WALK, None, d.ell_w, d.cap_next, d.theta_w, ws=d.ws_sched)
 
 
 def rnn_sample(d: DeviceRound):

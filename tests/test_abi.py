@@ -64,7 +64,10 @@ def test_workspace_sizes(lib):
     assert B.dspark_workspace_size(B.WS_VERIFY, 128, 16, 129280, 256) >= 4 * 128 * (2 * n_c + 33)
     assert B.dspark_workspace_size(B.WS_SAMPLE, 0, 16, 129280, 256) == 0
     assert B.dspark_workspace_size(B.WS_VERIFY, 4, 0, 1000, 256) == 0
-    assert B.dspark_workspace_size(B.WS_SCHEDULE, 128, 16, 0, 0) == 0
+    # the scheduler's ranked slot keys: 8 bytes per slot, rounded up to 256
+    assert B.dspark_workspace_size(B.WS_SCHEDULE, 128, 16, 0, 0) == 8 * 128 * 16
+    assert B.dspark_workspace_size(B.WS_SCHEDULE, 3, 5, 0, 0) == 256
+    assert B.dspark_workspace_size(B.WS_SCHEDULE, 482, 16, 0, 0) == 0   # 482 * 17 > 8191
 
 
 P = ctypes.c_void_p
@@ -109,6 +112,9 @@ def test_schedule_rejects_bad_arguments(lib):
     assert call(gamma=0) == EINVAL
     assert call(R=482, gamma=16, n_sps=10000) == EINVAL   # 482 * 17 > 8191
     assert call(ptr=None) == EINVAL
+    # valid arguments without the workspace (or with too little of it)
+    assert call() == EWORKSPACE
+    assert lib.dspark_schedule(4, 3, FAKE, FAKE, 16, FAKE, None, None, FAKE, 95, None) == EWORKSPACE
 
 
 def test_schedule_ex_rejects_bad_arguments(lib):
@@ -120,6 +126,7 @@ def test_schedule_ex_rejects_bad_arguments(lib):
     assert call(n_sps=15) == EINVAL
     assert call(R=482, gamma=16, n_sps=10000) == EINVAL
     assert call(ptr=None) == EINVAL
+    assert call() == EWORKSPACE
 
 
 def test_verify_greedy_rejects_bad_arguments(lib):
