@@ -163,3 +163,15 @@ def test_gpu_lossless_and_acceptance_rate(dev):
     say(f"  chi2 p={p:.3g}, accept {acc:.4f} vs {want:.4f} (z={z:.2f})")
     assert p > 1e-4
     assert abs(z) < 4.5
+
+
+@pytest.mark.parametrize("R,gamma", [(4095, 1), (126, 64), (1, 64), (2, 1), (100, 3), (33, 31)])
+def test_extreme_shapes_bit_exact(R, gamma, dev):
+    """Runs of one key (gamma = 1, 4095 requests), of the largest length
+    (gamma = 64), and shapes whose slot counts are not multiples of the
+    ranking's 32-key work groups: bit-exact with and without ties."""
+    for ties in (False, True):
+        rng = np.random.default_rng(R * 1000 + gamma + (7 if ties else 0))
+        say(f"[schedule] R={R} gamma={gamma} ties={ties}")
+        c, sps = random_case(rng, R, gamma, ties=ties)
+        assert_same(c, sps, dev)
