@@ -107,6 +107,7 @@ def main():
               "--gpus > 1 is not run.", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -185,6 +186,18 @@ def main():
 
     ms = timed("round", args.steps, args.warmup)
     log(f"[bench] round: {ms * 1e3:.1f} us")
+    # the spread of single rounds, each bracketed by its own events (a second
+    # pass after the timed region above, which alone gives `value`)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(args.steps, 20))]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        graphs["round"][i % 2].replay()
+        e1.record()
+    torch.cuda.synchronize()
+    singles = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    spread = [round(float(np.percentile(singles, q)), 1) for q in (10, 50, 90)]
+    log(f"[bench] single rounds p10/p50/p90: {spread} us")
     parts = {}
     for name in ("sample", "confidence", "schedule", "verify"):
         parts[name] = timed(name, max(args.steps, 10), 2) * 1e3
@@ -211,11 +224,14 @@ def main():
     # launch duration (a few percent high, so `achieved` is a lower bound).
     launch_us = parts["sample"]
     bytes_launch = sample_bytes_per_position(w) * w.gamma
+    # the on-chip-reuse floor: W2 read once per launch instead of once per position
+    bytes_model_b = bytes_launch - (w.gamma - 1) * w.r * w.V * 2
     achieved = bytes_launch / (launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(w.name),
                 "kernel": "sample_steps_wide (all gamma positions in one launch; timed as the sampling call)",
-                "bytes_per_launch": bytes_launch, "us_per_launch": round(launch_us, 2)}
+                "bytes_per_launch": bytes_launch, "us_per_launch": round(launch_us, 2),
+                "bytes_per_launch_w2_once": bytes_model_b}
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -225,6 +241,7 @@ def main():
         "config": {"workload": w.name, "R": w.R, "gamma": w.gamma, "V": w.V, "r": w.r, "d": w.d,
                    "global_batch": w.R, "admitted": out["A"], "accepted": int(out["n_acc"].sum()),
                    "parallelism": "none (1 GPU)"},
+        "round_us_p10_p50_p90": spread,
         "parts_us": {k: round(v, 2) for k, v in parts.items()},
         "modes_us": {k: round(v, 2) for k, v in modes.items()},
         "roofline": roofline,
