@@ -48,17 +48,10 @@ def sample_bytes_per_position(w) -> int:
     return w.R * w.V * 2 + w.r * w.V * 2 + w.R * w.n_chunks * 4
 
 
-def cpu_baseline(inps, n_req: int, min_seconds: float = 10.0, max_rounds: int = 8) -> dict:
-    """The float64 oracle, free running, on a bounded sample of the same
-    workload: n_req requests per round (the whole batch when n_req >= R),
-    repeated over the input sets until at least min_seconds of CPU work."""
+def _oracle_rounds(inps, n_req: int, min_seconds: float, max_rounds: int):
+    """Free-running oracle rounds over n_req requests: (rounds, requests, seconds)."""
     import numpy as np
     from oracle.round import run_round
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
     w = inps[0].w
     idx = np.arange(min(n_req, w.R))
     done, dt = 0, 0.0
@@ -67,11 +60,44 @@ def cpu_baseline(inps, n_req: int, min_seconds: float = 10.0, max_rounds: int = 
         run_round(inps[done % len(inps)], requests=idx)
         dt += time.perf_counter() - t0
         done += 1
-    part = "the whole batch" if len(idx) == w.R else f"{len(idx)} of {w.R} requests"
-    return {"value": done * len(idx) * w.gamma / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} free-running rounds of {part} (gamma={w.gamma}, V={w.V}): "
-                      f"sample, confidence, schedule, verify; {dt:.1f} s of CPU work"}
+    return done, len(idx), dt
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inps, n_req: int, min_seconds: float = 10.0, max_rounds: int = 8) -> dict:
+    """The float64 oracle, free running, on a bounded sample of the same
+    workload: n_req requests per round (the whole batch when n_req >= R),
+    repeated over the input sets until at least min_seconds of CPU work;
+    then a second, single-threaded run over a quarter of the requests."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threadpool_limits = None
+        threads = 1
+    w = inps[0].w
+    done, nr, dt = _oracle_rounds(inps, n_req, min_seconds, max_rounds)
+    part = "the whole batch" if nr == w.R else f"{nr} of {w.R} requests"
+    rec = {"value": done * nr * w.gamma / dt, "unit": "tokens/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{done} free-running rounds of {part} (gamma={w.gamma}, V={w.V}): "
+                     f"sample, confidence, schedule, verify; {dt:.1f} s of CPU work",
+           "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "blas_threads": int(threads)}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, n1, t1 = _oracle_rounds(inps, max(1, min(n_req, w.R) // 4), min_seconds / 2, max_rounds)
+        rec["single_thread"] = {"value": d1 * n1 * w.gamma / t1, "unit": "tokens/s",
+                                "sample": f"{d1} rounds of {n1} of {w.R} requests, one thread; {t1:.1f} s"}
+    return rec
 
 
 def traffic_record(workload: str):
