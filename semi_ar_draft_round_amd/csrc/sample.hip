@@ -381,7 +381,6 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
     const float* __restrict__ g, SampleWs ws, int nPart, int kb, int ke, const uint16_t* __restrict__ bvec) {
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
-  constexpr int T = wide_threads<RQ>();
   constexpr int NROWS = 32 * RQ;
   constexpr int kW = wide_tile_bytes<KS16>();   // tile bytes (padded rows)
   // two streaming slots, then the kResident tiles kept for the whole launch
