@@ -128,9 +128,9 @@ def main():
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build measures the per-GPU hot path; "
-              "requests shard across GPUs with no exchange (see the design notes), so "
-              "--gpus > 1 is not run.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: it measures one GPU's share of the hot path. "
+              "Requests shard across GPUs with no exchange, so the per-GPU figure is the "
+              "whole story; --gpus > 1 is not run.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
