@@ -340,6 +340,10 @@ __global__ __launch_bounds__(256) void verify_greedy_accept(int R, int gamma, co
 
 // ------------------------------------------------------- residual chunk masses
 
+// Tiles whose chunk masses a residual work group keeps in LDS until the end
+// of its sweep (4 KB each at 128 rows).
+constexpr int kMassStage = 12;
+
 // Row stride of the per-request chunk-mass arrays: ceil(V/16) rounded up to
 // a multiple of four floats, so select can read them as 16-byte vectors.
 __host__ __device__ __forceinline__ int mass_stride(int V) {
@@ -433,6 +437,11 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   constexpr int kW = wide_tile_bytes<KS16>();
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
   __shared__ float accsh[ACC ? NROWS : 1];
+  // chunk masses of the work group's tiles, [tile][row][chunk of the tile],
+  // written out together after the sweep (when the group has at most
+  // kMassStage tiles; otherwise they are stored as they are made)
+  __shared__ __attribute__((aligned(16))) float msh_c[ACC ? 1 : kMassStage][ACC ? 1 : NROWS][4];
+  __shared__ __attribute__((aligned(16))) float msh_p[ACC ? 1 : kMassStage][ACC ? 1 : NROWS][4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int th = wave & 1;
@@ -446,11 +455,16 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   const int nTiles = (V + kChunk - 1) / kChunk;
   const int nG = (V + kGChunk - 1) / kGChunk;
   const int ldm = mass_stride(V);
-  // the host launches at most one work group per tile, so nT >= 1
-  const int nT = (nTiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
-                 static_cast<int>(gridDim.x);
+  // work group b takes the contiguous tiles b per .. b per + nT - 1 (the
+  // host launches ceil(nTiles / p) work groups for some p >= per, so the last
+  // one starts below nTiles and nT >= 1): a request's chunk masses from one
+  // work group are then one contiguous run
+  const int per = (nTiles + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+  const int t0 = static_cast<int>(blockIdx.x) * per;
+  const int nT = min(per, nTiles - t0);
+  const bool staged = !ACC && nT <= kMassStage;
   const auto clampc = [&](int it) { return it < nT ? it : nT - 1; };
-  const auto tile_of = [&](int it) { return static_cast<int>(blockIdx.x) + it * static_cast<int>(gridDim.x); };
+  const auto tile_of = [&](int it) { return t0 + it; };
 
   const ResidualRow rr = ACC ? acceptance_row(min(req, nrows - 1), gamma, V, row0, x0, x, part, lse, bvec)
                              : residual_row(min(req, R - 1), R, gamma, V, row0, x0, x, ell, n_acc, lse_t, lse, bvec);
@@ -525,6 +539,9 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     }
     if constexpr (ACC) {
       mn += cs;
+    } else if (staged) {
+      msh_c[it][rq * 32 + j][2 * th + h] = cs;
+      msh_p[it][rq * 32 + j][2 * th + h] = ps;
     } else {
       const int c16 = 4 * tile_of(it) + 2 * th + h;
       if (live && c16 < nG) {
@@ -542,6 +559,28 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     step(it + 1, odd);
   }
   if (it < nT) step(it, even);
+  if (staged) {
+    // the staged masses: four chunks (16 bytes) per (tile, row) item, a
+    // request's items of consecutive tiles adjacent in memory
+    const int row0g = static_cast<int>(blockIdx.y) * NROWS;
+    for (int e = threadIdx.x; e < nT * NROWS; e += wide_threads<RQ>()) {
+      const int row = e / nT, itl = e % nT;
+      const int rr_ = row0g + row;
+      if (rr_ >= nrows) continue;
+      const int c0 = 4 * tile_of(itl);
+      float* dc = csum + static_cast<int64_t>(rr_) * ldm + c0;
+      float* dp = psum + static_cast<int64_t>(rr_) * ldm + c0;
+      if (c0 + 3 < nG) {
+        *reinterpret_cast<float4*>(dc) = *reinterpret_cast<const float4*>(msh_c[itl][row]);
+        *reinterpret_cast<float4*>(dp) = *reinterpret_cast<const float4*>(msh_p[itl][row]);
+      } else {
+        for (int q = 0; q < 4 && c0 + q < nG; ++q) {
+          dc[q] = msh_c[itl][row][q];
+          dp[q] = msh_p[itl][row][q];
+        }
+      }
+    }
+  }
   if constexpr (ACC) {
     const float t = mn + __shfl_xor(mn, 32);   // the request's two lanes of this token half
     if (th == 1 && h == 0) accsh[rq * 32 + j] = t;
@@ -844,6 +883,7 @@ static int launch_residual_wide(const SweepArgs& a, int rows, hipStream_t s) {
   const int groups = ceil_div(rows, 32 * RQ);
   int gx = compute_units() / groups;
   gx = gx < 1 ? 1 : (gx > nTiles ? nTiles : gx);
+  gx = ceil_div(nTiles, ceil_div(nTiles, gx));   // every work group has at least one tile
   dim3 grid(gx, groups);
   const auto b16 = [](const void* p) { return static_cast<const uint16_t*>(p); };
   if (a.V % kGChunk == 0)
