@@ -90,6 +90,42 @@ def test_full_size_sampled_parity(w, dev):
     assert np.all((out["next_tok"] >= 0) & (out["next_tok"] < w.V))
 
 
+MANY = [W.custom(f"many_r33000_g2_v{V}_bf16", R=33000, gamma=2, V=V, r=32, d=64, seed=51) for V in (320, 203)]
+
+
+@pytest.mark.parametrize("w", MANY, ids=[w.name for w in MANY])
+def test_many_requests_sampled_parity(w, dev):
+    """More request groups of 128 than compute units: the sampler takes one
+    launch per position instead of the persistent grid, and the target
+    normalisers walk every (row, part) item instead of a prefix of the
+    needed rows.  V = 320 takes the 16-byte vector loads, V = 203 the scalar
+    ones.  The scheduler's slot limit is far below R (1 + gamma), so the
+    admitted lengths are drawn (seeded) and sample and verify are called
+    directly; requested rows include the ragged last group."""
+    from semi_ar_draft_round_amd import device_round as DR
+    say(f"[parity] {w.name}: drawing inputs")
+    inp = W.make_inputs(w)
+    d = DR.to_device(inp, dev)
+    ell = np.random.default_rng(5).integers(0, w.gamma + 1, size=w.R).astype(np.int32)
+    d.ell.copy_(torch.from_numpy(ell))
+    say(f"[parity] {w.name}: GPU sample + verify")
+    DR.sample(d)
+    DR.verify(d)
+    torch.cuda.synchronize()
+    out = dict(x=d.x.cpu().numpy(), lse=d.lse.cpu().numpy(), logit=d.logit.cpu().numpy(), ell=ell,
+               n_acc=d.n_acc.cpu().numpy(), next_tok=d.next_tok.cpu().numpy())
+    rng = np.random.default_rng(9)
+    idx = np.unique(np.concatenate([rng.choice(w.R, size=6, replace=False), [0, 32767, 32768, w.R - 1]]))
+    say(f"[parity] {w.name}: oracle on requests {idx.tolist()}")
+    rs = check_sample(inp, out, idx)
+    rv = check_verify(inp, out, idx)
+    say(f"  sample {rs}\n  verify {rv}")
+    assert np.all((out["x"] >= 0) & (out["x"] < w.V))
+    assert np.all(np.isfinite(out["lse"])) and np.all(np.isfinite(out["logit"]))
+    assert np.all((out["n_acc"] >= 0) & (out["n_acc"] <= ell))
+    assert np.all((out["next_tok"] >= 0) & (out["next_tok"] < w.V))
+
+
 def test_packed_target_rows_match_dense(dev):
     """A flattened ragged verify batch (row0 offsets) gives the dense result."""
     from semi_ar_draft_round_amd import binding as B
