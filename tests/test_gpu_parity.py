@@ -44,6 +44,7 @@ SMALL = [
     W.custom("r130_g4_v700_r128_bf16", R=130, gamma=4, V=700, r=128, d=256, seed=13, temperatures=True),
     W.custom("r70_g6_v4100_r64_bf16", R=70, gamma=6, V=4100, r=64, d=128, seed=14),
     W.custom("f32_r9_g7_v333", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=15),
+    W.custom("gmax_r5_g64_v1000_bf16", R=5, gamma=64, V=1000, r=64, d=64, seed=16),
 ]
 
 
@@ -124,6 +125,41 @@ def test_many_requests_sampled_parity(w, dev):
     assert np.all(np.isfinite(out["lse"])) and np.all(np.isfinite(out["logit"]))
     assert np.all((out["n_acc"] >= 0) & (out["n_acc"] <= ell))
     assert np.all((out["next_tok"] >= 0) & (out["next_tok"] < w.V))
+
+
+def test_all_accepted_at_max_gamma(dev):
+    """gamma = 64 with every draft admitted and accepted, so the bonus row 64
+    is normalised in the accept kernel's second pass over the rows and the
+    next token is the bonus draw from it.  W1 = 0 makes p_d = softmax(U_k);
+    the target row k is U_k with the drafted token's logit raised by 2, so
+    p_t(x_k) > p_d(x_k) and every accept test passes by a wide margin.  One
+    request is admitted 63 drafts (its bonus is row 63) and one none."""
+    from semi_ar_draft_round_amd import device_round as DR
+    w = W.custom("accept_all_r4_g64_v1000_bf16", R=4, gamma=64, V=1000, r=64, d=64, seed=17)
+    say(f"[parity] {w.name}")
+    inp = W.make_inputs(w)
+    inp.E[:] = 0
+    d = DR.to_device(inp, dev)
+    DR.sample(d)
+    torch.cuda.synchronize()
+    x = d.x.cpu().numpy()
+    u = W.bf16_to_f32(inp.U)
+    t = np.concatenate([u, u[:, -1:, :]], axis=1)            # row gamma: a copy of row gamma - 1
+    rows = np.arange(w.R)[:, None]
+    t[rows, np.arange(w.gamma)[None, :], x] += 2.0
+    inp.target = W.bf16_bits(t.astype(np.float32))
+    d.target.copy_(DR.to_device(inp, dev).target)
+    ell = np.array([64, 63, 0, 64], dtype=np.int32)
+    d.ell.copy_(torch.from_numpy(ell))
+    DR.verify(d)
+    torch.cuda.synchronize()
+    out = dict(x=x, lse=d.lse.cpu().numpy(), logit=d.logit.cpu().numpy(), ell=ell,
+               n_acc=d.n_acc.cpu().numpy(), next_tok=d.next_tok.cpu().numpy())
+    idx = np.arange(w.R)
+    rs = check_sample(inp, out, idx)
+    rv = check_verify(inp, out, idx)
+    say(f"  sample {rs}\n  verify {rv}")
+    assert out["n_acc"].tolist() == ell.tolist()
 
 
 def test_packed_target_rows_match_dense(dev):
