@@ -1,8 +1,8 @@
 """CPU oracle for the DSpark draft-and-verify round: plain, slow, float64.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
-execute this package: only the test suite, the smoke check of the graft entry
-point and the CPU-baseline leg of the benchmark use it.  It shares no code with
+execute this package: only the test suite, `__graft_entry__.smoke()` and the
+CPU-baseline leg of the benchmark use it.  It shares no code with
 the HIP library (no kernels, headers, helpers, tables or generators); the two
 meet only in the seeded inputs both of them read.
 
