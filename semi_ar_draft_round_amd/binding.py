@@ -120,7 +120,11 @@ _ws_cache: dict = {}
 
 
 def workspace(kind: int, R: int, gamma: int, V: int, r: int, device) -> torch.Tensor:
-    """A cached device workspace of the size the library asks for."""
+    """A cached device workspace of the size the library asks for.
+
+    One buffer serves every call of the same kind and shape on a device, so
+    calls that may overlap (on different streams) must each pass a workspace
+    of their own."""
     n = max(1, dspark_workspace_size(kind, R, gamma, V, r, 0))
     key = (kind, R, gamma, V, r, str(device))
     ws = _ws_cache.get(key)
