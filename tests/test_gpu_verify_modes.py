@@ -61,6 +61,7 @@ GREEDY = [
     W.custom("greedy_r3_g3_v203_bf16", R=3, gamma=3, V=203, r=32, d=64, seed=22),
     W.custom("greedy_r70_g6_v4100_bf16", R=70, gamma=6, V=4100, r=32, d=64, seed=23),
     W.custom("greedy_r9_g7_v333_f32", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=24),
+    W.custom("greedy_r6_g64_v1000_bf16", R=6, gamma=64, V=1000, r=32, d=64, seed=25),
     W.BY_NAME["heavy_r128_g16_v129280"],
 ]
 
@@ -90,6 +91,26 @@ def test_greedy_bit_exact(w, dev):
     assert n_acc.cpu().numpy().tolist() == ref["n_acc"].tolist()
     assert next_tok.cpu().numpy().tolist() == ref["next_tok"].tolist()
     say(f"  accepted {int(ref['n_acc'].sum())} of {int(ell.sum())}")
+
+
+def test_greedy_all_accepted_at_max_gamma(dev):
+    """gamma = 64 with every admitted draft equal to its row's argmax: the
+    accepted prefix is the whole admitted length, and the next token is the
+    argmax of row l_r (row 64, the bonus row, when all 64 are admitted)."""
+    from semi_ar_draft_round_amd import binding as B
+    w = W.custom("greedy_all_r4_g64_v1000_bf16", R=4, gamma=64, V=1000, r=32, d=64, seed=26)
+    say(f"[greedy] {w.name}")
+    inp = W.make_inputs(w)
+    t64 = as_f64(inp.target, w.dtype)
+    x = t64.argmax(axis=2)[:, :w.gamma].astype(np.int32)
+    ell = np.array([64, 63, 0, 64], dtype=np.int32)
+    n_acc, next_tok = B.dspark_verify_greedy(_store(inp.target, w.dtype, dev), torch.tensor(x, device=dev),
+                                             torch.tensor(ell, device=dev))
+    torch.cuda.synchronize()
+    ref = OV.verify_greedy(t64, None, x, ell)
+    assert ref["n_acc"].tolist() == ell.tolist()
+    assert n_acc.cpu().numpy().tolist() == ell.tolist()
+    assert next_tok.cpu().numpy().tolist() == ref["next_tok"].tolist()
 
 
 def test_greedy_packed_rows_match_dense(dev):
