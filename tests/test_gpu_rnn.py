@@ -93,6 +93,7 @@ CASES = [
     W.custom("rnn_r70_g6_v4100_r64", R=70, gamma=6, V=4100, r=64, d=128, seed=43),
     W.custom("rnn_r130_g4_v700_r128", R=130, gamma=4, V=700, r=128, d=256, seed=44),
     W.custom("rnn_r9_g7_v333_f32", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=45),
+    W.custom("rnn_r5_g64_v1000_r32", R=5, gamma=64, V=1000, r=32, d=64, seed=46),
 ]
 
 
