@@ -44,7 +44,7 @@ def _run(z, n_acc, grid, M, dev):
 
 
 @pytest.mark.parametrize("N,gamma,beta,M", [(20000, 4, 2.0, 15), (5000, 6, 1.0, 10), (777, 3, 3.0, 15),
-                                           (65536, 16, 2.0, 15)])
+                                           (65536, 16, 2.0, 15), (20000, 64, 2.0, 15)])
 def test_sts_matches_oracle(N, gamma, beta, M, dev):
     say(f"[sts] N={N} gamma={gamma} beta={beta} M={M}")
     z, n_acc = W.make_rollouts(N, gamma, beta)
