@@ -141,6 +141,7 @@ ACC_SMALL = [
     W.custom("acc_r3_g3_v203_bf16", R=3, gamma=3, V=203, r=32, d=64, seed=32),
     W.custom("acc_r70_g6_v4100_r64_bf16", R=70, gamma=6, V=4100, r=64, d=128, seed=33),
     W.custom("acc_r9_g7_v333_f32", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=34),
+    W.custom("acc_r5_g64_v1000_bf16", R=5, gamma=64, V=1000, r=64, d=64, seed=35),
 ]
 
 
