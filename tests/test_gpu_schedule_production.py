@@ -105,9 +105,10 @@ def test_random_batches_bit_exact(seed, dev):
         same_capacity(c, sps, K, dev)
 
 
-def test_largest_batch_bit_exact(dev):
-    rng = np.random.default_rng(78)
-    R, gamma = 481, 16
+@pytest.mark.parametrize("R,gamma", [(481, 16), (126, 64)])
+def test_largest_batch_bit_exact(R, gamma, dev):
+    """The largest batches the slot limit admits: R (1 + gamma) = 8177 and 8190."""
+    rng = np.random.default_rng(78 + gamma)
     say(f"[production] R={R} gamma={gamma}")
     c = rng.uniform(0.3, 1.0, size=(R, gamma)).astype(np.float32)
     B = np.arange(1, R * (1 + gamma) + 1, dtype=np.float64)
