@@ -45,6 +45,9 @@ SMALL = [
     W.custom("r70_g6_v4100_r64_bf16", R=70, gamma=6, V=4100, r=64, d=128, seed=14),
     W.custom("f32_r9_g7_v333", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=15),
     W.custom("gmax_r5_g64_v1000_bf16", R=5, gamma=64, V=1000, r=64, d=64, seed=16),
+    # 18752 chunk masses per request: more than the residual draw keeps in
+    # registers, so it scans them from memory
+    W.custom("bigv_r3_g2_v300000_bf16", R=3, gamma=2, V=300000, r=32, d=64, seed=62),
 ]
 
 
