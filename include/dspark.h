@@ -9,6 +9,8 @@
  * sit between the backbone and the target model, as HIP kernels:
  *
  *   dspark_markov_sample  the sequential Markov-head sampling loop
+ *   dspark_markov_sample_ex  the same, with the confidence head, a cancel
+ *                         word and a device status word
  *   dspark_rnn_sample     the same loop with the RNN head
  *   dspark_confidence     the confidence head (linear + sigmoid, temperature)
  *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
@@ -35,8 +37,16 @@
  *     DSPARK_ELAUNCH.  Conditions on device data (token ranges, confidences
  *     in [0,1], a positive non-increasing step-speed table) are the caller's
  *     obligations and are not checked.
- *   - No call keeps state between calls; calls on different streams with
- *     different workspaces may run concurrently.
+ *   - No call keeps state between calls.  Calls on different streams with
+ *     different workspaces may run concurrently, with one exception: with
+ *     bf16 storage, dspark_markov_sample(_ex) runs all gamma positions in one
+ *     persistent launch whose work groups (one per compute unit) meet at a
+ *     grid barrier between positions, so it needs every compute unit of the
+ *     device at once.  Do not overlap it with other work on the device (the
+ *     library cannot see or serialise the caller's streams).  If its grid is
+ *     not resident as a whole, the barrier gives up after 0.5 s instead of
+ *     hanging: every x is then -1 and every lse and logit NaN, and the status
+ *     word of dspark_markov_sample_ex reads DSPARK_ETIMEOUT.
  *   - dt selects the storage type of the large tensors (U, W1, W2, w, h,
  *     target): fp32 or bf16.  Arithmetic is fp32 (scheduler: fp64 and exact
  *     integers).  Random draws are inputs, drawn by the caller.
@@ -61,7 +71,9 @@ typedef enum {
   DSPARK_EDTYPE = 2,      /* unsupported data type for this call / shape       */
   DSPARK_EWORKSPACE = 3,  /* workspace missing or smaller than required        */
   DSPARK_ELAUNCH = 4,     /* a kernel launch failed                            */
-  DSPARK_EDEVICE = 5      /* the current device is not a gfx950 GPU            */
+  DSPARK_EDEVICE = 5,     /* the current device is not a gfx950 GPU            */
+  DSPARK_ETIMEOUT = 6     /* device status only: the sampler's grid barrier
+                             gave up (time-out or cancel); no valid draw        */
 } dspark_status;
 
 typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
@@ -111,14 +123,52 @@ typedef enum {
  *   ws     workspace of at least dspark_workspace_size(DSPARK_WS_SAMPLE, ...)
  *          bytes; contents on entry are irrelevant.
  *
- * Limits: R >= 1, 1 <= gamma <= 64, 2 <= V < 2^24.  bf16: r a multiple of
- * 32, r <= 256.  fp32: 1 <= r <= 1024.
+ * With bf16 storage the call is one persistent launch that needs the whole
+ * device (see the conventions above).  If its grid barrier gives up, every
+ * x is -1 and every lse and logit NaN (a sentinel: valid draws are in
+ * [0, V)); dspark_markov_sample_ex also reports it in a status word.
+ *
+ * Limits: R >= 1, 1 <= gamma <= 64, 2 <= V < 2^24.  bf16: r in {32, 64, 128,
+ * 256} (else DSPARK_EDTYPE).  fp32: 1 <= r <= 1024.
  */
 dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int r,
                                    const void* U, const void* W1, const void* W2t,
                                    const int32_t* x0, const float* G, const float* g,
                                    int32_t* x, float* lse, float* logit,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_markov_sample_ex — dspark_markov_sample, optionally followed by the
+ * confidence head on the drafted tokens, with a cancel word and a status word.
+ *
+ * Passage: as dspark_markov_sample and dspark_confidence (caijizhuo section
+ * 四: the sequential loop computes each position's confidence from its
+ * hidden state and the previous token right after drawing it).
+ *
+ *   dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws
+ *          as in dspark_markov_sample
+ *   d, h, w, T, c, z
+ *          as in dspark_confidence, computed on the drafted x.  h NULL skips
+ *          the confidence head (d, w, T, c and z are then ignored); with h
+ *          given, w and c are required and z may be NULL.
+ *   cancel [1] u32 device word or NULL.  While it is non-zero, the
+ *          persistent launch's grid-barrier waits give up as on a time-out,
+ *          so a caller can abandon a call that cannot complete.  It is read
+ *          on the device; other paths (fp32, per-position launches) have no
+ *          barrier and ignore it.
+ *   status [1] i32 device word out, or NULL: DSPARK_OK, or DSPARK_ETIMEOUT
+ *          when the grid barrier gave up (x = -1, lse and logit NaN; c and z
+ *          are then computed on no token, x0 for the first position).
+ *
+ * Limits: as dspark_markov_sample, and as dspark_confidence when h is given.
+ */
+dspark_status dspark_markov_sample_ex(dspark_dtype dt, int R, int gamma, int V, int r, int d,
+                                      const void* U, const void* W1, const void* W2t,
+                                      const int32_t* x0, const float* G, const float* g,
+                                      const void* h, const void* w, const float* T,
+                                      int32_t* x, float* lse, float* logit, float* c, float* z,
+                                      const uint32_t* cancel, int32_t* status,
+                                      void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dspark_rnn_sample — the gamma-step sampling loop with the RNN head.
@@ -351,8 +401,9 @@ dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r,
  * integers in units of 2^-32, so the fit is deterministic.  ece_before is
  * the raw chain's (every T = 1).  auc[k] is the ROC-AUC of the raw logit
  * z_k between accepted (n_acc >= k) and rejected (n_acc = k - 1) rollouts
- * that reached position k, ties counted half (NaN without both classes);
- * it is an exact pair count, O(N^2) work per position.
+ * that reached position k, ties counted half (NaN without both classes).
+ * The count equals the pairwise definition exactly but is computed from one
+ * sort of the rejected logits and rank counts: O(N log N) work in all.
  *
  *   z       [N][gamma] f32: the confidence head's logits per rollout
  *   n_acc   [N] i32: accepted prefix length of each rollout, 0..gamma

@@ -30,6 +30,8 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "dspark_markov_sample": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_markov_sample_ex": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _P, _P, _SZ, _P],
     "dspark_confidence": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "dspark_schedule": [_I, _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P],
     "dspark_schedule_ex": [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
@@ -159,6 +161,55 @@ def dspark_markov_sample(U, W1, W2t, x0, G, g, x=None, lse=None, logit=None, ws=
                                   ws.numel(), _stream())
     _raise("dspark_markov_sample", st)
     return x, lse, logit
+
+
+def dspark_markov_sample_ex(U, W1, W2t, x0, G, g, h=None, w=None, T=None, x=None, lse=None, logit=None,
+                            c=None, z=None, cancel=None, status=None, ws=None):
+    """dspark_markov_sample plus, when h and w are given, the confidence head
+    on the drafted tokens.  cancel: an optional uint32/int32 [1] device word
+    (non-zero ends the grid-barrier waits); status: an int32 [1] device word
+    out (0 = ok, 6 = the grid barrier gave up).  Returns x, lse, logit, c, z,
+    status (c and z None without h)."""
+    lib = load_library()
+    R, gamma, V = U.shape
+    r = W1.shape[1]
+    dev = U.device
+    sdt = (U.dtype,)
+    _check(U, "U", (R, gamma, V), sdt, dev)
+    _check(W1, "W1", (V, r), sdt, dev)
+    _check(W2t, "W2t", (V, r), sdt, dev)
+    _check(x0, "x0", (R,), (torch.int32,), dev)
+    _check(G, "G", (gamma, (V + CHUNK - 1) // CHUNK, R), (torch.float32,), dev)
+    _check(g, "g", (R, gamma, CHUNK), (torch.float32,), dev)
+    x = torch.empty((R, gamma), dtype=torch.int32, device=dev) if x is None else x
+    lse = torch.empty((R, gamma), dtype=torch.float32, device=dev) if lse is None else lse
+    logit = torch.empty((R, gamma), dtype=torch.float32, device=dev) if logit is None else logit
+    _check(x, "x", (R, gamma), (torch.int32,), dev)
+    _check(lse, "lse", (R, gamma), (torch.float32,), dev)
+    _check(logit, "logit", (R, gamma), (torch.float32,), dev)
+    d = 0
+    if h is not None:
+        d = h.shape[2]
+        _check(h, "h", (R, gamma, d), sdt, dev)
+        _check(w, "w", (d + r,), sdt, dev)
+        if T is not None:
+            _check(T, "T", (gamma,), (torch.float32,), dev)
+        c = torch.empty((R, gamma), dtype=torch.float32, device=dev) if c is None else c
+        _check(c, "c", (R, gamma), (torch.float32,), dev)
+        if z is not None:
+            _check(z, "z", (R, gamma), (torch.float32,), dev)
+    else:
+        c = z = None
+    if cancel is not None:
+        _check(cancel, "cancel", (1,), (torch.int32,), dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev) if status is None else status
+    _check(status, "status", (1,), (torch.int32,), dev)
+    ws = workspace(WS_SAMPLE, R, gamma, V, r, dev) if ws is None else ws
+    st = lib.dspark_markov_sample_ex(_dt(U), R, gamma, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(x0), _ptr(G),
+                                     _ptr(g), _ptr(h), _ptr(w), _ptr(T), _ptr(x), _ptr(lse), _ptr(logit), _ptr(c),
+                                     _ptr(z), _ptr(cancel), _ptr(status), _ptr(ws), ws.numel(), _stream())
+    _raise("dspark_markov_sample_ex", st)
+    return x, lse, logit, c, z, status
 
 
 def dspark_confidence(h, w, W1, x0, x, T=None, c=None, z=None, want_z=True):

@@ -20,7 +20,7 @@ hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, co
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                         hipStream_t s, const RnnHead* rnn);
+                         hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status);
 // confidence.hip
 hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
                              const void* w, const void* W1, const int32_t* x0, const int32_t* x,
@@ -109,6 +109,7 @@ const char* dspark_status_string(dspark_status s) {
     case DSPARK_EWORKSPACE: return "workspace missing or too small";
     case DSPARK_ELAUNCH: return "kernel launch failed";
     case DSPARK_EDEVICE: return "current device is not a gfx950 GPU";
+    case DSPARK_ETIMEOUT: return "the sampler's grid barrier timed out or was cancelled (no valid draw)";
   }
   return "unknown status";
 }
@@ -155,21 +156,38 @@ size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r
   return 0;
 }
 
-dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
-                                   const void* W1, const void* W2t, const int32_t* x0, const float* G,
-                                   const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                                   size_t ws_bytes, void* stream) {
+dspark_status dspark_markov_sample_ex(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                      const void* W1, const void* W2t, const int32_t* x0, const float* G,
+                                      const float* g, const void* h, const void* w, const float* T, int32_t* x,
+                                      float* lse, float* logit, float* c, float* z, const uint32_t* cancel,
+                                      int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   if (!dtype_ok(dt)) return DSPARK_EDTYPE;
   if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
   if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
   if (!U || !W1 || !W2t || !x0 || !G || !g || !x || !lse || !logit) return DSPARK_EINVAL;
+  const bool conf = h != nullptr;
+  if (conf) {
+    const int vec = (dt == DSPARK_BF16) ? 8 : 4;
+    if (!w || !c || d < 1 || d % vec != 0 || r % vec != 0) return DSPARK_EINVAL;
+  }
   if (!ws || ws_bytes < sample_workspace_bytes(dt, R, gamma, V)) return DSPARK_EWORKSPACE;
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
-  if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws,
-                    static_cast<hipStream_t>(stream), nullptr) != hipSuccess)
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, s, nullptr, cancel, status) !=
+      hipSuccess)
+    return DSPARK_ELAUNCH;
+  if (conf && confidence_launch(dt, R, gamma, d, r, V, h, w, W1, x0, x, T, c, z, s) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
+}
+
+dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
+                                   const void* W1, const void* W2t, const int32_t* x0, const float* G,
+                                   const float* g, int32_t* x, float* lse, float* logit, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return dspark_markov_sample_ex(dt, R, gamma, V, r, 0, U, W1, W2t, x0, G, g, nullptr, nullptr, nullptr, x, lse,
+                                 logit, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
@@ -292,7 +310,7 @@ dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r,
   const size_t off = (sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255);
   const RnnHead head{Wrnn, h, d, s, o, reinterpret_cast<float*>(static_cast<char*>(ws) + off)};
   if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, static_cast<hipStream_t>(stream),
-                    &head) != hipSuccess)
+                    &head, nullptr, nullptr) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

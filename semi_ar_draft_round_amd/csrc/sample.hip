@@ -25,6 +25,8 @@
 #include "sample_keys.hpp"
 #include "rnn_head.hpp"
 
+#include <atomic>
+
 namespace dspark {
 
 // Upper bound on the work groups per position along the vocabulary (the
@@ -81,7 +83,11 @@ __device__ __forceinline__ void lane_draw_init(LaneDraw& d) {
 
 // Fold one Gumbel chunk (the lane's sixteen logits l, first token `first`,
 // chunk Gumbel G) into the lane's state.  Chunks with no finite logit get a
-// score of -inf and add nothing.
+// score of -inf and add nothing: their base is a finite stand-in far below
+// any logit (kEmptyBase), so merging them never lifts the running maximum
+// (which would flush the real partial sum to zero for very negative logits)
+// and never forms -inf - (-inf).
+constexpr float kEmptyBase = -1e30f;
 __device__ __forceinline__ bool fold_chunk(const f32x4 (&acc)[4], float G, int first, LaneDraw& d) {
   float l[kGChunk];
 #pragma unroll
@@ -89,7 +95,7 @@ __device__ __forceinline__ bool fold_chunk(const f32x4 (&acc)[4], float G, int f
   float m = l[0];
 #pragma unroll
   for (int c = 1; c < kGChunk; ++c) m = fmaxf(m, l[c]);
-  const float m2 = (m == neg_inf() ? 0.f : m) * kLog2e;
+  const float m2 = m == neg_inf() ? kEmptyBase : m * kLog2e;
   float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < kGChunk; ++c) s4[c & 3] += __builtin_amdgcn_exp2f(fmaf(l[c], kLog2e, -m2));
@@ -326,11 +332,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
 // needed to publish them; each wave waits for its own atomics to complete
 // before the work group arrives.  The wait is bounded: after kBarrierTicks of
 // the 100 MHz real-time clock the work group raises the time-out flag and
-// the launch ends early (sample_finalize then reports every token as -1), so
-// a grid that is not resident as a whole cannot hang.
+// the launch ends early (sample_finalize then reports every token as -1 and
+// the call's status word, if any, as DSPARK_ETIMEOUT), so a grid that is not
+// resident as a whole cannot hang.  A caller's cancel word, when given and
+// non-zero, ends the wait the same way.
 constexpr unsigned long long kBarrierTicks = 50000000ull;   // 0.5 s
 
-__device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int round, int* flag) {
+__device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int round, int* flag,
+                                             const uint32_t* cancel) {
   __builtin_amdgcn_s_waitcnt(0);   // this wave's key atomics have completed
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -348,7 +357,8 @@ __device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int rou
     int ok = 1;
     while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < round * groups) {
       if (__hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u ||
-          __builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks) {
+          __builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks ||
+          (cancel && __hip_atomic_load(cancel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u)) {
         __hip_atomic_fetch_or(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         ok = 0;
         break;
@@ -382,7 +392,8 @@ template <int RQ, int KS16, bool VEC>
 __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     int R, int gamma, int V, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
-    const float* __restrict__ g, SampleWs ws, int nPart, int kb, int ke, const uint16_t* __restrict__ bvec) {
+    const float* __restrict__ g, SampleWs ws, int nPart, int kb, int ke, const uint16_t* __restrict__ bvec,
+    const uint32_t* __restrict__ cancel) {
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
   constexpr int NROWS = 32 * RQ;
   constexpr int kW = wide_tile_bytes<KS16>();   // tile bytes (padded rows)
@@ -594,7 +605,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     // next position: its in-chunk Gumbels are fetched before the barrier; its
     // logits and first two W2t tiles are already in flight
     gq = load_gq(k + 1);
-    if (!grid_barrier(ws.bar, k + 1, &barflag)) return;
+    if (!grid_barrier(ws.bar, k + 1, &barflag, cancel)) return;
     const unsigned long long* kp = ws.keys + static_cast<int64_t>(k) * kKeySlots * R + reqc;
     unsigned long long best = 0;
 #pragma unroll
@@ -678,10 +689,12 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
                                                        const int32_t* __restrict__ x0, SampleWs ws,
                                                        int nPart, int32_t* __restrict__ x,
                                                        float* __restrict__ lse, float* __restrict__ logit,
-                                                       const typename Elt::T* __restrict__ bvec) {
+                                                       const typename Elt::T* __restrict__ bvec,
+                                                       int32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= static_cast<int64_t>(R) * gamma) return;
+  if (status && row == 0 && lane == 0) *status = ws.bar[1] != 0u ? DSPARK_ETIMEOUT : DSPARK_OK;
   const int req = static_cast<int>(row / gamma);
   const int k = static_cast<int>(row % gamma);
   // the time-out flag, the keys and the partials are loaded together; only
@@ -779,6 +792,7 @@ struct SampleArgs {
   const void *U, *W1, *W2t, *bvec;
   const int32_t* x0;
   const float *G, *g;
+  const uint32_t* cancel;   // nullable: a non-zero word ends the grid-barrier waits
 };
 
 template <int NBW, int KS, bool VEC>
@@ -796,7 +810,43 @@ static void launch_steps_wide(const SampleArgs& a, int kb, int ke, const SampleW
   hipLaunchKernelGGL((sample_steps_wide<RQ, KS16, VEC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R, a.gamma, a.V,
                      static_cast<const uint16_t*>(a.U), static_cast<const uint16_t*>(a.W1),
                      static_cast<const uint16_t*>(a.W2t), a.x0, a.G, a.g, w, gx, kb, ke,
-                     static_cast<const uint16_t*>(a.bvec));
+                     static_cast<const uint16_t*>(a.bvec), a.cancel);
+}
+
+// Whether one work group of the persistent kernel fits on a compute unit
+// (registers, LDS and threads), asked of the runtime once per device: the
+// grid barrier needs the whole grid resident, one work group per compute
+// unit.  When it does not fit, the sampler takes the per-position launches.
+template <int RQ, int KS16, bool VEC>
+static bool wide_fits() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(&sample_steps_wide<RQ, KS16, VEC>), wide_threads<RQ>(), 0);
+    v = (e == hipSuccess && n >= 1) ? 1 : 2;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+template <int KS16>
+static bool wide_fits_ks(int R, int V) {
+  const bool vec = (V % kGChunk) == 0;
+  if (R <= 64) return vec ? wide_fits<2, KS16, true>() : wide_fits<2, KS16, false>();
+  return vec ? wide_fits<4, KS16, true>() : wide_fits<4, KS16, false>();
+}
+
+static bool wide_fits_r(int R, int V, int r) {
+  switch (r / 32) {
+    case 1: return wide_fits_ks<2>(R, V);
+    case 2: return wide_fits_ks<4>(R, V);
+    case 4: return wide_fits_ks<8>(R, V);
+    default: return wide_fits_ks<16>(R, V);
+  }
 }
 
 template <int KS16>
@@ -833,10 +883,10 @@ hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, 
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                         hipStream_t s, const RnnHead* rnn) {
+                         hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status) {
   const SampleWs w = carve(ws, R, gamma);
-  const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g};
-  const int gxw = dt == DSPARK_BF16 ? wide_grid_x(R, V) : 0;
+  const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g, cancel};
+  const int gxw = dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
   const int nPart = gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
   const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
   hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys, 256) < 1024 ? ceil_div(nkeys, 256) : 1024),
@@ -880,12 +930,12 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
     hipLaunchKernelGGL(sample_finalize<BF16>, dim3(blocks), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
                        static_cast<const uint16_t*>(W2t), x0, w, nPart, x, lse, logit,
-                       static_cast<const uint16_t*>(a.bvec));
+                       static_cast<const uint16_t*>(a.bvec), status);
   else
     hipLaunchKernelGGL(sample_finalize<F32>, dim3(blocks), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const float*>(U), static_cast<const float*>(W1),
                        static_cast<const float*>(W2t), x0, w, nPart, x, lse, logit,
-                       static_cast<const float*>(a.bvec));
+                       static_cast<const float*>(a.bvec), status);
   return hipGetLastError();
 }
 

@@ -48,6 +48,13 @@ SMALL = [
     # 18752 chunk masses per request: more than the residual draw keeps in
     # registers, so it scans them from memory
     W.custom("bigv_r3_g2_v300000_bf16", R=3, gamma=2, V=300000, r=32, d=64, seed=62),
+    # the instantiations the benchmark runs, on every request: 128-request
+    # groups with r = 256 (sampler and residual sweep at 4 request quarters and
+    # 16 k-steps), with V a multiple of 16 (16-byte logit loads) and not
+    # (token-by-token loads), and two request groups side by side
+    W.custom("wide_r130_g4_v4096_r256_bf16", R=130, gamma=4, V=4096, r=256, d=128, seed=18),
+    W.custom("wide_r130_g4_v4100_r256_bf16", R=130, gamma=4, V=4100, r=256, d=128, seed=19),
+    W.custom("wide_r256_g3_v2048_r256_bf16", R=256, gamma=3, V=2048, r=256, d=64, seed=20, temperatures=True),
 ]
 
 
@@ -128,6 +135,83 @@ def test_many_requests_sampled_parity(w, dev):
     assert np.all(np.isfinite(out["lse"])) and np.all(np.isfinite(out["logit"]))
     assert np.all((out["n_acc"] >= 0) & (out["n_acc"] <= ell))
     assert np.all((out["next_tok"] >= 0) & (out["next_tok"] < w.V))
+
+
+@pytest.mark.parametrize("R", [20, 100])
+def test_very_negative_logits_with_a_phantom_tile(R, dev):
+    """Logits near -200 (U shifted by -200) and an odd tile count (V = 700:
+    11 tiles of 64, so one work group also sweeps a phantom tile past V whose
+    chunks hold no logit).  Folding an empty chunk must not lift the running
+    maximum: with every real logit below about -87 that would flush the
+    work group's partial sum to zero and corrupt lse."""
+    w = W.custom(f"neg200_r{R}_g3_v700_r256_bf16", R=R, gamma=3, V=700, r=256, d=64, seed=22)
+    say(f"[parity] {w.name}")
+    inp = W.make_inputs(w)
+    inp.U = W.bf16_bits(W.bf16_to_f32(inp.U) - np.float32(200.0))
+    _, out = run_gpu(inp, dev)
+    idx = np.arange(w.R)
+    rs = check_sample(inp, out, idx)
+    rv = check_verify(inp, out, idx)
+    say(f"  sample {rs}\n  verify {rv}")
+    assert np.all(out["lse"] < -150.0)
+
+
+def test_free_running_round_equals_oracle_round(dev):
+    """The whole round on the GPU, free running (no teacher forcing), equals
+    the oracle's run_round token for token on the tiny fp32 workload: the
+    drafted tokens, the admitted lengths, A, the accepted lengths and the
+    next tokens; lse, logit, c and Theta_best within the parity tolerances."""
+    from oracle.round import run_round as oracle_round
+    w = W.BY_NAME["tiny_r1_g4_v1024_f32"]
+    say(f"[parity] free-running round {w.name}")
+    for rnd in range(3):
+        inp = W.make_inputs(w, round_index=rnd)
+        _, out = run_gpu(inp, dev)
+        ref = oracle_round(inp)
+        assert out["x"].tolist() == ref["x"].tolist(), rnd
+        assert out["ell"].tolist() == ref["ell"].tolist(), rnd
+        assert out["A"] == ref["A"], rnd
+        # Theta_best is bit-exact given the same confidences (checked next);
+        # the oracle's free-running c comes from its own float64 dot products,
+        # which round to fp32 differently from the GPU's in the last place
+        check_schedule(inp.sps, out)
+        assert out["theta_best"] == pytest.approx(ref["theta_best"], rel=1e-6), rnd
+        assert out["n_acc"].tolist() == ref["n_acc"].tolist(), rnd
+        assert out["next_tok"].tolist() == ref["next_tok"].tolist(), rnd
+        np.testing.assert_allclose(out["lse"], ref["lse"], rtol=1e-5)
+        np.testing.assert_allclose(out["logit"], ref["logit"], rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(out["c"], ref["c"], rtol=1e-5)
+
+
+def test_cancelled_sampler_reports_time_out(dev):
+    """dspark_markov_sample_ex with its cancel word set: the persistent
+    launch's grid-barrier waits give up at once (every work group exits
+    normally), the status word reads DSPARK_ETIMEOUT and every token is the
+    -1 sentinel with NaN lse and logit.  With the word cleared, the same call
+    matches dspark_markov_sample followed by dspark_confidence bit for bit."""
+    from semi_ar_draft_round_amd import binding as B
+    from semi_ar_draft_round_amd import device_round as DR
+    w = W.custom("cancel_r24_g4_v1500", R=24, gamma=4, V=1500, r=256, d=128, seed=43, temperatures=True)
+    inp = W.make_inputs(w)
+    say(f"[parity] {w.name}")
+    d = DR.to_device(inp, dev)
+    cancel = torch.ones(1, dtype=torch.int32, device=dev)
+    status = torch.full((1,), -9, dtype=torch.int32, device=dev)
+    x, lse, logit, c, z, st = B.dspark_markov_sample_ex(d.U, d.W1, d.W2t, d.x0, d.G, d.g, h=d.h, w=d.w, T=d.T,
+                                                        z=torch.empty_like(d.z), cancel=cancel, status=status)
+    torch.cuda.synchronize()
+    assert int(st.cpu()[0]) == 6
+    assert np.all(x.cpu().numpy() == -1)
+    assert np.all(np.isnan(lse.cpu().numpy())) and np.all(np.isnan(logit.cpu().numpy()))
+    cancel.zero_()
+    x, lse, logit, c, z, st = B.dspark_markov_sample_ex(d.U, d.W1, d.W2t, d.x0, d.G, d.g, h=d.h, w=d.w, T=d.T,
+                                                        z=torch.empty_like(d.z), cancel=cancel, status=status)
+    DR.sample(d)
+    DR.confidence(d)
+    torch.cuda.synchronize()
+    assert int(st.cpu()[0]) == 0
+    for a, b in ((x, d.x), (lse, d.lse), (logit, d.logit), (c, d.c), (z, d.z)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
 def test_all_accepted_at_max_gamma(dev):
