@@ -15,6 +15,7 @@
  *   dspark_confidence     the confidence head (linear + sigmoid, temperature)
  *   dspark_schedule       the batched prefix scheduler (Algorithm 1)
  *   dspark_schedule_ex    the same with the production admission rules
+ *   dspark_schedule_noalloc  the same without a workspace (static scratch)
  *   dspark_verify         rejection-sampling verification + residual draw
  *   dspark_verify_ex      the same with the RNN head's bias vectors
  *   dspark_verify_greedy  temperature-0 (exact-match) verification
@@ -295,6 +296,27 @@ typedef enum {
 dspark_status dspark_schedule_ex(int R, int gamma, const float* c, const double* sps, int n_sps,
                                  int mode, const int32_t* cap, int32_t* ell, int32_t* admitted,
                                  double* theta_best, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dspark_schedule_noalloc — dspark_schedule_ex without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture
+ * that may not call hipMalloc, tight serving loops, and harnesses that
+ * forbid allocation.  The ranked slot keys live in a static device array of
+ * the library instead: 8192 slots (64 KiB) on each device the library runs
+ * on, held until the process ends.  Every call on one device shares that
+ * array, so calls that overlap on one device race and must be serialised by
+ * the caller (one stream, or events).  Every key is rewritten before it is
+ * read, so no clearing is needed between calls.  The call itself allocates
+ * nothing (the array's address is looked up once per device).
+ *
+ *   every argument as in dspark_schedule_ex, without ws and ws_bytes
+ *
+ * Limits: as dspark_schedule_ex, and R * gamma <= 8192 (implied by
+ * R * (1 + gamma) <= 8191); larger batches return DSPARK_EINVAL.
+ */
+dspark_status dspark_schedule_noalloc(int R, int gamma, const float* c, const double* sps, int n_sps,
+                                      int mode, const int32_t* cap, int32_t* ell, int32_t* admitted,
+                                      double* theta_best, void* stream);
 
 /*
  * dspark_verify — lossless rejection-sampling verification.

@@ -35,6 +35,7 @@ _SIGNATURES = {
     "dspark_confidence": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "dspark_schedule": [_I, _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P],
     "dspark_schedule_ex": [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
+    "dspark_schedule_noalloc": [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P],
     "dspark_verify": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                       _P, _SZ, _P],
     "dspark_verify_greedy": [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -273,6 +274,27 @@ def dspark_schedule_ex(c, sps, mode, cap=None, ell=None, admitted=None, theta_be
     st = lib.dspark_schedule_ex(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), int(mode), _ptr(cap), _ptr(ell),
                                 _ptr(admitted), _ptr(theta_best), _ptr(ws), ws.numel(), _stream())
     _raise("dspark_schedule_ex", st)
+    return ell, admitted, theta_best
+
+
+def dspark_schedule_noalloc(c, sps, mode, cap=None, ell=None, admitted=None, theta_best=None):
+    """dspark_schedule_ex with the library's static device scratch instead of
+    a workspace (for callers that cannot allocate).  Calls on one device must
+    not overlap.  Returns ell [R] int32, admitted [1] int32, theta_best [1]
+    float64."""
+    lib = load_library()
+    R, gamma = c.shape
+    dev = c.device
+    _check(c, "c", (R, gamma), (torch.float32,), dev)
+    _check(sps, "sps", (sps.shape[0],), (torch.float64,), dev)
+    if cap is not None:
+        _check(cap, "cap", (1,), (torch.int32,), dev)
+    ell = torch.empty(R, dtype=torch.int32, device=dev) if ell is None else ell
+    admitted = torch.empty(1, dtype=torch.int32, device=dev) if admitted is None else admitted
+    theta_best = torch.empty(1, dtype=torch.float64, device=dev) if theta_best is None else theta_best
+    st = lib.dspark_schedule_noalloc(R, gamma, _ptr(c), _ptr(sps), int(sps.shape[0]), int(mode), _ptr(cap),
+                                     _ptr(ell), _ptr(admitted), _ptr(theta_best), _stream())
+    _raise("dspark_schedule_noalloc", st)
     return ell, admitted, theta_best
 
 

@@ -29,6 +29,9 @@ hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, in
 size_t schedule_workspace_bytes(int R, int gamma);
 hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
                            int32_t* ell, int32_t* admitted, double* theta_best, void* ws, hipStream_t s);
+int schedule_static_slots();
+hipError_t schedule_launch_static(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
+                                  int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s);
 // verify.hip
 size_t verify_greedy_workspace_bytes(int R, int gamma);
 size_t acceptance_workspace_bytes(int R, int gamma, int V);
@@ -221,6 +224,25 @@ dspark_status dspark_schedule_ex(int R, int gamma, const float* c, const double*
   if (st != DSPARK_OK) return st;
   if (schedule_launch(R, gamma, c, sps, mode, cap, ell, admitted, theta_best, ws, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_schedule_noalloc(int R, int gamma, const float* c, const double* sps, int n_sps, int mode,
+                                      const int32_t* cap, int32_t* ell, int32_t* admitted, double* theta_best,
+                                      void* stream) {
+  if (R < 1 || gamma < 1 || gamma > kMaxGamma) return DSPARK_EINVAL;
+  if (static_cast<int64_t>(R) * (1 + gamma) > kMaxSchedSlots) return DSPARK_EINVAL;
+  if (static_cast<int64_t>(R) * gamma > schedule_static_slots()) return DSPARK_EINVAL;
+  if (n_sps < R * (1 + gamma)) return DSPARK_EINVAL;
+  if (!c || !sps || !ell) return DSPARK_EINVAL;
+  if (mode != DSPARK_SCHED_EARLY_STOP && mode != DSPARK_SCHED_WHOLE_WALK && mode != DSPARK_SCHED_CAPACITY)
+    return DSPARK_EINVAL;
+  if (mode == DSPARK_SCHED_CAPACITY && !cap) return DSPARK_EINVAL;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (schedule_launch_static(R, gamma, c, sps, mode, cap, ell, admitted, theta_best,
+                             static_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

@@ -36,6 +36,9 @@
 // in which threads add things up.
 #include "common.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace dspark {
 
 constexpr int kSchedThreads = 1024;
@@ -349,6 +352,49 @@ hipError_t schedule_launch(int R, int gamma, const float* c, const double* sps, 
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, R, gamma, sps, mode, cap, ranked, ell,
                      admitted, theta_best);
   return hipGetLastError();
+}
+
+// The allocation-free variant's scratch: the ranked slot keys in a static
+// device array instead of a caller workspace.  Every slot key is written by
+// schedule_rank before schedule_kernel reads it, so nothing needs clearing.
+// Each device holds its own copy until the process ends; host code reaches
+// it only through the address hipGetSymbolAddress returns for the current
+// device (the array's name is a host-side stand-in, not a device address).
+constexpr int kStaticSlots = 8192;
+static __device__ __align__(256) uint64_t scratch[kStaticSlots];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<uint64_t*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// The scratch array's address on the current device, looked up once per
+// device (nullptr on failure).
+static uint64_t* schedule_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uint64_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    p = static_cast<uint64_t*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+int schedule_static_slots() { return kStaticSlots; }
+
+hipError_t schedule_launch_static(int R, int gamma, const float* c, const double* sps, int mode, const int32_t* cap,
+                                  int32_t* ell, int32_t* admitted, double* theta_best, hipStream_t s) {
+  if (static_cast<int64_t>(R) * gamma > kStaticSlots) return hipErrorInvalidValue;
+  uint64_t* p = schedule_scratch();
+  if (!p) return hipErrorInvalidSymbol;
+  return schedule_launch(R, gamma, c, sps, mode, cap, ell, admitted, theta_best, p, s);
 }
 
 }  // namespace dspark

@@ -215,3 +215,14 @@ def test_sample_ex_rejects_bad_arguments(lib):
     assert call(ws=None) == EWORKSPACE
     # without the confidence head its arguments are ignored
     assert call(h=None, w=None, c=None, d=0, ws=None) == EWORKSPACE
+
+
+def test_schedule_noalloc_rejects_bad_arguments(lib):
+    def call(R=4, gamma=3, n_sps=16, mode=0, cap=FAKE, ptr=FAKE):
+        return lib.dspark_schedule_noalloc(R, gamma, ptr, ptr, n_sps, mode, cap, ptr, None, None, None)
+    assert call(mode=3) == EINVAL
+    assert call(mode=2, cap=None) == EINVAL
+    assert call(n_sps=15) == EINVAL
+    assert call(R=482, gamma=16, n_sps=10000) == EINVAL   # beyond the static scratch
+    assert call(R=0) == EINVAL
+    assert call(ptr=None) == EINVAL
