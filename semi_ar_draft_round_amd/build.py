@@ -2,8 +2,9 @@
 
     python -m semi_ar_draft_round_amd.build
 
-Compiles every csrc/*.hip with hipcc into one shared library next to this
-file.  No GPU is needed: hipcc cross-compiles for gfx950.
+Compiles every csrc/*.hip with hipcc (one object per source, in parallel)
+and links them into one shared library next to this file.  No GPU is
+needed: hipcc cross-compiles for gfx950.
 """
 
 from __future__ import annotations
@@ -36,10 +37,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", "-o", tmp, *sources]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,8 +48,27 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+
+
+def build(verbose: bool = False, csrc: str = CSRC, out: str = LIB) -> str:
+    """Compile every source of `csrc` to an object (in parallel), then link
+    the shared library `out`."""
+    import concurrent.futures
+    import tempfile
+    sources = sorted(glob.glob(os.path.join(csrc, "*.hip")))
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="dspark_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in sources]
+        jobs = min(len(sources), max(1, min(16, os.cpu_count() or 1)))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            futs = [ex.submit(_run, [hipcc(), *compile_flags, f"-I{INCLUDE}", "-c", "-o", obj, src], verbose)
+                    for src, obj in zip(sources, objs)]
+            for f in futs:
+                f.result()
+        tmp = out + ".tmp"
+        _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+        os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

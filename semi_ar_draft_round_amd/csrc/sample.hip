@@ -24,6 +24,7 @@
 #include "wide_tile.hpp"
 #include "sample_keys.hpp"
 #include "rnn_head.hpp"
+#include "sample_common.hpp"
 
 #include <atomic>
 
@@ -36,15 +37,6 @@ constexpr int kMaxSampleWGs = 1024;
 template <int NBW>
 __host__ __device__ constexpr int sample_reqs_per_wg() { return kTileWaves * 16 * NBW; }
 
-struct SampleWs {
-  unsigned long long* keys;   // [gamma][kKeySlots][R]
-  unsigned int* bar;          // [0]: grid-barrier arrivals, [1]: barrier time-out flag
-  float2* lsep;               // [gamma][R][nPart]  (M, S) log-sum-exp partials
-};
-// 64-bit words after the keys that sample_init also clears (the barrier words:
-// the top counter and time-out flag, then kBarGroups group counters 128 bytes apart)
-constexpr int kBarWords = 256;
-constexpr int kBarGroups = 8;
 
 __global__ __launch_bounds__(256) void sample_init(unsigned long long* keys, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
@@ -52,8 +44,6 @@ __global__ __launch_bounds__(256) void sample_init(unsigned long long* keys, int
     keys[i] = 0ull;
 }
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 // MFMA C operand of M-block mb: the lane's tokens 4 mb .. 4 mb + 3 as fp32.
 __device__ __forceinline__ f32x4 lane16_c(const u32x4 (&u)[2], int mb) {
@@ -63,52 +53,6 @@ __device__ __forceinline__ f32x4 lane16_c(const u32x4 (&u)[2], int mb) {
                __uint_as_float(w1 & 0xFFFF0000u)};
 }
 
-// Running state of one lane for one request: the log-sum-exp of every chunk
-// it has folded (T * 2^M2, base 2) and the best chunk so far under the
-// chunk-level Gumbel-max (score log2(e) * (LSE_c + G_c) and its first token).
-// The best chunk's sixteen logits, needed for the in-chunk draw at the end,
-// are kept in LDS (`keep`, four f32x4 at a stride of kTileThreads).
-struct LaneDraw {
-  float M2, T;
-  float best;
-  int first;
-};
-
-__device__ __forceinline__ void lane_draw_init(LaneDraw& d) {
-  d.M2 = neg_inf();
-  d.T = 0.f;
-  d.best = neg_inf();
-  d.first = -1;
-}
-
-// Fold one Gumbel chunk (the lane's sixteen logits l, first token `first`,
-// chunk Gumbel G) into the lane's state.  Chunks with no finite logit get a
-// score of -inf and add nothing: their base is a finite stand-in far below
-// any logit (kEmptyBase), so merging them never lifts the running maximum
-// (which would flush the real partial sum to zero for very negative logits)
-// and never forms -inf - (-inf).
-constexpr float kEmptyBase = -1e30f;
-__device__ __forceinline__ bool fold_chunk(const f32x4 (&acc)[4], float G, int first, LaneDraw& d) {
-  float l[kGChunk];
-#pragma unroll
-  for (int c = 0; c < kGChunk; ++c) l[c] = acc[c >> 2][c & 3];
-  float m = l[0];
-#pragma unroll
-  for (int c = 1; c < kGChunk; ++c) m = fmaxf(m, l[c]);
-  const float m2 = m == neg_inf() ? kEmptyBase : m * kLog2e;
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < kGChunk; ++c) s4[c & 3] += __builtin_amdgcn_exp2f(fmaf(l[c], kLog2e, -m2));
-  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  const float score = fmaf(G, kLog2e, m2 + __builtin_amdgcn_logf(s));
-  const float Mn = fmaxf(d.M2, m2);
-  d.T = d.T * __builtin_amdgcn_exp2f(d.M2 - Mn) + s * __builtin_amdgcn_exp2f(m2 - Mn);
-  d.M2 = Mn;
-  const bool take = score > d.best;   // strict: the earlier chunk keeps ties
-  d.best = take ? score : d.best;
-  d.first = take ? first : d.first;
-  return take;
-}
 
 // Per-chunk loads that each lane makes for itself: its sixteen logits and
 // its chunk Gumbel, for every request group.
@@ -336,7 +280,6 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
 // the call's status word, if any, as DSPARK_ETIMEOUT), so a grid that is not
 // resident as a whole cannot hang.  A caller's cancel word, when given and
 // non-zero, ends the wait the same way.
-constexpr unsigned long long kBarrierTicks = 50000000ull;   // 0.5 s
 
 __device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int round, int* flag,
                                              const uint32_t* cancel) {

@@ -1,0 +1,77 @@
+// Pieces shared by the sampling kernels: the workspace layout (argmax key
+// slots, grid-barrier words, log-sum-exp partials), the grid barrier's time
+// bound and the per-lane fold of one 16-token Gumbel chunk.
+#pragma once
+
+#include "common.hpp"
+#include "sample_keys.hpp"
+
+namespace dspark {
+
+struct SampleWs {
+  unsigned long long* keys;   // [gamma][kKeySlots][R]
+  unsigned int* bar;          // barrier words (below)
+  float2* lsep;               // [gamma][R][nPart]  (M, S) log-sum-exp partials
+};
+
+// Barrier words (32-bit), cleared on every call: bar[0] is the top counter
+// of the persistent kernel's grid barrier and bar[1] its time-out flag; the
+// group counters sit at bar[64 + 32 g], 128 bytes apart.
+constexpr int kBarGroups = 8;              // arrival groups of the two-level barrier
+constexpr int kBarWords = 256;             // as 64-bit words
+
+// The wait at a grid barrier is bounded: after this many ticks of the 100 MHz
+// real-time clock a work group gives up (0.5 s).
+constexpr unsigned long long kBarrierTicks = 50000000ull;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Running state of one lane for one request: the log-sum-exp of every chunk
+// it has folded (T * 2^M2, base 2) and the best chunk so far under the
+// chunk-level Gumbel-max (score log2(e) * (LSE_c + G_c) and its first token).
+// The best chunk's sixteen logits, needed for the in-chunk draw at the end,
+// are kept in LDS (`keep`, four f32x4 at a stride of kTileThreads).
+struct LaneDraw {
+  float M2, T;
+  float best;
+  int first;
+};
+
+__device__ __forceinline__ void lane_draw_init(LaneDraw& d) {
+  d.M2 = neg_inf();
+  d.T = 0.f;
+  d.best = neg_inf();
+  d.first = -1;
+}
+
+// Fold one Gumbel chunk (the lane's sixteen logits l, first token `first`,
+// chunk Gumbel G) into the lane's state.  Chunks with no finite logit get a
+// score of -inf and add nothing: their base is a finite stand-in far below
+// any logit (kEmptyBase), so merging them never lifts the running maximum
+// (which would flush the real partial sum to zero for very negative logits)
+// and never forms -inf - (-inf).
+constexpr float kEmptyBase = -1e30f;
+__device__ __forceinline__ bool fold_chunk(const f32x4 (&acc)[4], float G, int first, LaneDraw& d) {
+  float l[kGChunk];
+#pragma unroll
+  for (int c = 0; c < kGChunk; ++c) l[c] = acc[c >> 2][c & 3];
+  float m = l[0];
+#pragma unroll
+  for (int c = 1; c < kGChunk; ++c) m = fmaxf(m, l[c]);
+  const float m2 = m == neg_inf() ? kEmptyBase : m * kLog2e;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kGChunk; ++c) s4[c & 3] += __builtin_amdgcn_exp2f(fmaf(l[c], kLog2e, -m2));
+  const float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  const float score = fmaf(G, kLog2e, m2 + __builtin_amdgcn_logf(s));
+  const float Mn = fmaxf(d.M2, m2);
+  d.T = d.T * __builtin_amdgcn_exp2f(d.M2 - Mn) + s * __builtin_amdgcn_exp2f(m2 - Mn);
+  d.M2 = Mn;
+  const bool take = score > d.best;   // strict: the earlier chunk keeps ties
+  d.best = take ? score : d.best;
+  d.first = take ? first : d.first;
+  return take;
+}
+
+}  // namespace dspark

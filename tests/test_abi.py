@@ -58,8 +58,8 @@ def test_workspace_sizes(lib):
     n_c = (129280 + 63) // 64
     ws = B.dspark_workspace_size(B.WS_SAMPLE, 128, 16, 129280, 256)
     # argmax keys (4 slots per request and position) and 256 barrier words,
-    # then one (max, sum) pair per
-    # chunk, request and position (the fp32 path's bound)
+    # then one (max, sum) pair per chunk, request and position (the fp32
+    # path's bound)
     assert ws == 8 * (4 * 128 * 16 + 256) + 16 * 128 * n_c * 8
     assert B.dspark_workspace_size(B.WS_VERIFY, 128, 16, 129280, 256) >= 4 * 128 * (2 * n_c + 33)
     assert B.dspark_workspace_size(B.WS_SAMPLE, 0, 16, 129280, 256) == 0
