@@ -1,5 +1,6 @@
-"""Benchmark: one DSpark draft-and-verify round (sample -> confidence ->
-schedule -> verify) on one MI355X, as drafted tokens per second.
+"""Benchmark: one DSpark draft-and-verify round (the draft with its
+confidences -> schedule -> verify) on one MI355X, as drafted tokens per
+second.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -44,8 +45,15 @@ def source_hash() -> str:
 
 def sample_bytes_per_position(w) -> int:
     """Algorithmic HBM bytes of one sampling position: the U_k slice of every
-    request, the whole W2t (bias GEMM operand) and the chunk Gumbels."""
-    return w.R * w.V * 2 + w.r * w.V * 2 + w.R * w.n_chunks * 4
+    request and the whole W2t (the bias product's operand).  The chunk
+    Gumbels, which a counter-based generator would make in registers, are
+    not counted (noise_bytes_per_position)."""
+    return w.R * w.V * 2 + w.r * w.V * 2
+
+
+def noise_bytes_per_position(w) -> int:
+    """HBM bytes of one position's chunk Gumbels as this harness stores them."""
+    return w.R * w.n_chunks * 4
 
 
 def _oracle_rounds(inps, n_req: int, min_seconds: float, max_rounds: int):
@@ -179,8 +187,8 @@ def main():
         return g
 
     graphs = {name: [capture(fn, d) for d in rounds]
-              for name, fn in (("round", DR.run_round), ("sample", DR.sample),
-                               ("confidence", DR.confidence), ("schedule", DR.schedule),
+              for name, fn in (("round", DR.run_round), ("sample_conf", DR.sample_conf),
+                               ("sample", DR.sample), ("confidence", DR.confidence), ("schedule", DR.schedule),
                                ("verify", DR.verify), ("schedule_production", DR.schedule_production),
                                ("verify_greedy", DR.verify_greedy), ("acceptance", DR.acceptance),
                                ("rnn_sample", DR.rnn_sample))}
@@ -224,19 +232,35 @@ def main():
     singles = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
     spread = [round(float(np.percentile(singles, q)), 1) for q in (10, 50, 90)]
     log(f"[bench] single rounds p10/p50/p90: {spread} us")
+    # the round's three calls, each replayed on its own
     parts = {}
-    for name in ("sample", "confidence", "schedule", "verify"):
+    for name in ("sample_conf", "schedule", "verify"):
         parts[name] = timed(name, max(args.steps, 10), 2) * 1e3
         log(f"[bench] {name}: {parts[name]:.1f} us")
-    # the production (asynchronous) scheduler's two calls, timed on their
-    # own: not part of the round above, which runs Algorithm 1
+    # the persistent sampling launch alone: eager rounds (the same calls as
+    # the graph, the same alternation of input sets), with the sampling call
+    # stamping two HIP events with that launch's start and end on its stream
+    timer = binding.SweepTimer()
+    sweeps = []
+    for i in range(max(args.steps, 10) + 2):
+        d = rounds[i % 2]
+        DR.sample_conf(d, timer=timer)
+        DR.schedule(d)
+        DR.verify(d)
+        if i >= 2:
+            sweeps.append(timer.elapsed_ms() * 1e3)
+    torch.cuda.synchronize()
+    sweep_us = float(np.mean(sweeps))
+    log(f"[bench] sample_steps_wide launch: mean {sweep_us:.1f} us over {len(sweeps)} eager rounds "
+        f"(min {min(sweeps):.1f}, max {max(sweeps):.1f})")
     # the other modes, each timed on its own and outside the round: the
+    # sampling call without and the confidence head as a call of its own, the
     # production (asynchronous) scheduler's two calls, greedy verification of
     # the round's drafts, the analytic acceptance of all its positions, the
     # draft with the RNN head, and the calibration fit
     modes = {}
-    for name in () if args.no_modes else ("schedule_production", "verify_greedy", "acceptance", "rnn_sample",
-                                          "sts_fit"):
+    for name in () if args.no_modes else ("sample", "confidence", "schedule_production", "verify_greedy",
+                                          "acceptance", "rnn_sample", "sts_fit"):
         modes[name] = timed(name, max(args.steps, 10), 2) * 1e3
         log(f"[bench] {name}: {modes[name]:.1f} us")
 
@@ -245,19 +269,22 @@ def main():
     out = DR.outputs_to_host(rounds[0])
     value = w.R * w.gamma / (ms * 1e-3)
 
-    # The sampling call is one persistent launch over all gamma positions plus
-    # two small kernels (key clear, finalize); the call time stands in for the
-    # launch duration (a few percent high, so `achieved` is a lower bound).
-    launch_us = parts["sample"]
+    # The dominant kernel is the persistent sampling launch over all gamma
+    # positions.  Its algorithmic bytes: gamma x (U_k of every request + W2t).
     bytes_launch = sample_bytes_per_position(w) * w.gamma
     # the on-chip-reuse floor: W2 read once per launch instead of once per position
     bytes_model_b = bytes_launch - (w.gamma - 1) * w.r * w.V * 2
-    achieved = bytes_launch / (launch_us * 1e-6) / 1e9
+    achieved = bytes_launch / (sweep_us * 1e-6) / 1e9
+    traffic = traffic_record(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_record(w.name),
-                "kernel": "sample_steps_wide (all gamma positions in one launch; timed as the sampling call)",
-                "bytes_per_launch": bytes_launch, "us_per_launch": round(launch_us, 2),
-                "bytes_per_launch_w2_once": bytes_model_b}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "sample_steps_wide (all gamma positions in one launch)",
+                "bytes_per_launch": bytes_launch, "us_per_launch": round(sweep_us, 2),
+                "noise_bytes_per_launch": noise_bytes_per_position(w) * w.gamma,
+                "bytes_per_launch_w2_once": bytes_model_b,
+                "frac_w2_once": round(bytes_model_b / (sweep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "frac_traffic": None if traffic is None else
+                round(traffic / (sweep_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

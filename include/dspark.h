@@ -160,6 +160,12 @@ dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int
  *   status [1] i32 device word out, or NULL: DSPARK_OK, or DSPARK_ETIMEOUT
  *          when the grid barrier gave up (x = -1, lse and logit NaN; c and z
  *          are then computed on no token, x0 for the first position).
+ *   events [2] hipEvent_t (host array of two events the caller created with
+ *          timing enabled) or NULL.  The position sweep's start and end are
+ *          recorded on them: the persistent launch's own start and end, or,
+ *          on the per-position paths, around all position launches.  The
+ *          key clear and the finalize step (the draws' read-out and the
+ *          confidence head) are outside.  Not for use under graph capture.
  *
  * Limits: as dspark_markov_sample, and as dspark_confidence when h is given.
  */
@@ -168,7 +174,7 @@ dspark_status dspark_markov_sample_ex(dspark_dtype dt, int R, int gamma, int V, 
                                       const int32_t* x0, const float* G, const float* g,
                                       const void* h, const void* w, const float* T,
                                       int32_t* x, float* lse, float* logit, float* c, float* z,
-                                      const uint32_t* cancel, int32_t* status,
+                                      const uint32_t* cancel, int32_t* status, void* const* events,
                                       void* ws, size_t ws_bytes, void* stream);
 
 /*

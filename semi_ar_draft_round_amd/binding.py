@@ -31,7 +31,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "dspark_markov_sample": [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_markov_sample_ex": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                _P, _P, _P, _SZ, _P],
+                                _P, _P, _P, _P, _SZ, _P],
     "dspark_confidence": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "dspark_schedule": [_I, _I, _P, _P, _I, _P, _P, _P, _P, _SZ, _P],
     "dspark_schedule_ex": [_I, _I, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
@@ -165,12 +165,13 @@ def dspark_markov_sample(U, W1, W2t, x0, G, g, x=None, lse=None, logit=None, ws=
 
 
 def dspark_markov_sample_ex(U, W1, W2t, x0, G, g, h=None, w=None, T=None, x=None, lse=None, logit=None,
-                            c=None, z=None, cancel=None, status=None, ws=None):
+                            c=None, z=None, cancel=None, status=None, ws=None, timer=None):
     """dspark_markov_sample plus, when h and w are given, the confidence head
     on the drafted tokens.  cancel: an optional uint32/int32 [1] device word
     (non-zero ends the grid-barrier waits); status: an int32 [1] device word
-    out (0 = ok, 6 = the grid barrier gave up).  Returns x, lse, logit, c, z,
-    status (c and z None without h)."""
+    out (0 = ok, 6 = the grid barrier gave up); timer: a SweepTimer whose
+    events record the position sweep.  Returns x, lse, logit, c, z, status
+    (c and z None without h)."""
     lib = load_library()
     R, gamma, V = U.shape
     r = W1.shape[1]
@@ -208,9 +209,46 @@ def dspark_markov_sample_ex(U, W1, W2t, x0, G, g, h=None, w=None, T=None, x=None
     ws = workspace(WS_SAMPLE, R, gamma, V, r, dev) if ws is None else ws
     st = lib.dspark_markov_sample_ex(_dt(U), R, gamma, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(x0), _ptr(G),
                                      _ptr(g), _ptr(h), _ptr(w), _ptr(T), _ptr(x), _ptr(lse), _ptr(logit), _ptr(c),
-                                     _ptr(z), _ptr(cancel), _ptr(status), _ptr(ws), ws.numel(), _stream())
+                                     _ptr(z), _ptr(cancel), _ptr(status), None if timer is None else timer.pair,
+                                     _ptr(ws), ws.numel(), _stream())
     _raise("dspark_markov_sample_ex", st)
     return x, lse, logit, c, z, status
+
+
+class SweepTimer:
+    """Two HIP events with timing enabled, made by the HIP runtime this
+    process already has loaded, for dspark_markov_sample_ex's `events`."""
+
+    def __init__(self):
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.pair = (ctypes.c_void_p * 2)()
+        for i in range(2):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.pair[i] = ev.value
+
+    def elapsed_ms(self) -> float:
+        """Milliseconds between the two events of the last call (waits for it)."""
+        if self._hip.hipEventSynchronize(self.pair[1]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.pair[0], self.pair[1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            for i in range(2):
+                if self.pair[i]:
+                    self._hip.hipEventDestroy(self.pair[i])
+        except Exception:
+            pass
 
 
 def dspark_confidence(h, w, W1, x0, x, T=None, c=None, z=None, want_z=True):

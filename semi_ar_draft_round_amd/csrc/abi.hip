@@ -7,6 +7,7 @@
 
 #include "common.hpp"
 #include "rnn_head.hpp"
+#include "sample_common.hpp"
 
 namespace dspark {
 // sample.hip
@@ -20,7 +21,8 @@ hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, co
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                         hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status);
+                         hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status,
+                         const SampleConf* conf, hipEvent_t ev0, hipEvent_t ev1);
 // confidence.hip
 hipError_t confidence_launch(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
                              const void* w, const void* W1, const int32_t* x0, const int32_t* x,
@@ -163,7 +165,8 @@ dspark_status dspark_markov_sample_ex(dspark_dtype dt, int R, int gamma, int V, 
                                       const void* W1, const void* W2t, const int32_t* x0, const float* G,
                                       const float* g, const void* h, const void* w, const float* T, int32_t* x,
                                       float* lse, float* logit, float* c, float* z, const uint32_t* cancel,
-                                      int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+                                      int32_t* status, void* const* events, void* ws, size_t ws_bytes,
+                                      void* stream) {
   if (!dtype_ok(dt)) return DSPARK_EDTYPE;
   if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
   if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
@@ -173,14 +176,16 @@ dspark_status dspark_markov_sample_ex(dspark_dtype dt, int R, int gamma, int V, 
     const int vec = (dt == DSPARK_BF16) ? 8 : 4;
     if (!w || !c || d < 1 || d % vec != 0 || r % vec != 0) return DSPARK_EINVAL;
   }
+  if (events && (!events[0] || !events[1])) return DSPARK_EINVAL;
   if (!ws || ws_bytes < sample_workspace_bytes(dt, R, gamma, V)) return DSPARK_EWORKSPACE;
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, s, nullptr, cancel, status) !=
-      hipSuccess)
-    return DSPARK_ELAUNCH;
-  if (conf && confidence_launch(dt, R, gamma, d, r, V, h, w, W1, x0, x, T, c, z, s) != hipSuccess)
+  const SampleConf cf{h, w, d, T, c, z};
+  const hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
+  const hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+  if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, s, nullptr, cancel, status,
+                    conf ? &cf : nullptr, e0, e1) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }
@@ -190,7 +195,7 @@ dspark_status dspark_markov_sample(dspark_dtype dt, int R, int gamma, int V, int
                                    const float* g, int32_t* x, float* lse, float* logit, void* ws,
                                    size_t ws_bytes, void* stream) {
   return dspark_markov_sample_ex(dt, R, gamma, V, r, 0, U, W1, W2t, x0, G, g, nullptr, nullptr, nullptr, x, lse,
-                                 logit, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
+                                 logit, nullptr, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 dspark_status dspark_confidence(dspark_dtype dt, int R, int gamma, int d, int r, int V, const void* h,
@@ -332,7 +337,7 @@ dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r,
   const size_t off = (sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255);
   const RnnHead head{Wrnn, h, d, s, o, reinterpret_cast<float*>(static_cast<char*>(ws) + off)};
   if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, static_cast<hipStream_t>(stream),
-                    &head, nullptr, nullptr) != hipSuccess)
+                    &head, nullptr, nullptr, nullptr, nullptr, nullptr) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

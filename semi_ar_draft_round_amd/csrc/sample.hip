@@ -20,11 +20,14 @@
 // its log-sum-exp partial.  The next position reads the keys back as its
 // previous tokens.  sample_finalize decodes x, merges the log-sum-exp
 // partials and recomputes the logit of each drafted token.
+#include <hip/hip_ext.h>
+
 #include "bias_tile.hpp"
 #include "wide_tile.hpp"
 #include "sample_keys.hpp"
 #include "rnn_head.hpp"
 #include "sample_common.hpp"
+#include "confidence_row.hpp"
 
 #include <atomic>
 
@@ -623,7 +626,10 @@ __global__ __launch_bounds__(64) void sample_step_f32(
 
 // Decode x, merge the log-sum-exp partials and recompute each drafted
 // token's logit U_k(x_k) + W1[x_{k-1}] . W2t[x_k] (or the given bias vector
-// of (request, k) in W1[x_{k-1}]'s place): one wave per (request, k).
+// of (request, k) in W1[x_{k-1}]'s place): one wave per (request, k).  With
+// the confidence head asked for, the same wave then computes c_k from h_k
+// and the previous token's W1 row (caijizhuo section 四: the loop scores each
+// position right after drawing it).
 template <typename Elt>
 __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, int r,
                                                        const typename Elt::T* __restrict__ U,
@@ -633,7 +639,7 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
                                                        int nPart, int32_t* __restrict__ x,
                                                        float* __restrict__ lse, float* __restrict__ logit,
                                                        const typename Elt::T* __restrict__ bvec,
-                                                       int32_t* __restrict__ status) {
+                                                       int32_t* __restrict__ status, SampleConf conf) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= static_cast<int64_t>(R) * gamma) return;
@@ -650,6 +656,19 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   for (int p = lane; p < nPart; p += 64) {
     const float2 v = lp[p];
     run = lse_combine(run, Lse{v.x, v.y});
+  }
+  // the confidence head's previous token: the anchor, else the token this
+  // kernel emits for position k - 1 (token 0 where no key was drawn, -1 after
+  // a time-out)
+  const int prev_conf = k == 0 ? token_or_none(x0[req], V) : (timed_out != 0u ? -1 : (prev < 0 ? 0 : prev));
+  if (conf.h) {
+    const float zz = confidence_logit<Elt>(static_cast<const typename Elt::T*>(conf.h) + row * conf.d,
+                                           static_cast<const typename Elt::T*>(conf.w), conf.d, W1, r, prev_conf,
+                                           lane);
+    if (lane == 0) {
+      conf.c[row] = sigmoid_stable(zz / (conf.T ? conf.T[k] : 1.f));
+      if (conf.z) conf.z[row] = zz;
+    }
   }
   if (timed_out != 0u) {   // the persistent launch timed out at a grid barrier: no valid draw
     if (lane == 0) {
@@ -736,6 +755,7 @@ struct SampleArgs {
   const int32_t* x0;
   const float *G, *g;
   const uint32_t* cancel;   // nullable: a non-zero word ends the grid-barrier waits
+  hipEvent_t ev0, ev1;      // nullable: recorded at the start and the end of the position sweep
 };
 
 template <int NBW, int KS, bool VEC>
@@ -750,10 +770,11 @@ static void launch_step_bf16(const SampleArgs& a, int k, const SampleWs& w, int 
 template <int RQ, int KS16, bool VEC>
 static void launch_steps_wide(const SampleArgs& a, int kb, int ke, const SampleWs& w, int gx, hipStream_t s) {
   dim3 grid(gx, ceil_div(a.R, 32 * RQ));
-  hipLaunchKernelGGL((sample_steps_wide<RQ, KS16, VEC>), grid, dim3(wide_threads<RQ>()), 0, s, a.R, a.gamma, a.V,
-                     static_cast<const uint16_t*>(a.U), static_cast<const uint16_t*>(a.W1),
-                     static_cast<const uint16_t*>(a.W2t), a.x0, a.G, a.g, w, gx, kb, ke,
-                     static_cast<const uint16_t*>(a.bvec), a.cancel);
+  // with events, the runtime stamps them with the launch's own start and end
+  hipExtLaunchKernelGGL((sample_steps_wide<RQ, KS16, VEC>), grid, dim3(wide_threads<RQ>()), 0, s, a.ev0, a.ev1, 0,
+                        a.R, a.gamma, a.V, static_cast<const uint16_t*>(a.U), static_cast<const uint16_t*>(a.W1),
+                        static_cast<const uint16_t*>(a.W2t), a.x0, a.G, a.g, w, gx, kb, ke,
+                        static_cast<const uint16_t*>(a.bvec), a.cancel);
 }
 
 // Whether one work group of the persistent kernel fits on a compute unit
@@ -826,10 +847,16 @@ hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, 
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
-                         hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status) {
+                         hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status,
+                         const SampleConf* conf, hipEvent_t ev0, hipEvent_t ev1) {
+  const SampleConf cf = conf ? *conf : SampleConf{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
   const SampleWs w = carve(ws, R, gamma);
-  const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g, cancel};
   const int gxw = dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
+  // the one-launch sweep stamps the events itself; the per-position paths
+  // record them around all their launches
+  const bool one_launch = gxw > 0 && !rnn;
+  const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g, cancel,
+                     one_launch ? ev0 : nullptr, one_launch ? ev1 : nullptr};
   const int nPart = gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
   const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
   hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys, 256) < 1024 ? ceil_div(nkeys, 256) : 1024),
@@ -840,6 +867,8 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   // persistent path meets at a grid barrier between positions), one at a
   // time with the RNN head (its projection runs between positions)
   const int span = rnn ? 1 : gamma;
+  const bool record = ev0 && ev1 && !one_launch;
+  if (record && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
   for (int kb = 0; kb < gamma; kb += span) {
     if (rnn && (err = rnn_step_launch(dt, *rnn, R, gamma, V, r, kb, W1, x0, w.keys, s)) != hipSuccess) return err;
     if (gxw > 0) {
@@ -868,17 +897,18 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
+  if (record && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
   const int blocks = ceil_div(static_cast<int64_t>(R) * gamma, 4);
   if (dt == DSPARK_BF16)
     hipLaunchKernelGGL(sample_finalize<BF16>, dim3(blocks), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
                        static_cast<const uint16_t*>(W2t), x0, w, nPart, x, lse, logit,
-                       static_cast<const uint16_t*>(a.bvec), status);
+                       static_cast<const uint16_t*>(a.bvec), status, cf);
   else
     hipLaunchKernelGGL(sample_finalize<F32>, dim3(blocks), dim3(256), 0, s, R, gamma, V, r,
                        static_cast<const float*>(U), static_cast<const float*>(W1),
                        static_cast<const float*>(W2t), x0, w, nPart, x, lse, logit,
-                       static_cast<const float*>(a.bvec), status);
+                       static_cast<const float*>(a.bvec), status, cf);
   return hipGetLastError();
 }
 

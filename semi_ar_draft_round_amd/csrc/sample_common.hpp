@@ -24,6 +24,17 @@ constexpr int kBarWords = 256;             // as 64-bit words
 // real-time clock a work group gives up (0.5 s).
 constexpr unsigned long long kBarrierTicks = 50000000ull;
 
+// The confidence head's inputs when a sampling call computes it too (h null:
+// not asked for).
+struct SampleConf {
+  const void* h;   // [R][gamma][d]
+  const void* w;   // [d + r]
+  int d;
+  const float* T;  // [gamma] or null
+  float* c;        // [R][gamma]
+  float* z;        // [R][gamma] or null
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -2,7 +2,7 @@
 
 `to_device` copies a RoundInputs (the seeded arrays of workloads.py) into
 device tensors once, with every output buffer and workspace preallocated, so
-that `run_round` only enqueues the four library calls and can be captured in
+that `run_round` only enqueues its three library calls and can be captured in
 a HIP graph.
 """
 
@@ -59,6 +59,7 @@ class DeviceRound:
     ws_sample: torch.Tensor
     ws_sched: torch.Tensor
     ws_verify: torch.Tensor
+    status: torch.Tensor
     # the production scheduler: this round's capacity, its fill, and the
     # capacity its confidences set for two rounds later
     cap: torch.Tensor
@@ -109,6 +110,7 @@ def to_device(inp, device="cuda:0", rnn: bool = False) -> DeviceRound:
                              dtype=torch.uint8, device=dev),
         ws_verify=torch.empty(max(1, B.dspark_workspace_size(B.WS_VERIFY, R, gamma, V, r)),
                               dtype=torch.uint8, device=dev),
+        status=torch.zeros(1, dtype=torch.int32, device=dev),
         cap=torch.full((1,), R * gamma // 8, dtype=torch.int32, device=dev),
         ell_p=torch.empty(R, dtype=torch.int32, device=dev),
         admitted_p=torch.empty(1, dtype=torch.int32, device=dev),
@@ -141,6 +143,14 @@ def to_device(inp, device="cuda:0", rnn: bool = False) -> DeviceRound:
 
 def sample(d: DeviceRound):
     B.dspark_markov_sample(d.U, d.W1, d.W2t, d.x0, d.G, d.g, d.x, d.lse, d.logit, ws=d.ws_sample)
+
+
+def sample_conf(d: DeviceRound, timer=None):
+    """The draft and its confidences in one call (dspark_markov_sample_ex):
+    the sampler's finalize step scores every position.  timer: a
+    binding.SweepTimer to stamp with the position sweep (eager calls only)."""
+    B.dspark_markov_sample_ex(d.U, d.W1, d.W2t, d.x0, d.G, d.g, h=d.h, w=d.w, T=d.T, x=d.x, lse=d.lse,
+                              logit=d.logit, c=d.c, z=d.z, status=d.status, ws=d.ws_sample, timer=timer)
 
 
 def confidence(d: DeviceRound):
@@ -182,7 +192,16 @@ def verify(d: DeviceRound):
 
 
 def run_round(d: DeviceRound):
-    """Enqueue sample -> confidence -> schedule -> verify on the current stream."""
+    """Enqueue one round on the current stream: the draft with its
+    confidences (one call), the schedule, the verification."""
+    sample_conf(d)
+    schedule(d)
+    verify(d)
+
+
+def run_round_four_calls(d: DeviceRound):
+    """The same round as the four separate calls sample -> confidence ->
+    schedule -> verify."""
     sample(d)
     confidence(d)
     schedule(d)

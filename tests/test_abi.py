@@ -201,10 +201,10 @@ def test_verify_rejects_bad_arguments(lib):
 
 def test_sample_ex_rejects_bad_arguments(lib):
     def call(dt=1, R=4, gamma=3, V=1000, r=256, d=64, ptr=FAKE, h=FAKE, w=FAKE, c=FAKE, ws=FAKE,
-             ws_bytes=1 << 30):
+             ws_bytes=1 << 30, events=None):
         a = [ptr] * 6
         return lib.dspark_markov_sample_ex(dt, R, gamma, V, r, d, *a, h, w, None, ptr, ptr, ptr, c, None,
-                                           None, None, ws, ws_bytes, None)
+                                           None, None, events, ws, ws_bytes, None)
     assert call(dt=7) == EDTYPE
     assert call(R=0) == EINVAL
     assert call(r=96) == EDTYPE
@@ -212,6 +212,7 @@ def test_sample_ex_rejects_bad_arguments(lib):
     assert call(w=None) == EINVAL               # the confidence head needs its weights
     assert call(c=None) == EINVAL               # ... and somewhere to put c
     assert call(d=60) == EINVAL                 # bf16 hidden size: a multiple of 8
+    assert call(events=(ctypes.c_void_p * 2)(FAKE, None)) == EINVAL   # both events or none
     assert call(ws=None) == EWORKSPACE
     # without the confidence head its arguments are ignored
     assert call(h=None, w=None, c=None, d=0, ws=None) == EWORKSPACE

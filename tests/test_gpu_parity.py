@@ -311,3 +311,29 @@ def test_graph_capture_replays_match_eager(dev):
         got = DR.outputs_to_host(d)
         for k in ref:
             np.testing.assert_array_equal(np.asarray(ref[k]), np.asarray(got[k]), err_msg=f"{k} replay {rep}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_round_equals_four_calls(dev, dtype):
+    """The round's fused draft-and-confidence call and the four separate
+    calls (sample, confidence, schedule, verify) give the same outputs bit
+    for bit; the sweep events of the fused call bracket a positive time."""
+    from semi_ar_draft_round_amd import binding as B
+    from semi_ar_draft_round_amd import device_round as DR
+    w = W.custom(f"fused_{dtype}_r40_g5_v3000", R=40, gamma=5, V=3000, r=256 if dtype == "bf16" else 64, d=128,
+                 dtype=dtype, seed=47, temperatures=True)
+    inp = W.make_inputs(w)
+    say(f"[parity] {w.name}")
+    d = DR.to_device(inp, dev)
+    DR.run_round_four_calls(d)
+    ref = DR.outputs_to_host(d)
+    timer = B.SweepTimer()
+    DR.sample_conf(d, timer=timer)
+    DR.schedule(d)
+    DR.verify(d)
+    out = DR.outputs_to_host(d)
+    assert timer.elapsed_ms() > 0
+    assert int(d.status.cpu()[0]) == 0
+    for k in ("x", "lse", "logit", "c", "z", "ell", "n_acc", "next_tok"):
+        np.testing.assert_array_equal(out[k], ref[k], err_msg=k)
+    assert out["A"] == ref["A"] and out["theta_best"] == ref["theta_best"]
