@@ -55,6 +55,61 @@ __device__ __forceinline__ float dot_stride(const typename Elt::T* a, const type
   return acc;
 }
 
+// The hidden-state part of z, split so that a caller can put the first
+// batch of its loads in flight together with loads of its own:
+// conf_h_issue loads the lane's first kConfBatch pieces of h_k and w[:d],
+// conf_h_fold adds them up (then loads and adds any further batches) and
+// returns the lane's partial sum.
+template <typename Elt>
+struct ConfH {
+  uint4 hv[kConfBatch], wv[kConfBatch];
+};
+
+template <typename Elt>
+__device__ __forceinline__ void conf_h_issue(ConfH<Elt>& cb, const typename Elt::T* __restrict__ hrow,
+                                             const typename Elt::T* __restrict__ w, int d, int i0) {
+  constexpr int N = Vec16<Elt>::N;
+#pragma unroll
+  for (int b = 0; b < kConfBatch; ++b) {
+    const int i = i0 + b * 64 * N;
+    if (i < d) {
+      cb.hv[b] = *reinterpret_cast<const uint4*>(hrow + i);
+      cb.wv[b] = *reinterpret_cast<const uint4*>(w + i);
+    }
+  }
+}
+
+template <typename Elt>
+__device__ __forceinline__ float conf_h_fold(ConfH<Elt>& cb, const typename Elt::T* __restrict__ hrow,
+                                             const typename Elt::T* __restrict__ w, int d, int lane) {
+  constexpr int N = Vec16<Elt>::N;
+  float acc = 0.f;
+  for (int i0 = lane * N; i0 < d; i0 += 64 * N * kConfBatch) {
+    if (i0 != lane * N) conf_h_issue<Elt>(cb, hrow, w, d, i0);   // batches after the first
+#pragma unroll
+    for (int b = 0; b < kConfBatch; ++b) {
+      if (i0 + b * 64 * N < d) {
+        float va[N], vb[N];
+        Vec16<Elt>::load(reinterpret_cast<const typename Elt::T*>(&cb.hv[b]), va);
+        Vec16<Elt>::load(reinterpret_cast<const typename Elt::T*>(&cb.wv[b]), vb);
+#pragma unroll
+        for (int t = 0; t < N; ++t) acc = fmaf(va[t], vb[t], acc);
+      }
+    }
+  }
+  return acc;
+}
+
+// z from the lane's hidden-state partial: adds the previous token's part
+// (prev in [0, V), or -1 for none) and reduces over the wave (the same value
+// in every lane).
+template <typename Elt>
+__device__ __forceinline__ float conf_finish(float hacc, const typename Elt::T* __restrict__ w, int d,
+                                             const typename Elt::T* __restrict__ W1, int r, int prev, int lane) {
+  if (prev >= 0) hacc += dot_stride<Elt>(W1 + static_cast<int64_t>(prev) * r, w + d, r, lane);
+  return wave_reduce_sum(hacc);
+}
+
 // z of one position (the same value in every lane).  prev is the previous
 // token, already checked to lie in [0, V), or -1 for none (no W1 part).
 template <typename Elt>
@@ -62,31 +117,9 @@ __device__ __forceinline__ float confidence_logit(const typename Elt::T* __restr
                                                   const typename Elt::T* __restrict__ w, int d,
                                                   const typename Elt::T* __restrict__ W1, int r, int prev,
                                                   int lane) {
-  constexpr int N = Vec16<Elt>::N;
-  float acc = 0.f;
-  for (int i0 = lane * N; i0 < d; i0 += 64 * N * kConfBatch) {
-    uint4 hv[kConfBatch], wv[kConfBatch];
-#pragma unroll
-    for (int b = 0; b < kConfBatch; ++b) {
-      const int i = i0 + b * 64 * N;
-      if (i < d) {
-        hv[b] = *reinterpret_cast<const uint4*>(hrow + i);
-        wv[b] = *reinterpret_cast<const uint4*>(w + i);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kConfBatch; ++b) {
-      if (i0 + b * 64 * N < d) {
-        float va[N], vb[N];
-        Vec16<Elt>::load(reinterpret_cast<const typename Elt::T*>(&hv[b]), va);
-        Vec16<Elt>::load(reinterpret_cast<const typename Elt::T*>(&wv[b]), vb);
-#pragma unroll
-        for (int t = 0; t < N; ++t) acc = fmaf(va[t], vb[t], acc);
-      }
-    }
-  }
-  if (prev >= 0) acc += dot_stride<Elt>(W1 + static_cast<int64_t>(prev) * r, w + d, r, lane);
-  return wave_reduce_sum(acc);
+  ConfH<Elt> cb;
+  conf_h_issue<Elt>(cb, hrow, w, d, lane * Vec16<Elt>::N);
+  return conf_finish<Elt>(conf_h_fold<Elt>(cb, hrow, w, d, lane), w, d, W1, r, prev, lane);
 }
 
 // sigmoid(t) without overflow for either sign of t

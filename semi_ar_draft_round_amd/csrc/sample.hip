@@ -646,25 +646,70 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   if (status && row == 0 && lane == 0) *status = ws.bar[1] != 0u ? DSPARK_ETIMEOUT : DSPARK_OK;
   const int req = static_cast<int>(row / gamma);
   const int k = static_cast<int>(row % gamma);
-  // the time-out flag, the keys and the partials are loaded together; only
-  // the rows of the bias dot wait on the keys
+  // Every load that needs no token goes out first, together: the time-out
+  // flag, the key slots of positions k (the drawn token) and k - 1 (the
+  // previous one), the first log-sum-exp partials and the first batch of
+  // the hidden-state row.  The loads that need the tokens (the W1 and W2t
+  // rows of the bias dot, the drawn token's logit, the confidence head's W1
+  // part) then go out together as well: two round trips to memory per row.
   const unsigned int timed_out = ws.bar[1];
-  const int drawn = previous_token(ws.keys, x0, R, V, k + 1, req);
-  const int prev = bvec ? -1 : previous_token(ws.keys, x0, R, V, k, req);
-  Lse run{neg_inf(), 0.f};
-  const float2* lp = ws.lsep + (static_cast<int64_t>(k) * R + req) * nPart;
-  for (int p = lane; p < nPart; p += 64) {
-    const float2 v = lp[p];
-    run = lse_combine(run, Lse{v.x, v.y});
+  unsigned long long kd[kKeySlots], kq[kKeySlots];
+  const unsigned long long* kpd = ws.keys + static_cast<int64_t>(k) * kKeySlots * R + req;
+#pragma unroll
+  for (int sl = 0; sl < kKeySlots; ++sl) {
+    kd[sl] = kpd[static_cast<int64_t>(sl) * R];
+    kq[sl] = k > 0 ? kpd[static_cast<int64_t>(sl - kKeySlots) * R] : 0ull;
   }
+  const int x0v = x0[req];
+  constexpr int kLp = 4;   // partials per lane loaded up front
+  const float2* lp = ws.lsep + (static_cast<int64_t>(k) * R + req) * nPart;
+  float2 lpv[kLp];
+#pragma unroll
+  for (int q = 0; q < kLp; ++q) lpv[q] = lane + 64 * q < nPart ? lp[lane + 64 * q] : make_float2(neg_inf(), 0.f);
+  using T = typename Elt::T;
+  const T* hrow = conf.h ? static_cast<const T*>(conf.h) + row * conf.d : nullptr;
+  const T* cw = static_cast<const T*>(conf.w);
+  ConfH<Elt> cb;
+  if (conf.h) conf_h_issue<Elt>(cb, hrow, cw, conf.d, lane * Vec16<Elt>::N);
+
+  if (status && row == 0 && lane == 0) *status = timed_out != 0u ? DSPARK_ETIMEOUT : DSPARK_OK;
+  unsigned long long bd = 0, bq = 0;
+#pragma unroll
+  for (int sl = 0; sl < kKeySlots; ++sl) {
+    bd = kd[sl] > bd ? kd[sl] : bd;
+    bq = kq[sl] > bq ? kq[sl] : bq;
+  }
+  const int drawn = token_or_none(key_token(bd), V);
+  const int prevk = k == 0 ? token_or_none(x0v, V) : token_or_none(key_token(bq), V);
+  const int prev = bvec ? -1 : prevk;
   // the confidence head's previous token: the anchor, else the token this
   // kernel emits for position k - 1 (token 0 where no key was drawn, -1 after
   // a time-out)
-  const int prev_conf = k == 0 ? token_or_none(x0[req], V) : (timed_out != 0u ? -1 : (prev < 0 ? 0 : prev));
+  const int prev_conf = k == 0 ? prevk : (timed_out != 0u ? -1 : (prevk < 0 ? 0 : prevk));
+  const int tok = drawn < 0 ? 0 : drawn;   // every position draws a token in [0, V)
+  // the bias dot's first kBq elements per lane and the drawn token's logit
+  constexpr int kBq = 4;
+  const T* e = bvec ? bvec + row * r : (prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : nullptr);
+  float ev[kBq], wv[kBq];
+#pragma unroll
+  for (int q = 0; q < kBq; ++q) {
+    const int i = lane + 64 * q;
+    ev[q] = e && i < r ? Elt::load(e, i) : 0.f;
+    wv[q] = e && i < r ? Elt::load(W2t, static_cast<int64_t>(tok) * r + i) : 0.f;
+  }
+  const float utok = Elt::load(U, row * V + tok);
+
+  Lse run{neg_inf(), 0.f};
+#pragma unroll
+  for (int q = 0; q < kLp; ++q)
+    if (lane + 64 * q < nPart) run = lse_combine(run, Lse{lpv[q].x, lpv[q].y});
+  for (int p = lane + 64 * kLp; p < nPart; p += 64) {
+    const float2 v = lp[p];
+    run = lse_combine(run, Lse{v.x, v.y});
+  }
   if (conf.h) {
-    const float zz = confidence_logit<Elt>(static_cast<const typename Elt::T*>(conf.h) + row * conf.d,
-                                           static_cast<const typename Elt::T*>(conf.w), conf.d, W1, r, prev_conf,
-                                           lane);
+    const float zz = conf_finish<Elt>(conf_h_fold<Elt>(cb, hrow, cw, conf.d, lane), cw, conf.d, W1, r, prev_conf,
+                                      lane);
     if (lane == 0) {
       conf.c[row] = sigmoid_stable(zz / (conf.T ? conf.T[k] : 1.f));
       if (conf.z) conf.z[row] = zz;
@@ -678,19 +723,20 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
     }
     return;
   }
-  const int tok = drawn < 0 ? 0 : drawn;   // every position draws a token in [0, V)
   run = wave_reduce_lse(run);
   float b = 0.f;
-  if (bvec || prev >= 0) {
-    const typename Elt::T* e = bvec ? bvec + row * r : W1 + static_cast<int64_t>(prev) * r;
-    for (int i = lane; i < r; i += 64)
+  if (e) {
+#pragma unroll
+    for (int q = 0; q < kBq; ++q)
+      if (lane + 64 * q < r) b = fmaf(ev[q], wv[q], b);
+    for (int i = lane + 64 * kBq; i < r; i += 64)
       b = fmaf(Elt::load(e, i), Elt::load(W2t, static_cast<int64_t>(tok) * r + i), b);
   }
   b = wave_reduce_sum(b);
   if (lane == 0) {
     x[row] = tok;
     lse[row] = run.M + logf(run.S);
-    logit[row] = Elt::load(U, row * V + tok) + b;
+    logit[row] = utok + b;
   }
 }
 

@@ -211,6 +211,12 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
   // 3: thread t owns ranked positions [t*8, t*8+8)
   constexpr int kPer = kSchedMaxSlots / kSchedThreads;   // 8
   const uint64_t cand_limit = kOne << 13;                // keys below are candidates
+  // the step speeds of this thread's positions, SPS(R + m) for
+  // m = tid * kPer - 1 .. tid * kPer + kPer - 1 (those past the pool unread),
+  // fetched alongside the ranked keys rather than after them
+  double sp[kPer + 1];
+#pragma unroll
+  for (int u = 0; u <= kPer; ++u) sp[u] = (tid * kPer + u <= P) ? sps[R + tid * kPer + u - 1] : 0.0;
   uint64_t myk[kPer];
   uint64_t local = 0;
 #pragma unroll
@@ -249,16 +255,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(int R, int gamm
   int my_first_drop = 0x7FFFFFFF;
   int my_count = 0;
   // whole walk: this thread's best point (thread 0 also holds m = 0)
-  WalkPoint mine{static_cast<uint64_t>(R) * kOne, sps[R - 1], tid == 0 ? 0 : -1};
+  WalkPoint mine{static_cast<uint64_t>(R) * kOne, sp[0], tid == 0 ? 0 : -1};
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     if (myk[t] >= cand_limit) break;
     ++my_count;
     const int m = tid * kPer + t + 1;               // admitting the m-th ranked slot
     const uint64_t tau = tau_prev + (kOne - (myk[t] >> 13));
-    const double s_m = sps[R + m - 1];
+    const double s_m = sp[t + 1];                   // SPS(R + m)
     if (mode == DSPARK_SCHED_EARLY_STOP) {
-      if (my_first_drop == 0x7FFFFFFF && cmp_theta(tau, s_m, tau_prev, sps[R + m - 2]) <= 0) my_first_drop = m;
+      if (my_first_drop == 0x7FFFFFFF && cmp_theta(tau, s_m, tau_prev, sp[t]) <= 0) my_first_drop = m;
     } else if (mode == DSPARK_SCHED_WHOLE_WALK) {
       mine = better(mine, WalkPoint{tau, s_m, m});
     }
