@@ -24,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 matrix cores
 METRIC = "drafted tokens/s (sample+schedule+verify) at R=128 γ=16 V=129280; % HBM peak"
 
 
@@ -34,7 +35,8 @@ def log(*a):
 def source_hash() -> str:
     """Hash of the sources the sampling launch is built from."""
     h = hashlib.sha256()
-    for rel in ("semi_ar_draft_round_amd/csrc/sample.hip", "semi_ar_draft_round_amd/csrc/bias_tile.hpp",
+    for rel in ("semi_ar_draft_round_amd/csrc/sample.hip", "semi_ar_draft_round_amd/csrc/sample_res.hip",
+                "semi_ar_draft_round_amd/csrc/sample_common.hpp", "semi_ar_draft_round_amd/csrc/bias_tile.hpp",
                 "semi_ar_draft_round_amd/csrc/wide_tile.hpp", "semi_ar_draft_round_amd/csrc/common.hpp",
                 "semi_ar_draft_round_amd/csrc/sample_keys.hpp", "semi_ar_draft_round_amd/csrc/rnn_head.hpp",
                 "include/dspark.h"):
@@ -251,7 +253,7 @@ def main():
             sweeps.append(timer.elapsed_ms() * 1e3)
     torch.cuda.synchronize()
     sweep_us = float(np.mean(sweeps))
-    log(f"[bench] sample_steps_wide launch: mean {sweep_us:.1f} us over {len(sweeps)} eager rounds "
+    log(f"[bench] persistent sampling launch: mean {sweep_us:.1f} us over {len(sweeps)} eager rounds "
         f"(min {min(sweeps):.1f}, max {max(sweeps):.1f})")
     # the other modes, each timed on its own and outside the round: the
     # sampling call without and the confidence head as a call of its own, the
@@ -276,9 +278,16 @@ def main():
     bytes_model_b = bytes_launch - (w.gamma - 1) * w.r * w.V * 2
     achieved = bytes_launch / (sweep_us * 1e-6) / 1e9
     traffic = traffic_record(w.name)
+    kernel = binding.dspark_markov_sample_kernel(rounds[0].U.dtype, w.R, w.gamma, w.V, w.r)
+    # the bias product's work, for the matrix-core view of the same launch
+    flops_launch = 2.0 * w.R * w.r * w.V * w.gamma
+    tflops = flops_launch / (sweep_us * 1e-6) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "sample_steps_wide (all gamma positions in one launch)",
+                "kernel": kernel,
+                "mfma_bf16": {"achieved_tflops": round(tflops, 1), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "flops_per_launch": flops_launch},
                 "bytes_per_launch": bytes_launch, "us_per_launch": round(sweep_us, 2),
                 "noise_bytes_per_launch": noise_bytes_per_position(w) * w.gamma,
                 "bytes_per_launch_w2_once": bytes_model_b,

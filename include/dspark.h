@@ -470,6 +470,18 @@ size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r
 /* A static, human-readable description of a status code. */
 const char* dspark_status_string(dspark_status s);
 
+/*
+ * dspark_markov_sample_kernel — which kernel dspark_markov_sample(_ex) runs
+ * the positions with for this shape on the current device: a static string
+ * naming it and how it treats W2t, or NULL for arguments the sampling call
+ * would reject or a device that is not gfx950.  With bf16 storage, R <= 128,
+ * r in {32, 64, 128, 256} and at most eight 64-token tiles per compute unit
+ * (V <= 131072 on 256 compute units), each work group keeps its slice of
+ * W2t in registers and LDS for the whole launch; larger shapes stream W2t
+ * through LDS at every position.  Enqueues nothing.
+ */
+const char* dspark_markov_sample_kernel(dspark_dtype dt, int R, int gamma, int V, int r);
+
 #ifdef __cplusplus
 }
 #endif

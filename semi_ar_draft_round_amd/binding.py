@@ -47,6 +47,7 @@ _SIGNATURES = {
     "dspark_sts_fit": [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
     "dspark_status_string": [_I],
+    "dspark_markov_sample_kernel": [_I, _I, _I, _I, _I],
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -71,12 +72,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.dspark_workspace_size.restype = ctypes.c_size_t
     lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_markov_sample_kernel.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
 
 def dspark_status_string(status: int) -> str:
     return load_library().dspark_status_string(int(status)).decode()
+
+
+def dspark_markov_sample_kernel(dtype: torch.dtype, R: int, gamma: int, V: int, r: int):
+    """Which kernel the sampling call runs for this shape on the current
+    device (None when the call would reject the shape)."""
+    name = load_library().dspark_markov_sample_kernel(BF16 if dtype == torch.bfloat16 else F32,
+                                                      R, gamma, V, r)
+    return None if name is None else name.decode()
 
 
 def dspark_workspace_size(kind: int, R: int, gamma: int, V: int, r: int = 0, n_sps: int = 0) -> int:

@@ -271,53 +271,6 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
   }
 }
 
-// Grid-wide barrier between positions of the persistent kernel: every work
-// group of the launch is resident (one per compute unit, at most as many as
-// the device has), so a counter of arrivals suffices.  The key slots and the
-// counter are updated with system-scope atomics, which are performed in
-// memory rather than in the issuing die's L2, so no cache write-back is
-// needed to publish them; each wave waits for its own atomics to complete
-// before the work group arrives.  The wait is bounded: after kBarrierTicks of
-// the 100 MHz real-time clock the work group raises the time-out flag and
-// the launch ends early (sample_finalize then reports every token as -1 and
-// the call's status word, if any, as DSPARK_ETIMEOUT), so a grid that is not
-// resident as a whole cannot hang.  A caller's cancel word, when given and
-// non-zero, ends the wait the same way.
-
-__device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int round, int* flag,
-                                             const uint32_t* cancel) {
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's key atomics have completed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // two levels: work group b arrives at group counter b mod kBarGroups; the
-    // last arrival of a group arrives at the top counter, which everyone polls
-    const unsigned int nWG = gridDim.x * gridDim.y;
-    const unsigned int id = blockIdx.y * gridDim.x + blockIdx.x;
-    const unsigned int groups = nWG < kBarGroups ? nWG : kBarGroups;
-    const unsigned int grp = id % groups;
-    const unsigned int per = (nWG - grp + groups - 1) / groups;
-    const unsigned int old =
-        __hip_atomic_fetch_add(bar + 64 + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    if (old + 1 == round * per) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-    int ok = 1;
-    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < round * groups) {
-      if (__hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u ||
-          __builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks ||
-          (cancel && __hip_atomic_load(cancel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u)) {
-        __hip_atomic_fetch_or(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        ok = 0;
-        break;
-      }
-      // no sleep between polls: the next load goes out as soon as this one
-      // returns (a sleep of one measured about 2 % slower per launch)
-    }
-    *flag = ok;
-  }
-  __syncthreads();
-  return *flag != 0;
-}
-
 // W2t tiles of each work group that stay in LDS for the whole launch (the
 // middle pair of its tiles): they are read from HBM once instead of once per
 // position.
@@ -885,10 +838,27 @@ static void launch_step_bf16_ks(const SampleArgs& a, int k, const SampleWs& w, i
   }
 }
 
+// sample_res.hip: the Markov-head loop with W2t held in registers
+int res_grid_x(int V, int max_wgs);
+bool res_usable(int R, int V, int r, int max_wgs);
+hipError_t res_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
+                      const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx, int kb, int ke,
+                      const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s);
+
 // rnn.hip: the RNN head's projection and gating for position k (reads the
 // keys of position k - 1 for the previous token)
 hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, int V, int r, int k,
                            const void* W1, const int32_t* x0, const unsigned long long* keys, hipStream_t s);
+
+// The kernel sample_launch runs the Markov-head positions with, for a shape
+// (the same choice, in the same order).
+const char* sample_kernel_name(dspark_dtype dt, int R, int V, int r) {
+  if (dt == DSPARK_BF16 && res_usable(R, V, r, kMaxSampleWGs))
+    return "sample_steps_res: W2t held in registers, all positions in one persistent launch";
+  if (dt == DSPARK_BF16 && wide_fits_r(R, V, r))
+    return "sample_steps_wide: W2t streamed through LDS, all positions in one persistent launch";
+  return dt == DSPARK_BF16 ? "sample_step_bf16: one launch per position" : "sample_step_f32: one launch per position";
+}
 
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
@@ -897,13 +867,16 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                          const SampleConf* conf, hipEvent_t ev0, hipEvent_t ev1) {
   const SampleConf cf = conf ? *conf : SampleConf{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
   const SampleWs w = carve(ws, R, gamma);
-  const int gxw = dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
-  // the one-launch sweep stamps the events itself; the per-position paths
-  // record them around all their launches
-  const bool one_launch = gxw > 0 && !rnn;
+  // bf16 Markov head: W2t held in registers when the vocabulary fits the
+  // register files (res), else streamed through LDS at every position (wide)
+  const int gxr = dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(V, kMaxSampleWGs) : 0;
+  const int gxw = gxr == 0 && dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
+  // the one-launch sweeps stamp the events themselves; the per-position
+  // paths record them around all their launches
+  const bool one_launch = (gxr > 0 || gxw > 0) && !rnn;
   const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g, cancel,
                      one_launch ? ev0 : nullptr, one_launch ? ev1 : nullptr};
-  const int nPart = gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
+  const int nPart = gxr > 0 ? gxr : gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
   const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
   hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys, 256) < 1024 ? ceil_div(nkeys, 256) : 1024),
                      dim3(256), 0, s, w.keys, nkeys);
@@ -915,7 +888,10 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   const int span = rnn ? 1 : gamma;
   const bool record = ev0 && ev1 && !one_launch;
   if (record && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
-  for (int kb = 0; kb < gamma; kb += span) {
+  if (gxr > 0 &&
+      (err = res_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxr, 0, gamma, cancel, ev0, ev1, s)) != hipSuccess)
+    return err;
+  for (int kb = 0; gxr == 0 && kb < gamma; kb += span) {
     if (rnn && (err = rnn_step_launch(dt, *rnn, R, gamma, V, r, kb, W1, x0, w.keys, s)) != hipSuccess) return err;
     if (gxw > 0) {
       switch (r / 32) {

@@ -85,4 +85,51 @@ __device__ __forceinline__ bool fold_chunk(const f32x4 (&acc)[4], float G, int f
   return take;
 }
 
+// Grid-wide barrier between positions of the persistent kernel: every work
+// group of the launch is resident (one per compute unit, at most as many as
+// the device has), so a counter of arrivals suffices.  The key slots and the
+// counter are updated with system-scope atomics, which are performed in
+// memory rather than in the issuing die's L2, so no cache write-back is
+// needed to publish them; each wave waits for its own atomics to complete
+// before the work group arrives.  The wait is bounded: after kBarrierTicks of
+// the 100 MHz real-time clock the work group raises the time-out flag and
+// the launch ends early (sample_finalize then reports every token as -1 and
+// the call's status word, if any, as DSPARK_ETIMEOUT), so a grid that is not
+// resident as a whole cannot hang.  A caller's cancel word, when given and
+// non-zero, ends the wait the same way.
+
+__device__ __forceinline__ bool grid_barrier(unsigned int* bar, unsigned int round, int* flag,
+                                             const uint32_t* cancel) {
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's key atomics have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // two levels: work group b arrives at group counter b mod kBarGroups; the
+    // last arrival of a group arrives at the top counter, which everyone polls
+    const unsigned int nWG = gridDim.x * gridDim.y;
+    const unsigned int id = blockIdx.y * gridDim.x + blockIdx.x;
+    const unsigned int groups = nWG < kBarGroups ? nWG : kBarGroups;
+    const unsigned int grp = id % groups;
+    const unsigned int per = (nWG - grp + groups - 1) / groups;
+    const unsigned int old =
+        __hip_atomic_fetch_add(bar + 64 + 32 * grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (old + 1 == round * per) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    int ok = 1;
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < round * groups) {
+      if (__hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u ||
+          __builtin_amdgcn_s_memrealtime() - t0 > kBarrierTicks ||
+          (cancel && __hip_atomic_load(cancel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0u)) {
+        __hip_atomic_fetch_or(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        ok = 0;
+        break;
+      }
+      // no sleep between polls: the next load goes out as soon as this one
+      // returns (a sleep of one measured about 2 % slower per launch)
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 }  // namespace dspark

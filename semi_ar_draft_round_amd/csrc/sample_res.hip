@@ -1,0 +1,406 @@
+// The Markov-head sampling loop with the bias operand W2t held on chip.
+//
+// Passage: DSpark reading notes, eq (4) (the bias is added inside the
+// softmax) and eq (5) (Markov head B(x_{k-1}, .) = W1[x_{k-1}] W2, rank r);
+// caijizhuo section 四, the sequential loop of dspark_cycle.  The draw is the
+// exact two-level Gumbel-max of the other sampling kernels (chunk-level
+// log-sum-exp plus chunk Gumbel, then the in-chunk argmax).
+//
+// Every position multiplies the same W2t (V x r) by the previous tokens' W1
+// rows.  Streaming W2t from memory at every position costs more than the
+// logits themselves at r = 256 (66 MB against 33 MB per position at
+// R = 128, V = 129280), so this kernel keeps it on chip instead: one work
+// group per compute unit owns a contiguous range of at most eight 64-token
+// tiles, and each of its eight waves holds one tile's W2t rows in registers
+// as 32x32x16 MFMA A fragments for the whole launch (128 registers a lane at
+// r = 256; the whole vocabulary of the 256 compute units' register files at
+// V <= 131072).  A position then streams only the logits U_k and the chunk
+// Gumbels.
+//
+// Per position a wave walks the request blocks of 32: the block's logits
+// seed the accumulators, the previous tokens' W1 rows (gathered into LDS
+// once per position, the B operand) are multiplied in, and each lane folds
+// its two 16-token chunks (one per 32-token half of the tile) into the
+// request's log-sum-exp and chunk-level Gumbel-max, then draws inside the
+// winning chunk.  The waves' results per request merge in LDS, and one
+// thread per request merges them into the request's key slot (64-bit atomic
+// max) and log-sum-exp partial, as the other sampling kernels do.  The work
+// groups then meet at the grid barrier, read the keys back and gather the
+// next position's W1 rows.  Logits are loaded two request blocks ahead, so
+// the next position's first two blocks are in flight across the barrier.
+// At r = 256 the last four k-steps of each wave's A fragments sit in LDS
+// (64 KB per work group) to leave registers for those loads.
+#include <hip/hip_ext.h>
+
+#include "wide_tile.hpp"
+#include "sample_keys.hpp"
+#include "sample_common.hpp"
+
+#include <atomic>
+
+namespace dspark {
+
+constexpr int kResWaves = 8;
+constexpr int kResThreads = kResWaves * kWave;   // 512
+constexpr int kResMaxTiles = kResWaves;          // one tile per wave
+
+// LDS bytes of one request's W1 row (r = 16 KS16 bf16) plus a 16-byte pad,
+// so the rows a half-wave reads for one B fragment fall in different banks.
+template <int KS16>
+__host__ __device__ constexpr int res_erow_bytes() { return KS16 * 32 + 16; }
+
+// k-steps of each wave's A fragments kept in LDS rather than registers: at
+// r = 256 the last four (the registers they free hold a second request
+// block of logits in flight)
+template <int KS16>
+__host__ __device__ constexpr int res_lds_ksteps() { return KS16 >= 16 ? 4 : 0; }
+
+template <int RB, int KS16>
+__host__ __device__ constexpr int res_big_bytes() {
+  // the W1 rows of the group's requests, or (at the start) two W2t tiles
+  return 32 * RB * res_erow_bytes<KS16>() > 2 * wide_tile_bytes<KS16>() ? 32 * RB * res_erow_bytes<KS16>()
+                                                                          : 2 * wide_tile_bytes<KS16>();
+}
+
+// A request block's logits and chunk Gumbels for one lane: tokens
+// 32 tb + 16 h .. + 15 of the wave's tile for tb = 0, 1.
+struct ResLane {
+  u32x4 u[2][2];
+  float G[2];
+};
+
+template <int RB, int KS16, bool VEC>
+__global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
+    int R, int gamma, int V, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
+    const float* __restrict__ g, SampleWs ws, int kb, int ke, const uint32_t* __restrict__ cancel) {
+  static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
+  constexpr int NROWS = 32 * RB;
+  constexpr int kE = res_erow_bytes<KS16>();
+  constexpr int kWt = wide_tile_bytes<KS16>();
+  __shared__ __attribute__((aligned(1024))) uint8_t big[res_big_bytes<RB, KS16>()];
+  __shared__ float gsh[NROWS][kGChunk];                 // in-chunk Gumbels of the position
+  __shared__ unsigned long long mkey[kResWaves][NROWS];  // per-wave results, merged per request
+  __shared__ float2 mlse[kResWaves][NROWS];
+  constexpr int KL = res_lds_ksteps<KS16>();   // k-steps of A in LDS
+  constexpr int KR = KS16 - KL;                // k-steps of A in registers
+  __shared__ __attribute__((aligned(16))) bf16x8 alds[KL > 0 ? kResWaves : 1][2][KL > 0 ? KL : 1][kWave];
+  __shared__ int barflag;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int nTiles = (V + kChunk - 1) / kChunk;
+  const int nG = (V + kGChunk - 1) / kGChunk;
+  // the group's tiles: a contiguous range of base or base + 1 (<= 8, checked
+  // by the host); wave w owns tile t0 + w
+  const int gx = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
+  const int base = nTiles / gx, rem = nTiles % gx;
+  const int nT = base + (bx < rem ? 1 : 0);
+  const int t0 = bx * base + min(bx, rem);
+  const bool active = wave < nT;
+  const int tile = t0 + min(wave, nT - 1);
+  const int v0 = tile * kChunk;
+
+  // 1. W2t: each tile goes through LDS (two slots) into its wave's registers
+  bf16x8 A[2][KR > 0 ? KR : 1];
+  {
+    WideW<KS16, 4> wr;
+    for (int q = 0; q < nT; ++q) {
+      wide_load_w<KS16, 4>(wr, W2t, V, (t0 + q) * kChunk);
+      wide_store_w<KS16, 4>(big + (q & 1) * kWt, wr);
+      __syncthreads();
+      if (wave == q) {
+        const uint8_t* slot = big + (q & 1) * kWt;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int ks = 0; ks < KS16; ++ks) {
+            const bf16x8 f = *reinterpret_cast<const bf16x8*>(
+                slot + ((32 * tb + j) * wide_row_pieces<KS16>() + h) * 16 + ks * 32);
+            if (ks < KR)
+              A[tb][ks < KR ? ks : 0] = f;
+            else
+              alds[wave][tb][ks - KR][lane] = f;   // lane-contiguous: conflict-free reads
+          }
+      }
+    }
+    __syncthreads();   // the slots become the W1 rows
+  }
+
+  // 2. the W1 rows of the previous tokens (the B operand) for position k:
+  // the anchors at the first position, else the tokens drawn at k - 1
+  constexpr int TPR = kResThreads / NROWS;   // threads per row
+  constexpr int PPR = 2 * KS16;              // 16-byte pieces per row
+  auto gather_e = [&](int k, bool first) {
+    const int i = static_cast<int>(threadIdx.x) / TPR;
+    const int part = static_cast<int>(threadIdx.x) % TPR;
+    int prev = -1;
+    if (i < R) {
+      if (first) {
+        prev = token_or_none(x0[i], V);
+      } else {
+        const unsigned long long* kp = ws.keys + static_cast<int64_t>(k - 1) * kKeySlots * R + i;
+        unsigned long long best = 0;
+#pragma unroll
+        for (int sl = 0; sl < kKeySlots; ++sl) {
+          const unsigned long long v =
+              __hip_atomic_load(kp + static_cast<int64_t>(sl) * R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          best = v > best ? v : best;
+        }
+        prev = token_or_none(key_token(best), V);
+      }
+    }
+    const uint16_t* src = prev >= 0 ? W1 + static_cast<int64_t>(prev) * (KS16 * 16) : kZeroRow;
+#pragma unroll
+    for (int p = part; p < PPR; p += TPR)
+      *reinterpret_cast<u32x4*>(big + i * kE + p * 16) = *reinterpret_cast<const u32x4*>(src + p * 8);
+  };
+  // the in-chunk Gumbels of position k: four floats per thread
+  auto load_gq = [&](int k) {
+    const int i = static_cast<int>(threadIdx.x) >> 2, q = static_cast<int>(threadIdx.x) & 3;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (i < NROWS) v = *reinterpret_cast<const f32x4*>(g + (static_cast<int64_t>(min(i, R - 1)) * gamma + k) * kGChunk + 4 * q);
+    return v;
+  };
+  auto store_gq = [&](f32x4 v) {
+    const int i = static_cast<int>(threadIdx.x) >> 2, q = static_cast<int>(threadIdx.x) & 3;
+    if (i < NROWS) *reinterpret_cast<f32x4*>(&gsh[i][4 * q]) = v;
+  };
+
+  // logits and chunk Gumbels of step s = k * RB + rb (request block rb of
+  // position k) for this lane
+  auto load_step = [&](ResLane& p, int s) {
+    const int k = s / RB, rb = s % RB;
+    const int reqc = min(32 * rb + j, R - 1);
+    const uint16_t* row = U + (static_cast<int64_t>(reqc) * gamma + k) * V;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      // the -inf stand-in is picked by address, not by value, so the loads
+      // stay in flight until the step that uses them
+      load_lane16<VEC>(p.u[tb], row, v0 + 32 * tb + 16 * h, V);
+      p.G[tb] = G[(static_cast<int64_t>(k) * nG + min(4 * tile + 2 * tb + h, nG - 1)) * R + reqc];
+    }
+  };
+
+  const int s_end = ke * RB;
+  ResLane pa, pb;   // steps s and s + 1 in flight
+  if (active) {
+    load_step(pa, kb * RB);
+    load_step(pb, min(kb * RB + 1, s_end - 1));
+  }
+  gather_e(kb, kb == 0);
+  store_gq(load_gq(kb));
+  __syncthreads();
+
+  for (int k = kb; k < ke; ++k) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ResLane& cur = (rb & 1) ? pb : pa;
+      if (active) {
+        f32x16 acc0, acc1;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const uint32_t w0 = cur.u[0][q >> 3][(q >> 1) & 3];
+          const uint32_t w1 = cur.u[1][q >> 3][(q >> 1) & 3];
+          acc0[q] = __uint_as_float((q & 1) ? (w0 & 0xFFFF0000u) : (w0 << 16));
+          acc1[q] = __uint_as_float((q & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16));
+        }
+        const float G0 = cur.G[0], G1 = cur.G[1];
+        const int s = k * RB + rb;
+        load_step(cur, min(s + 2, s_end - 1));   // unconditional: no branch near the end
+        const uint8_t* erow = big + (32 * rb + j) * kE + h * 16;
+        // B fragments two k-steps ahead of their products; the empty asm
+        // with a memory clobber keeps the compiler from hoisting every read
+        // of the chain to the top, which would cost KS16 x 4 registers
+        bf16x8 bc = *reinterpret_cast<const bf16x8*>(erow);
+        bf16x8 bn = KS16 > 1 ? *reinterpret_cast<const bf16x8*>(erow + 32) : bc;
+#pragma unroll
+        for (int ks = 0; ks < KS16; ++ks) {
+          const bf16x8 bnn = ks + 2 < KS16 ? *reinterpret_cast<const bf16x8*>(erow + (ks + 2) * 32) : bn;
+          if (ks < KR) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0][ks < KR ? ks : 0], bc, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1][ks < KR ? ks : 0], bc, acc1, 0, 0, 0);
+          } else {
+            const int kl = ks < KR ? 0 : ks - KR;
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alds[wave][0][kl][lane], bc, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alds[wave][1][kl][lane], bc, acc1, 0, 0, 0);
+          }
+          asm volatile("" ::: "memory");
+          bc = bn;
+          bn = bnn;
+        }
+        // the lane's two chunks (tokens v0 + 16 h and v0 + 32 + 16 h onwards),
+        // then the in-chunk draw on the one that wins
+        const int loc = 32 * rb + j;
+        LaneDraw dr;
+        lane_draw_init(dr);
+        f32x4 a[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = f32x4{acc0[4 * m], acc0[4 * m + 1], acc0[4 * m + 2], acc0[4 * m + 3]};
+        fold_chunk(a, G0, v0 + 16 * h, dr);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = f32x4{acc1[4 * m], acc1[4 * m + 1], acc1[4 * m + 2], acc1[4 * m + 3]};
+        const bool take1 = fold_chunk(a, G1, v0 + 32 + 16 * h, dr);
+        float bs = neg_inf();
+        int bo = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(&gsh[loc][4 * m]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int c = 4 * m + t;
+            const float sc = (take1 ? acc1[c] : acc0[c]) + gv[t];
+            if (sc > bs) {
+              bs = sc;
+              bo = c;
+            }
+          }
+        }
+        unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
+        float M2 = dr.M2, Ts = dr.T;
+        {   // the request's other lane (h ^ 1)
+          const unsigned long long ok = __shfl_xor(key, 32);
+          const float M2o = __shfl_xor(M2, 32), To = __shfl_xor(Ts, 32);
+          key = ok > key ? ok : key;
+          const float Mn = fmaxf(M2, M2o);
+          Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);
+          M2 = Mn;
+        }
+        if (h == 0) {
+          mkey[wave][loc] = key;
+          mlse[wave][loc] = make_float2(M2, Ts);
+        }
+      }
+    }
+    if (RB & 1) {   // an odd block count flips the step parity across positions
+      const ResLane t = pa;
+      pa = pb;
+      pb = t;
+    }
+    __syncthreads();
+    // one thread per request merges the waves (tile order) into its key
+    // slot and log-sum-exp partial
+    if (static_cast<int>(threadIdx.x) < NROWS) {
+      const int i = static_cast<int>(threadIdx.x);
+      unsigned long long key = 0ull;
+      float M2 = neg_inf(), Ts = 0.f;
+      for (int w = 0; w < nT; ++w) {
+        const unsigned long long ok = mkey[w][i];
+        const float2 o = mlse[w][i];
+        key = ok > key ? ok : key;
+        const float Mn = fmaxf(M2, o.x);
+        Ts = (M2 == neg_inf() ? 0.f : Ts * __builtin_amdgcn_exp2f(M2 - Mn)) +
+             (o.x == neg_inf() ? 0.f : o.y * __builtin_amdgcn_exp2f(o.x - Mn));
+        M2 = Mn;
+      }
+      if (i < R) {
+        ws.lsep[(static_cast<int64_t>(k) * R + i) * gx + bx] = make_float2(M2 * kLn2, Ts);
+        if (key != 0ull)
+          __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * kKeySlots + bx % kKeySlots) * R + i, key,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+    if (k + 1 == ke) break;
+    const f32x4 gq = load_gq(k + 1);
+    if (!grid_barrier(ws.bar, k + 1, &barflag, cancel)) return;
+    gather_e(k + 1, false);
+    store_gq(gq);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+int compute_units();   // abi.hip
+
+// Work groups of the launch: one per compute unit (at most one per tile and
+// kMaxSampleWGs), or 0 when some group would get more than kResMaxTiles
+// tiles (the vocabulary is too large for the register files).
+int res_grid_x(int V, int max_wgs) {
+  const int nTiles = (V + kChunk - 1) / kChunk;
+  int gx = compute_units();
+  if (gx > nTiles) gx = nTiles;
+  if (gx > max_wgs) gx = max_wgs;
+  if (gx < 1) return 0;
+  return (nTiles + gx - 1) / gx <= kResMaxTiles ? gx : 0;
+}
+
+template <int RB, int KS16, bool VEC>
+static bool res_fits_one() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &n, reinterpret_cast<const void*>(&sample_steps_res<RB, KS16, VEC>), kResThreads, 0);
+    v = (e == hipSuccess && n >= 1) ? 1 : 2;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+template <int KS16>
+static bool res_fits_ks(int R, bool vec) {
+  if (R <= 32) return vec ? res_fits_one<1, KS16, true>() : res_fits_one<1, KS16, false>();
+  if (R <= 64) return vec ? res_fits_one<2, KS16, true>() : res_fits_one<2, KS16, false>();
+  return vec ? res_fits_one<4, KS16, true>() : res_fits_one<4, KS16, false>();
+}
+
+// Whether the resident-W2t kernel takes a bf16 Markov-head launch of this
+// shape: R <= 128, r in {32, 64, 128, 256}, at most kResMaxTiles tiles per
+// work group, and the work group fits on a compute unit.
+bool res_usable(int R, int V, int r, int max_wgs) {
+  if (R < 1 || R > 128 || res_grid_x(V, max_wgs) == 0) return false;
+  const bool vec = (V % kGChunk) == 0;
+  switch (r) {
+    case 32: return res_fits_ks<2>(R, vec);
+    case 64: return res_fits_ks<4>(R, vec);
+    case 128: return res_fits_ks<8>(R, vec);
+    case 256: return res_fits_ks<16>(R, vec);
+    default: return false;
+  }
+}
+
+template <int RB, int KS16, bool VEC>
+static void launch_res(int R, int gamma, int V, const void* U, const void* W1, const void* W2t, const int32_t* x0,
+                       const float* G, const float* g, const SampleWs& w, int gx, int kb, int ke,
+                       const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+  hipExtLaunchKernelGGL((sample_steps_res<RB, KS16, VEC>), dim3(gx), dim3(kResThreads), 0, s, ev0, ev1, 0, R, gamma,
+                        V, static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
+                        static_cast<const uint16_t*>(W2t), x0, G, g, w, kb, ke, cancel);
+}
+
+template <int KS16>
+static void launch_res_ks(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
+                          const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx, int kb,
+                          int ke, const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+  const bool vec = (V % kGChunk) == 0;
+#define DSPARK_RES(RB)                                                                                      \
+  (vec ? launch_res<RB, KS16, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s) \
+       : launch_res<RB, KS16, false>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s))
+  if (R <= 32)
+    DSPARK_RES(1);
+  else if (R <= 64)
+    DSPARK_RES(2);
+  else
+    DSPARK_RES(4);
+#undef DSPARK_RES
+}
+
+// Launches all positions kb .. ke - 1 (the caller checked res_usable).
+hipError_t res_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
+                      const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx, int kb, int ke,
+                      const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+  switch (r) {
+    case 32: launch_res_ks<2>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s); break;
+    case 64: launch_res_ks<4>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s); break;
+    case 128: launch_res_ks<8>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s); break;
+    default: launch_res_ks<16>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -227,3 +227,11 @@ def test_schedule_noalloc_rejects_bad_arguments(lib):
     assert call(R=482, gamma=16, n_sps=10000) == EINVAL   # beyond the static scratch
     assert call(R=0) == EINVAL
     assert call(ptr=None) == EINVAL
+
+
+def test_sample_kernel_query_rejects_what_the_call_rejects(lib):
+    # the same host checks as the sampling call: NULL for a bad type, shape
+    # or rank, and (on a machine without a gfx950 device) for valid ones too
+    assert lib.dspark_markov_sample_kernel(7, 128, 16, 129280, 256) is None
+    assert lib.dspark_markov_sample_kernel(1, 0, 16, 129280, 256) is None
+    assert lib.dspark_markov_sample_kernel(1, 128, 16, 129280, 96) is None

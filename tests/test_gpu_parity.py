@@ -337,3 +337,16 @@ def test_fused_round_equals_four_calls(dev, dtype):
     for k in ("x", "lse", "logit", "c", "z", "ell", "n_acc", "next_tok"):
         np.testing.assert_array_equal(out[k], ref[k], err_msg=k)
     assert out["A"] == ref["A"] and out["theta_best"] == ref["theta_best"]
+
+
+def test_sampling_kernel_choice(dev):
+    """The sampling call names the kernel it runs: W2t held in registers up
+    to 128 requests and eight tiles per compute unit, streamed otherwise."""
+    from semi_ar_draft_round_amd import binding as B
+    bf, f32 = torch.bfloat16, torch.float32
+    assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 256).startswith("sample_steps_res")
+    assert B.dspark_markov_sample_kernel(bf, 1, 16, 4096, 128).startswith("sample_steps_res")
+    assert B.dspark_markov_sample_kernel(bf, 256, 16, 129280, 256).startswith("sample_steps_wide")
+    assert B.dspark_markov_sample_kernel(bf, 128, 16, 151936, 256).startswith("sample_steps_wide")
+    assert B.dspark_markov_sample_kernel(f32, 4, 3, 1000, 64).startswith("sample_step_f32")
+    assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 96) is None

@@ -138,7 +138,11 @@ def test_rnn_reduces_to_markov_bit_for_bit(name, dev):
     x, lse, logit, s, o = got
     xm, lsem, logitm = B.dspark_markov_sample(d.U, W1, d.W2t, d.x0, d.G, d.g)
     torch.cuda.synchronize()
-    assert torch.equal(x, xm.cpu()) and torch.equal(lse, lsem.cpu()) and torch.equal(logit, logitm.cpu())
+    # same tokens and logits; the Markov call may take the kernel that keeps
+    # W2t in registers, which merges its log-sum-exp partials in another
+    # order, so lse agrees to rounding rather than bit for bit
+    assert torch.equal(x, xm.cpu()) and torch.equal(logit, logitm.cpu())
+    np.testing.assert_allclose(lse.numpy(), lsem.cpu().numpy(), rtol=2e-6, atol=0)
     prev = np.concatenate([inp.x0[:, None], x.numpy()[:, :-1]], axis=1)
     assert np.array_equal(o.float().numpy(), E[prev])
 
