@@ -110,10 +110,11 @@ def cpu_baseline(inps, n_req: int, min_seconds: float = 10.0, max_rounds: int = 
     return rec
 
 
-def traffic_record(workload: str):
-    """HBM traffic per sampling launch from committed rocprofv3 counter runs,
-    only if they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"traffic_sample_steps_{workload}.json")
+def traffic_record(workload: str, kernel: str):
+    """HBM traffic per sampling launch from committed rocprofv3 counter runs
+    of the kernel in use, only if they were taken on the current sources."""
+    tag = (kernel or "").split(":")[0].replace("sample_steps_", "")
+    p = os.path.join(ROOT, "profiles", f"traffic_sample_steps_{tag}_{workload}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
@@ -277,8 +278,8 @@ def main():
     # the on-chip-reuse floor: W2 read once per launch instead of once per position
     bytes_model_b = bytes_launch - (w.gamma - 1) * w.r * w.V * 2
     achieved = bytes_launch / (sweep_us * 1e-6) / 1e9
-    traffic = traffic_record(w.name)
     kernel = binding.dspark_markov_sample_kernel(rounds[0].U.dtype, w.R, w.gamma, w.V, w.r)
+    traffic = traffic_record(w.name, kernel)
     # the bias product's work, for the matrix-core view of the same launch
     flops_launch = 2.0 * w.R * w.r * w.V * w.gamma
     tflops = flops_launch / (sweep_us * 1e-6) / 1e12
