@@ -213,6 +213,7 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
         // B fragments two k-steps ahead of their products; the empty asm
         // with a memory clobber keeps the compiler from hoisting every read
         // of the chain to the top, which would cost KS16 x 4 registers
+        __builtin_amdgcn_iglp_opt(1);   // interleave the products with the neighbouring vector work
         bf16x8 bc = *reinterpret_cast<const bf16x8*>(erow);
         bf16x8 bn = KS16 > 1 ? *reinterpret_cast<const bf16x8*>(erow + 32) : bc;
 #pragma unroll
