@@ -845,6 +845,13 @@ hipError_t res_launch(int R, int gamma, int V, int r, const void* U, const void*
                       const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx, int kb, int ke,
                       const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s);
 
+// sample_pipe.hip: the Markov-head loop with W2t held on chip and one grid
+// barrier per request block (more than 64 requests)
+int pipe_grid(int R, int V, int r, int max_wgs);
+hipError_t pipe_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
+                       const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
+                       const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s);
+
 // rnn.hip: the RNN head's projection and gating for position k (reads the
 // keys of position k - 1 for the previous token)
 hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, int V, int r, int k,
@@ -853,6 +860,8 @@ hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, 
 // The kernel sample_launch runs the Markov-head positions with, for a shape
 // (the same choice, in the same order).
 const char* sample_kernel_name(dspark_dtype dt, int R, int V, int r) {
+  if (dt == DSPARK_BF16 && pipe_grid(R, V, r, kMaxSampleWGs) > 0)
+    return "sample_steps_pipe: W2t held on chip, one grid barrier per block of 32 requests, all positions in one persistent launch";
   if (dt == DSPARK_BF16 && res_usable(R, V, r, kMaxSampleWGs))
     return "sample_steps_res: W2t held in registers, all positions in one persistent launch";
   if (dt == DSPARK_BF16 && wide_fits_r(R, V, r))
@@ -869,14 +878,16 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   const SampleWs w = carve(ws, R, gamma);
   // bf16 Markov head: W2t held in registers when the vocabulary fits the
   // register files (res), else streamed through LDS at every position (wide)
-  const int gxr = dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(V, kMaxSampleWGs) : 0;
-  const int gxw = gxr == 0 && dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
+  const int gxp = dt == DSPARK_BF16 && !rnn ? pipe_grid(R, V, r, kMaxSampleWGs) : 0;
+  const int gxr =
+      gxp == 0 && dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(V, kMaxSampleWGs) : 0;
+  const int gxw = gxp == 0 && gxr == 0 && dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
   // the one-launch sweeps stamp the events themselves; the per-position
   // paths record them around all their launches
-  const bool one_launch = (gxr > 0 || gxw > 0) && !rnn;
+  const bool one_launch = (gxp > 0 || gxr > 0 || gxw > 0) && !rnn;
   const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g, cancel,
                      one_launch ? ev0 : nullptr, one_launch ? ev1 : nullptr};
-  const int nPart = gxr > 0 ? gxr : gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
+  const int nPart = gxp > 0 ? gxp : gxr > 0 ? gxr : gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
   const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
   hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys, 256) < 1024 ? ceil_div(nkeys, 256) : 1024),
                      dim3(256), 0, s, w.keys, nkeys);
@@ -888,10 +899,13 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   const int span = rnn ? 1 : gamma;
   const bool record = ev0 && ev1 && !one_launch;
   if (record && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+  if (gxp > 0 &&
+      (err = pipe_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxp, cancel, ev0, ev1, s)) != hipSuccess)
+    return err;
   if (gxr > 0 &&
       (err = res_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxr, 0, gamma, cancel, ev0, ev1, s)) != hipSuccess)
     return err;
-  for (int kb = 0; gxr == 0 && kb < gamma; kb += span) {
+  for (int kb = 0; gxp == 0 && gxr == 0 && kb < gamma; kb += span) {
     if (rnn && (err = rnn_step_launch(dt, *rnn, R, gamma, V, r, kb, W1, x0, w.keys, s)) != hipSuccess) return err;
     if (gxw > 0) {
       switch (r / 32) {

@@ -18,7 +18,12 @@ struct SampleWs {
 // of the persistent kernel's grid barrier and bar[1] its time-out flag; the
 // group counters sit at bar[64 + 32 g], 128 bytes apart.
 constexpr int kBarGroups = 8;              // arrival groups of the two-level barrier
-constexpr int kBarWords = 256;             // as 64-bit words
+// The per-block barriers of sample_steps_pipe: block d's group counter g at
+// bar[kPipeBarBase + 256 d + 32 g], for at most kPipeMaxBlocks blocks of 32
+// requests.
+constexpr int kPipeBarBase = 512;
+constexpr int kPipeMaxBlocks = 32;
+constexpr int kBarWords = (kPipeBarBase + 256 * kPipeMaxBlocks) / 2;   // as 64-bit words
 
 // The wait at a grid barrier is bounded: after this many ticks of the 100 MHz
 // real-time clock a work group gives up (0.5 s).

@@ -55,6 +55,11 @@ SMALL = [
     W.custom("wide_r130_g4_v4096_r256_bf16", R=130, gamma=4, V=4096, r=256, d=128, seed=18),
     W.custom("wide_r130_g4_v4100_r256_bf16", R=130, gamma=4, V=4100, r=256, d=128, seed=19),
     W.custom("wide_r256_g3_v2048_r256_bf16", R=256, gamma=3, V=2048, r=256, d=64, seed=20, temperatures=True),
+    # the per-block-barrier kernel with the fewest blocks it takes (3), with
+    # every compute unit holding two or three tiles; and a ragged last block
+    # of 8 at 7 blocks
+    W.custom("pipe_r96_g5_v40000_r256_bf16", R=96, gamma=5, V=40000, r=256, d=64, seed=23),
+    W.custom("pipe_r200_g3_v20000_r256_bf16", R=200, gamma=3, V=20000, r=256, d=64, seed=24),
 ]
 
 
@@ -183,7 +188,8 @@ def test_free_running_round_equals_oracle_round(dev):
         np.testing.assert_allclose(out["c"], ref["c"], rtol=1e-5)
 
 
-def test_cancelled_sampler_reports_time_out(dev):
+@pytest.mark.parametrize("R", [24, 100])
+def test_cancelled_sampler_reports_time_out(R, dev):
     """dspark_markov_sample_ex with its cancel word set: the persistent
     launch's grid-barrier waits give up at once (every work group exits
     normally), the status word reads DSPARK_ETIMEOUT and every token is the
@@ -191,7 +197,7 @@ def test_cancelled_sampler_reports_time_out(dev):
     matches dspark_markov_sample followed by dspark_confidence bit for bit."""
     from semi_ar_draft_round_amd import binding as B
     from semi_ar_draft_round_amd import device_round as DR
-    w = W.custom("cancel_r24_g4_v1500", R=24, gamma=4, V=1500, r=256, d=128, seed=43, temperatures=True)
+    w = W.custom(f"cancel_r{R}_g4_v1500", R=R, gamma=4, V=1500, r=256, d=128, seed=43, temperatures=True)
     inp = W.make_inputs(w)
     say(f"[parity] {w.name}")
     d = DR.to_device(inp, dev)
@@ -340,13 +346,17 @@ def test_fused_round_equals_four_calls(dev, dtype):
 
 
 def test_sampling_kernel_choice(dev):
-    """The sampling call names the kernel it runs: W2t held in registers up
-    to 128 requests and eight tiles per compute unit, streamed otherwise."""
+    """The sampling call names the kernel it runs: W2t held on chip up to
+    eight tiles per compute unit (one grid barrier per block of 32 requests
+    from 65 to 1024 requests, one per position up to 64), streamed
+    otherwise."""
     from semi_ar_draft_round_amd import binding as B
     bf, f32 = torch.bfloat16, torch.float32
-    assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 256).startswith("sample_steps_res")
+    assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 256).startswith("sample_steps_pipe")
+    assert B.dspark_markov_sample_kernel(bf, 256, 16, 129280, 256).startswith("sample_steps_pipe")
+    assert B.dspark_markov_sample_kernel(bf, 65, 16, 129280, 256).startswith("sample_steps_pipe")
+    assert B.dspark_markov_sample_kernel(bf, 64, 16, 129280, 256).startswith("sample_steps_res")
     assert B.dspark_markov_sample_kernel(bf, 1, 16, 4096, 128).startswith("sample_steps_res")
-    assert B.dspark_markov_sample_kernel(bf, 256, 16, 129280, 256).startswith("sample_steps_wide")
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 151936, 256).startswith("sample_steps_wide")
     assert B.dspark_markov_sample_kernel(f32, 4, 3, 1000, 64).startswith("sample_step_f32")
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 96) is None
