@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kRnnThreads) void rnn_proj_bf16(int R, int gamma, i
   const int i = ib * 32 + j;
   const int ic = min(i, R - 1);
   const int st1 = min(K / 16, (sp + 1) * per);
-  const int prev = previous_token(keys, x0, R, V, k, ic);
+  const int prev = previous_token(keys, kKeySlots, x0, R, V, k, ic);
   const float* srow = s + (static_cast<int64_t>(ic) * gamma + (k > 0 ? k - 1 : 0)) * r;   // read when k > 0
   const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
   const uint16_t* hrow = h + (static_cast<int64_t>(ic) * gamma + k) * d;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void rnn_proj_f32(int R, int gamma, int V, int
   const int i = static_cast<int>(idx / (3 * r));
   const int n = static_cast<int>(idx % (3 * r));
   const int K = 2 * r + d;
-  const int prev = previous_token(keys, x0, R, V, k, i);
+  const int prev = previous_token(keys, kKeySlots, x0, R, V, k, i);
   const float* w = W + static_cast<int64_t>(n) * K;
   float y = 0.f;
   if (k > 0) {

@@ -41,10 +41,11 @@ template <int NBW>
 __host__ __device__ constexpr int sample_reqs_per_wg() { return kTileWaves * 16 * NBW; }
 
 
-__global__ __launch_bounds__(256) void sample_init(unsigned long long* keys, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+// Clears the first n key words (the slots in use) and the barrier words.
+__global__ __launch_bounds__(256) void sample_init(unsigned long long* keys, int64_t n, unsigned long long* bar) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n + kBarWords;
        i += static_cast<int64_t>(gridDim.x) * 256)
-    keys[i] = 0ull;
+    (i < n ? keys[i] : bar[i - n]) = 0ull;
 }
 
 
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
   // the previous tokens first: the W1 rows they select gate the first products
   int prev[NBW];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) prev[nb] = !bvec && live[nb] ? previous_token(ws.keys, x0, R, V, k, req[nb]) : -1;
+  for (int nb = 0; nb < NBW; ++nb) prev[nb] = !bvec && live[nb] ? previous_token(ws.keys, ws.slots, x0, R, V, k, req[nb]) : -1;
   // in-chunk Gumbels: lane q brings offsets 4q .. 4q + 3 of its request
   f32x4 gq[NBW];
 #pragma unroll
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void sample_step_bf16(
     if (q == 0 && live[nb]) {
       ws.lsep[(static_cast<int64_t>(k) * R + req[nb]) * nPart + blockIdx.x] = make_float2(M2 * kLn2, T);
       if (key != 0ull)
-        atomicMax(ws.keys + (static_cast<int64_t>(k) * kKeySlots + blockIdx.x % kKeySlots) * R + req[nb], key);
+        atomicMax(ws.keys + (static_cast<int64_t>(k) * ws.slots + blockIdx.x % ws.slots) * R + req[nb], key);
     }
   }
 }
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
       merge(ksh[loc], o.x, o.y);
       ws.lsep[(static_cast<int64_t>(k) * R + req) * nPart + blockIdx.x] = make_float2(M2 * kLn2, Ts);
       if (key != 0ull)
-        __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * kKeySlots + blockIdx.x % kKeySlots) * R + req,
+        __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * ws.slots + blockIdx.x % ws.slots) * R + req,
                                key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     if (k + 1 == ke) break;
@@ -505,10 +506,9 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
     // logits and first two W2t tiles are already in flight
     gq = load_gq(k + 1);
     if (!grid_barrier(ws.bar, k + 1, &barflag, cancel)) return;
-    const unsigned long long* kp = ws.keys + static_cast<int64_t>(k) * kKeySlots * R + reqc;
+    const unsigned long long* kp = ws.keys + static_cast<int64_t>(k) * ws.slots * R + reqc;
     unsigned long long best = 0;
-#pragma unroll
-    for (int sl = 0; sl < kKeySlots; ++sl) {
+    for (int sl = 0; sl < ws.slots; ++sl) {
       const unsigned long long v = __hip_atomic_load(kp + static_cast<int64_t>(sl) * R, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_SYSTEM);
       best = v > best ? v : best;
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(64) void sample_step_f32(
   const int req = blockIdx.y;
   const int lane = threadIdx.x;
   const int nG = (V + kGChunk - 1) / kGChunk;
-  const int prev = bvec ? -1 : previous_token(ws.keys, x0, R, V, k, req);
+  const int prev = bvec ? -1 : previous_token(ws.keys, ws.slots, x0, R, V, k, req);
   const int v = tile * kChunk + lane;
   const int64_t rowk = static_cast<int64_t>(req) * gamma + k;
   float val = neg_inf();
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(64) void sample_step_f32(
   if (lane == 0) {
     ws.lsep[(static_cast<int64_t>(k) * R + req) * nPart + tile] = make_float2(run.M, run.S);
     if (ch.tok >= 0)
-      atomicMax(ws.keys + (static_cast<int64_t>(k) * kKeySlots + tile % kKeySlots) * R + req,
+      atomicMax(ws.keys + (static_cast<int64_t>(k) * ws.slots + tile % ws.slots) * R + req,
                 pack_key(ch.score, ch.tok));
   }
 }
@@ -606,12 +606,12 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   // rows of the bias dot, the drawn token's logit, the confidence head's W1
   // part) then go out together as well: two round trips to memory per row.
   const unsigned int timed_out = ws.bar[1];
-  unsigned long long kd[kKeySlots], kq[kKeySlots];
-  const unsigned long long* kpd = ws.keys + static_cast<int64_t>(k) * kKeySlots * R + req;
+  unsigned long long kd[kMaxKeySlots], kq[kMaxKeySlots];
+  const unsigned long long* kpd = ws.keys + static_cast<int64_t>(k) * ws.slots * R + req;
 #pragma unroll
-  for (int sl = 0; sl < kKeySlots; ++sl) {
-    kd[sl] = kpd[static_cast<int64_t>(sl) * R];
-    kq[sl] = k > 0 ? kpd[static_cast<int64_t>(sl - kKeySlots) * R] : 0ull;
+  for (int sl = 0; sl < kMaxKeySlots; ++sl) {
+    kd[sl] = sl < ws.slots ? kpd[static_cast<int64_t>(sl) * R] : 0ull;
+    kq[sl] = k > 0 && sl < ws.slots ? kpd[static_cast<int64_t>(sl - ws.slots) * R] : 0ull;
   }
   const int x0v = x0[req];
   constexpr int kLp = 4;   // partials per lane loaded up front
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(256) void sample_finalize(int R, int gamma, int V, 
   if (status && row == 0 && lane == 0) *status = timed_out != 0u ? DSPARK_ETIMEOUT : DSPARK_OK;
   unsigned long long bd = 0, bq = 0;
 #pragma unroll
-  for (int sl = 0; sl < kKeySlots; ++sl) {
+  for (int sl = 0; sl < kMaxKeySlots; ++sl) {
     bd = kd[sl] > bd ? kd[sl] : bd;
     bq = kq[sl] > bq ? kq[sl] : bq;
   }
@@ -704,18 +704,22 @@ int sample_parts(dspark_dtype dt, int V) {
 
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-static size_t cleared_words(int R, int gamma) {   // keys + barrier words, cleared per call
-  return static_cast<size_t>(kKeySlots) * R * gamma + kBarWords;
+static size_t key_words(int R, int gamma) {   // the key area, sized for the most slots
+  return static_cast<size_t>(kMaxKeySlots) * R * gamma;
+}
+static size_t cleared_words(int R, int gamma) {   // keys + barrier words
+  return key_words(R, gamma) + kBarWords;
 }
 size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V) {
   return align256(sizeof(unsigned long long) * cleared_words(R, gamma)) +
          sizeof(float2) * static_cast<size_t>(gamma) * R * sample_parts(dt, V);
 }
 
-static SampleWs carve(void* ws, int R, int gamma) {
+static SampleWs carve(void* ws, int R, int gamma, int slots) {
   SampleWs w;
+  w.slots = slots;
   w.keys = static_cast<unsigned long long*>(ws);
-  w.bar = reinterpret_cast<unsigned int*>(w.keys + static_cast<size_t>(kKeySlots) * R * gamma);
+  w.bar = reinterpret_cast<unsigned int*>(w.keys + key_words(R, gamma));
   w.lsep = reinterpret_cast<float2*>(static_cast<char*>(ws) + align256(sizeof(unsigned long long) * cleared_words(R, gamma)));
   return w;
 }
@@ -875,22 +879,22 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
                          hipStream_t s, const RnnHead* rnn, const uint32_t* cancel, int32_t* status,
                          const SampleConf* conf, hipEvent_t ev0, hipEvent_t ev1) {
   const SampleConf cf = conf ? *conf : SampleConf{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
-  const SampleWs w = carve(ws, R, gamma);
   // bf16 Markov head: W2t held in registers when the vocabulary fits the
   // register files (res), else streamed through LDS at every position (wide)
   const int gxp = dt == DSPARK_BF16 && !rnn ? pipe_grid(R, V, r, kMaxSampleWGs) : 0;
   const int gxr =
       gxp == 0 && dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(V, kMaxSampleWGs) : 0;
   const int gxw = gxp == 0 && gxr == 0 && dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
+  const SampleWs w = carve(ws, R, gamma, gxp > 0 ? kPipeKeySlots : kKeySlots);
   // the one-launch sweeps stamp the events themselves; the per-position
   // paths record them around all their launches
   const bool one_launch = (gxp > 0 || gxr > 0 || gxw > 0) && !rnn;
   const SampleArgs a{R, gamma, V, U, W1, W2t, rnn ? rnn->o : nullptr, x0, G, g, cancel,
                      one_launch ? ev0 : nullptr, one_launch ? ev1 : nullptr};
   const int nPart = gxp > 0 ? gxp : gxr > 0 ? gxr : gxw > 0 ? gxw : dt == DSPARK_BF16 ? bf16_grid_x(R, V) : ceil_div(V, kChunk);
-  const int64_t nkeys = static_cast<int64_t>(cleared_words(R, gamma));
-  hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys, 256) < 1024 ? ceil_div(nkeys, 256) : 1024),
-                     dim3(256), 0, s, w.keys, nkeys);
+  const int64_t nkeys = static_cast<int64_t>(w.slots) * R * gamma;
+  hipLaunchKernelGGL(sample_init, dim3(ceil_div(nkeys + kBarWords, 256) < 1024 ? ceil_div(nkeys + kBarWords, 256) : 1024),
+                     dim3(256), 0, s, w.keys, nkeys, reinterpret_cast<unsigned long long*>(w.bar));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // the positions one launch covers: all of them with the Markov head (the

@@ -9,9 +9,10 @@
 namespace dspark {
 
 struct SampleWs {
-  unsigned long long* keys;   // [gamma][kKeySlots][R]
+  unsigned long long* keys;   // [gamma][slots][R]
   unsigned int* bar;          // barrier words (below)
   float2* lsep;               // [gamma][R][nPart]  (M, S) log-sum-exp partials
+  int slots;                  // argmax key slots per (position, request)
 };
 
 // Barrier words (32-bit), cleared on every call: bar[0] is the top counter

@@ -63,6 +63,7 @@ constexpr int kPipeWaves = 8;
 constexpr int kPipeThreads = kPipeWaves * kWave;   // 512
 constexpr int kPipeMaxTiles = kPipeWaves;          // one tile per wave
 constexpr int kPipeMinBlocks = 3;                  // fewer blocks leave no steps to hide a barrier behind
+constexpr int kHalfSlots = kPipeKeySlots / 2;      // key slots one lane reads
 
 // k-steps of each wave's A fragments kept in LDS rather than registers
 template <int KS16>
@@ -163,22 +164,32 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
   // producer, start of step t + 1: merge the waves' results of step t into
   // the requests' key slots (atomic max) and log-sum-exp partials
   auto merge_step = [&](int k, int rb, const unsigned long long (*mk)[32], const float2 (*ml)[32]) {
-    const int i = 32 * rb + lane;
-    if (lane < 32 && i < R) {
-      unsigned long long key = 0ull;
-      float M2 = neg_inf(), Ts = 0.f;
-      for (int w = 0; w < nT; ++w) {
-        const unsigned long long ok = mk[w][lane];
-        const float2 o = ml[w][lane];
-        key = ok > key ? ok : key;
-        const float Mn = fmaxf(M2, o.x);
-        Ts = (M2 == neg_inf() ? 0.f : Ts * __builtin_amdgcn_exp2f(M2 - Mn)) +
-             (o.x == neg_inf() ? 0.f : o.y * __builtin_amdgcn_exp2f(o.x - Mn));
-        M2 = Mn;
-      }
-      ws.lsep[(static_cast<int64_t>(k) * R + i) * gx + bx] = make_float2(M2 * kLn2, Ts);
+    // lane (h, j): request j over waves 4 h .. 4 h + 3, then the two halves
+    unsigned long long key = 0ull;
+    float M2[4], T[4], M = neg_inf();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int w = 4 * h + q;
+      const unsigned long long ok = w < nT ? mk[w][j] : 0ull;
+      const float2 o = w < nT ? ml[w][j] : make_float2(neg_inf(), 0.f);
+      key = ok > key ? ok : key;
+      M2[q] = o.x;
+      T[q] = o.y;
+      M = fmaxf(M, o.x);
+    }
+    float Ts = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Ts += M2[q] == neg_inf() ? 0.f : T[q] * __builtin_amdgcn_exp2f(M2[q] - M);
+    const unsigned long long ko = __shfl_xor(key, 32);
+    const float Mo = __shfl_xor(M, 32), To = __shfl_xor(Ts, 32);
+    key = ko > key ? ko : key;
+    const float Mn = fmaxf(M, Mo);
+    Ts = (M == neg_inf() ? 0.f : Ts * __builtin_amdgcn_exp2f(M - Mn)) + (Mo == neg_inf() ? 0.f : To * __builtin_amdgcn_exp2f(Mo - Mn));
+    const int i = 32 * rb + j;
+    if (h == 0 && i < R) {
+      ws.lsep[(static_cast<int64_t>(k) * R + i) * gx + bx] = make_float2(Mn * kLn2, Ts);
       if (key != 0ull)
-        __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * kKeySlots + bx % kKeySlots) * R + i, key,
+        __hip_atomic_fetch_max(ws.keys + (static_cast<int64_t>(k) * kPipeKeySlots + bx % kPipeKeySlots) * R + i, key,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   };
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
   // consumer, start of step c - 1: every work group has arrived for the
   // block at position k - 1 (wait, bounded, only if not yet); then load the
   // block's key slots of that position.  False when the wait gave up.
-  auto poll_finish = [&](int k, int rb, uint32_t pv, unsigned long long& kr0, unsigned long long& kr1) {
+  auto poll_finish = [&](int k, int rb, uint32_t pv, unsigned long long (&kr)[kHalfSlots]) {
     const uint32_t target = static_cast<uint32_t>(k) * static_cast<uint32_t>(gx);
     bool ok = false, stop = stopped(pv);
     if (!stop) {
@@ -236,22 +247,26 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
     if (stop && lane == 0) __hip_atomic_fetch_or(ws.bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     // unconditional (requests past R read request R - 1's keys and are
     // dropped at the gather), so the wait for them can be counted exactly
-    const unsigned long long* kp = ws.keys + static_cast<int64_t>(k - 1) * kKeySlots * R + min(32 * rb + j, R - 1);
-    kr0 = __hip_atomic_load(kp + static_cast<int64_t>(h) * R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    kr1 = __hip_atomic_load(kp + static_cast<int64_t>(h + 2) * R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const unsigned long long* kp = ws.keys + (static_cast<int64_t>(k - 1) * kPipeKeySlots + h * kHalfSlots) * R +
+                                   min(32 * rb + j, R - 1);
+#pragma unroll
+    for (int q = 0; q < kHalfSlots; ++q)
+      kr[q] = __hip_atomic_load(kp + static_cast<int64_t>(q) * R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     return ok;
   };
-  // consumer, middle of step c - 1 (or the start, for the first two steps):
+  // consumer, middle of step c - 1 (the prologue, for the first two steps):
   // the block's previous tokens (the anchors at position 0), their W1 rows
   // and the block's in-chunk Gumbels, copied into the slot of step c
-  auto gather_issue = [&](int k, int rb, unsigned long long kr0, unsigned long long kr1, uint8_t* eslot,
+  auto gather_issue = [&](int k, int rb, const unsigned long long (&kr)[kHalfSlots], uint8_t* eslot,
                           float (*gslot)[kGChunk]) {
     int tok;
     if (k == 0) {
       const int i = 32 * rb + j;
       tok = i < R ? token_or_none(x0[i], V) : -1;
     } else {
-      unsigned long long b = kr0 > kr1 ? kr0 : kr1;
+      unsigned long long b = kr[0];
+#pragma unroll
+      for (int q = 1; q < kHalfSlots; ++q) b = kr[q] > b ? kr[q] : b;
       const unsigned long long o = __shfl_xor(b, 32);
       b = o > b ? o : b;
       tok = 32 * rb + j < R ? token_or_none(key_token(b), V) : -1;
@@ -270,7 +285,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
   };
 
   uint32_t pv = 0u;                          // consumer: the polled group counters
-  unsigned long long kr0 = 0ull, kr1 = 0ull; // consumer: the key slots read
+  unsigned long long kr[kHalfSlots] = {};    // consumer: the key slots read (half of them per lane)
   bool cok = true;                           // consumer: the wait did not give up
 
   // one step: the request block's logits plus bias for the wave's tile, the
@@ -286,10 +301,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
                   unsigned long long (*mkcur)[32], float2 (*mlcur)[32], uint8_t* enxt,
                   float (*gnxt)[kGChunk], const unsigned long long (*mkprev)[32], const float2 (*mlprev)[32]) {
     const bool prod = s >= 1 && ((s - 1) & (kPipeWaves - 1)) == wave;              // producer of step s - 1
-    const bool cons1 = s + 1 < s_end && s + 1 >= 2 && ((s + 1) & (kPipeWaves - 1)) == wave;   // consumer of s + 1
+    const bool cons1 = s + 1 < s_end && s + 1 >= 2 && ((s + 1) & (kPipeWaves - 1)) == wave;   // copies for s + 1
     const bool cons2 = s + 2 < s_end && p2.k > 0 && ((s + 2) & (kPipeWaves - 1)) == wave;     // polls for s + 2
     if (prod) merge_step(pm1.k, pm1.rb, mkprev, mlprev);
-    if (cons1) cok = p1.k > 0 ? poll_finish(p1.k, p1.rb, pv, kr0, kr1) : true;
+    if (cons1) cok = p1.k > 0 ? poll_finish(p1.k, p1.rb, pv, kr) : true;
 
     f32x16 acc0, acc1;
     {
@@ -331,7 +346,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
     // middle of the step
     if (prod && s - 1 + nb < s_end) arrive(pm1.rb);
     if (cons2) pv = poll_issue(p2.rb);
-    if (cons1 && cok) gather_issue(p1.k, p1.rb, kr0, kr1, enxt, gnxt);
+    if (cons1 && cok) gather_issue(p1.k, p1.rb, kr, enxt, gnxt);
 
     {
       LaneDraw dr;
@@ -383,8 +398,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
   load_step(pa, 0, 0);
   load_step(pb, 0, 1);
   // the first two steps' W1 rows and Gumbels (position 0: the anchors)
-  if (wave == 0) gather_issue(0, 0, 0ull, 0ull, eslot0, gslot0);
-  if (wave == 1) gather_issue(0, 1, 0ull, 0ull, eslot1, gslot1);
+  if (wave == 0) gather_issue(0, 0, kr, eslot0, gslot0);
+  if (wave == 1) gather_issue(0, 1, kr, eslot1, gslot1);
   __builtin_amdgcn_s_waitcnt(0);   // includes the A fragments copied into LDS
   __syncthreads();
 

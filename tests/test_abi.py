@@ -57,9 +57,9 @@ def test_workspace_sizes(lib):
     from semi_ar_draft_round_amd import binding as B
     n_c = (129280 + 63) // 64
     ws = B.dspark_workspace_size(B.WS_SAMPLE, 128, 16, 129280, 256)
-    # argmax keys (4 slots per request and position) and 4352 barrier words
-    # (the position barrier's words, then 32 blocks' per-block barriers of
-    # 1 KB each),
+    # argmax keys (4 slots per request and position) and 4352
+    # barrier words (the position barrier's words, then 32 blocks'
+    # per-block barriers of 1 KB each),
     # then one (max, sum) pair per chunk, request and position (the fp32
     # path's bound)
     assert ws == 8 * (4 * 128 * 16 + 4352) + 16 * 128 * n_c * 8
