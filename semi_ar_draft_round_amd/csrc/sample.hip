@@ -843,7 +843,7 @@ static void launch_step_bf16_ks(const SampleArgs& a, int k, const SampleWs& w, i
 }
 
 // sample_res.hip: the Markov-head loop with W2t held in registers
-int res_grid_x(int V, int max_wgs);
+int res_grid_x(int R, int V, int r, int max_wgs);
 bool res_usable(int R, int V, int r, int max_wgs);
 hipError_t res_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
                       const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx, int kb, int ke,
@@ -883,7 +883,7 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   // register files (res), else streamed through LDS at every position (wide)
   const int gxp = dt == DSPARK_BF16 && !rnn ? pipe_grid(R, V, r, kMaxSampleWGs) : 0;
   const int gxr =
-      gxp == 0 && dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(V, kMaxSampleWGs) : 0;
+      gxp == 0 && dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(R, V, r, kMaxSampleWGs) : 0;
   const int gxw = gxp == 0 && gxr == 0 && dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
   const SampleWs w = carve(ws, R, gamma, gxp > 0 ? kPipeKeySlots : kKeySlots);
   // the one-launch sweeps stamp the events themselves; the per-position

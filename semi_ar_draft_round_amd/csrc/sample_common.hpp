@@ -41,6 +41,23 @@ struct SampleConf {
   float* z;        // [R][gamma] or null
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// A 16-byte copy from global memory straight into LDS: lane l writes
+// dst + 16 l (dst the same for the whole wave).
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+
+// Token offset (within a 64-token tile) of the 32x32x16 A-operand row `row`
+// (0..63) of the sampling kernels: the rows are permuted so that a lane's
+// sixteen accumulators are sixteen consecutive tokens (one Gumbel chunk);
+// the inverse of row32_of_token.
+__host__ __device__ constexpr int token_of_row32(int row) {
+  return (row & 32) | (((row >> 2) & 1) << 4) | (((row >> 3) & 3) << 2) | (row & 3);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

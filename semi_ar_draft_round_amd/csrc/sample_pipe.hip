@@ -56,9 +56,6 @@
 
 namespace dspark {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
 constexpr int kPipeWaves = 8;
 constexpr int kPipeThreads = kPipeWaves * kWave;   // 512
 constexpr int kPipeMaxTiles = kPipeWaves;          // one tile per wave
@@ -68,18 +65,6 @@ constexpr int kHalfSlots = kPipeKeySlots / 2;      // key slots one lane reads
 // k-steps of each wave's A fragments kept in LDS rather than registers
 template <int KS16>
 __host__ __device__ constexpr int pipe_lds_ksteps() { return KS16 >= 16 ? 4 : 0; }
-
-// Token offset (within a 64-token tile) of stored A row `row` (0..63): the
-// inverse of row32_of_token.
-__host__ __device__ constexpr int token_of_row32(int row) {
-  return (row & 32) | (((row >> 2) & 1) << 4) | (((row >> 3) & 3) << 2) | (row & 3);
-}
-
-// A 16-byte copy from global memory straight into LDS: lane l writes
-// dst + 16 l (dst the same for the whole wave).
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
-}
 
 // Work-group barrier for LDS only: the waves' LDS operations have completed,
 // but their loads from memory may still be in flight (the step's logit

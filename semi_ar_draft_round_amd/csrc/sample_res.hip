@@ -11,11 +11,15 @@
 // logits themselves at r = 256 (66 MB against 33 MB per position at
 // R = 128, V = 129280), so this kernel keeps it on chip instead: one work
 // group per compute unit owns a contiguous range of at most eight 64-token
-// tiles, and each of its eight waves holds one tile's W2t rows in registers
-// as 32x32x16 MFMA A fragments for the whole launch (128 registers a lane at
-// r = 256; the whole vocabulary of the 256 compute units' register files at
-// V <= 131072).  A position then streams only the logits U_k and the chunk
-// Gumbels.
+// tiles, and each of its eight waves holds one tile's W2t rows as 32x32x16
+// MFMA A fragments for the whole launch (128 registers a lane at r = 256,
+// the last four k-steps in LDS; V <= 131072 on 256 compute units).  With a
+// single request block (R <= 32) at r = 256, the W1 rows need so little LDS
+// that two more tiles per work group fit there whole, taken by waves 0 and
+// 1 after their own (V <= 163840).  A position then streams only the logits
+// U_k and the chunk Gumbels.  The A fragments are loaded straight from W2t
+// at launch: registers for the first k-steps, a copy into LDS (no
+// registers) for the rest.
 //
 // Per position a wave walks the request blocks of 32: the block's logits
 // seed the accumulators, the previous tokens' W1 rows (gathered into LDS
@@ -29,7 +33,9 @@
 // next position's W1 rows.  Logits are loaded two request blocks ahead, so
 // the next position's first two blocks are in flight across the barrier.
 // At r = 256 the last four k-steps of each wave's A fragments sit in LDS
-// (64 KB per work group) to leave registers for those loads.
+// (64 KB per work group) to leave registers for those loads.  With a single
+// request block the logits are loaded one position ahead instead: one
+// register set for the wave's own tile, one for its LDS-held tile.
 #include <hip/hip_ext.h>
 
 #include "wide_tile.hpp"
@@ -37,12 +43,12 @@
 #include "sample_common.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 namespace dspark {
 
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * kWave;   // 512
-constexpr int kResMaxTiles = kResWaves;          // one tile per wave
 
 // LDS bytes of one request's W1 row (r = 16 KS16 bf16) plus a 16-byte pad,
 // so the rows a half-wave reads for one B fragment fall in different banks.
@@ -55,15 +61,15 @@ __host__ __device__ constexpr int res_erow_bytes() { return KS16 * 32 + 16; }
 template <int KS16>
 __host__ __device__ constexpr int res_lds_ksteps() { return KS16 >= 16 ? 4 : 0; }
 
+// Tiles a work group can hold: one per wave (registers plus LDS), and at
+// r = 256 with a single request block two more held wholly in LDS (one
+// block's W1 rows leave room for them), so vocabularies up to 2560 tiles
+// (V <= 163840 on 256 compute units) stay on chip for single requests.
 template <int RB, int KS16>
-__host__ __device__ constexpr int res_big_bytes() {
-  // the W1 rows of the group's requests, or (at the start) two W2t tiles
-  return 32 * RB * res_erow_bytes<KS16>() > 2 * wide_tile_bytes<KS16>() ? 32 * RB * res_erow_bytes<KS16>()
-                                                                          : 2 * wide_tile_bytes<KS16>();
-}
+__host__ __device__ constexpr int res_max_tiles() { return RB == 1 && KS16 == 16 ? kResWaves + 2 : kResWaves; }
 
 // A request block's logits and chunk Gumbels for one lane: tokens
-// 32 tb + 16 h .. + 15 of the wave's tile for tb = 0, 1.
+// 32 tb + 16 h .. + 15 of a tile for tb = 0, 1.
 struct ResLane {
   u32x4 u[2][2];
   float G[2];
@@ -77,14 +83,16 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
   constexpr int NROWS = 32 * RB;
   constexpr int kE = res_erow_bytes<KS16>();
-  constexpr int kWt = wide_tile_bytes<KS16>();
-  __shared__ __attribute__((aligned(1024))) uint8_t big[res_big_bytes<RB, KS16>()];
-  __shared__ float gsh[NROWS][kGChunk];                 // in-chunk Gumbels of the position
-  __shared__ unsigned long long mkey[kResWaves][NROWS];  // per-wave results, merged per request
-  __shared__ float2 mlse[kResWaves][NROWS];
-  constexpr int KL = res_lds_ksteps<KS16>();   // k-steps of A in LDS
-  constexpr int KR = KS16 - KL;                // k-steps of A in registers
+  constexpr int kMT = res_max_tiles<RB, KS16>();
+  constexpr int NX = kMT - kResWaves;            // tiles held wholly in LDS (0 or 2)
+  constexpr int KL = res_lds_ksteps<KS16>();     // k-steps of A in LDS
+  constexpr int KR = KS16 - KL;                  // k-steps of A in registers
+  __shared__ __attribute__((aligned(1024))) uint8_t erows[NROWS * kE];   // the W1 rows (B operand)
+  __shared__ float gsh[NROWS][kGChunk];                                  // in-chunk Gumbels of the position
+  __shared__ unsigned long long mkey[kMT][NROWS];                        // per-tile results, merged per request
+  __shared__ float2 mlse[kMT][NROWS];
   __shared__ __attribute__((aligned(16))) bf16x8 alds[KL > 0 ? kResWaves : 1][2][KL > 0 ? KL : 1][kWave];
+  __shared__ __attribute__((aligned(16))) bf16x8 xlds[NX > 0 ? NX : 1][2][NX > 0 ? KS16 : 1][kWave];
   __shared__ int barflag;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -92,8 +100,9 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
   const int h = lane >> 5;
   const int nTiles = (V + kChunk - 1) / kChunk;
   const int nG = (V + kGChunk - 1) / kGChunk;
-  // the group's tiles: a contiguous range of base or base + 1 (<= 8, checked
-  // by the host); wave w owns tile t0 + w
+  // the group's tiles: a contiguous range of base or base + 1 (<= kMT,
+  // checked by the host); wave w owns tile t0 + w, and waves 0 and 1 also
+  // tiles t0 + 8 and t0 + 9 when the group has them
   const int gx = static_cast<int>(gridDim.x), bx = static_cast<int>(blockIdx.x);
   const int base = nTiles / gx, rem = nTiles % gx;
   const int nT = base + (bx < rem ? 1 : 0);
@@ -101,31 +110,35 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
   const bool active = wave < nT;
   const int tile = t0 + min(wave, nT - 1);
   const int v0 = tile * kChunk;
+  const bool xact = NX > 0 && wave < nT - kResWaves;   // this wave also owns an LDS-held tile
+  const int xtile = t0 + kResWaves + min(wave, NX > 0 ? NX - 1 : 0);
+  const int xv0 = xtile * kChunk;
 
-  // 1. W2t: each tile goes through LDS (two slots) into its wave's registers
+  // 1. W2t: the wave's tile as A fragments, the first KR k-steps straight
+  // into registers, the rest (and any LDS-held tile) straight into LDS
   bf16x8 A[2][KR > 0 ? KR : 1];
-  {
-    WideW<KS16, 4> wr;
-    for (int q = 0; q < nT; ++q) {
-      wide_load_w<KS16, 4>(wr, W2t, V, (t0 + q) * kChunk);
-      wide_store_w<KS16, 4>(big + (q & 1) * kWt, wr);
-      __syncthreads();
-      if (wave == q) {
-        const uint8_t* slot = big + (q & 1) * kWt;
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < 2; ++tb) {
+    const int vrow = min(v0 + token_of_row32(32 * tb + j), V - 1);
+    const uint16_t* src = W2t + static_cast<int64_t>(vrow) * (KS16 * 16) + h * 8;
 #pragma unroll
-          for (int ks = 0; ks < KS16; ++ks) {
-            const bf16x8 f = *reinterpret_cast<const bf16x8*>(
-                slot + ((32 * tb + j) * wide_row_pieces<KS16>() + h) * 16 + ks * 32);
-            if (ks < KR)
-              A[tb][ks < KR ? ks : 0] = f;
-            else
-              alds[wave][tb][ks - KR][lane] = f;   // lane-contiguous: conflict-free reads
-          }
+    for (int ks = 0; ks < KS16; ++ks) {
+      if (ks < KR)
+        A[tb][ks < KR ? ks : 0] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+      else
+        copy16_to_lds(src + ks * 16, &alds[wave][tb][ks < KR ? 0 : ks - KR][0]);
+    }
+  }
+  if constexpr (NX > 0) {
+    if (xact) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int vrow = min(xv0 + token_of_row32(32 * tb + j), V - 1);
+        const uint16_t* src = W2t + static_cast<int64_t>(vrow) * (KS16 * 16) + h * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS16; ++ks) copy16_to_lds(src + ks * 16, &xlds[wave][tb][ks][0]);
       }
     }
-    __syncthreads();   // the slots become the W1 rows
   }
 
   // 2. the W1 rows of the previous tokens (the B operand) for position k:
@@ -154,7 +167,7 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     const uint16_t* src = prev >= 0 ? W1 + static_cast<int64_t>(prev) * (KS16 * 16) : kZeroRow;
 #pragma unroll
     for (int p = part; p < PPR; p += TPR)
-      *reinterpret_cast<u32x4*>(big + i * kE + p * 16) = *reinterpret_cast<const u32x4*>(src + p * 8);
+      *reinterpret_cast<u32x4*>(erows + i * kE + p * 16) = *reinterpret_cast<const u32x4*>(src + p * 8);
   };
   // the in-chunk Gumbels of position k: four floats per thread
   auto load_gq = [&](int k) {
@@ -168,119 +181,152 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     if (i < NROWS) *reinterpret_cast<f32x4*>(&gsh[i][4 * q]) = v;
   };
 
-  // logits and chunk Gumbels of step s = k * RB + rb (request block rb of
-  // position k) for this lane
-  auto load_step = [&](ResLane& p, int s) {
-    const int k = s / RB, rb = s % RB;
+  // logits and chunk Gumbels of request block rb at position k for this
+  // lane, tile starting at token vt
+  auto load_at = [&](ResLane& p, int k, int rb, int vt) {
     const int reqc = min(32 * rb + j, R - 1);
     const uint16_t* row = U + (static_cast<int64_t>(reqc) * gamma + k) * V;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       // the -inf stand-in is picked by address, not by value, so the loads
       // stay in flight until the step that uses them
-      load_lane16<VEC>(p.u[tb], row, v0 + 32 * tb + 16 * h, V);
-      p.G[tb] = G[(static_cast<int64_t>(k) * nG + min(4 * tile + 2 * tb + h, nG - 1)) * R + reqc];
+      load_lane16<VEC>(p.u[tb], row, vt + 32 * tb + 16 * h, V);
+      p.G[tb] = G[(static_cast<int64_t>(k) * nG + min(vt / kGChunk + 2 * tb + h, nG - 1)) * R + reqc];
+    }
+  };
+  // step s = k * RB + rb (request block rb of position k), the wave's own tile
+  auto load_step = [&](ResLane& p, int s) { load_at(p, s / RB, s % RB, v0); };
+
+  // the products of one request block and tile: the logits seed the
+  // accumulators and the bias is added on the matrix cores (A from
+  // registers and alds, or all from xlds for an LDS-held tile)
+  auto products = [&](const ResLane& cur, int rb, f32x16& acc0, f32x16& acc1, auto from_xlds) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t w0 = cur.u[0][q >> 3][(q >> 1) & 3];
+      const uint32_t w1 = cur.u[1][q >> 3][(q >> 1) & 3];
+      acc0[q] = __uint_as_float((q & 1) ? (w0 & 0xFFFF0000u) : (w0 << 16));
+      acc1[q] = __uint_as_float((q & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16));
+    }
+    const uint8_t* erow = erows + (32 * rb + j) * kE + h * 16;
+    // B fragments two k-steps ahead of their products; the empty asm
+    // with a memory clobber keeps the compiler from hoisting every read
+    // of the chain to the top, which would cost KS16 x 4 registers
+    if constexpr (KS16 >= 8) __builtin_amdgcn_iglp_opt(1);   // interleave the products with the vector work
+    bf16x8 bc = *reinterpret_cast<const bf16x8*>(erow);
+    bf16x8 bn = KS16 > 1 ? *reinterpret_cast<const bf16x8*>(erow + 32) : bc;
+#pragma unroll
+    for (int ks = 0; ks < KS16; ++ks) {
+      const bf16x8 bnn = ks + 2 < KS16 ? *reinterpret_cast<const bf16x8*>(erow + (ks + 2) * 32) : bn;
+      if constexpr (decltype(from_xlds)::value) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xlds[wave][0][ks][lane], bc, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xlds[wave][1][ks][lane], bc, acc1, 0, 0, 0);
+      } else if (ks < KR) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0][ks < KR ? ks : 0], bc, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1][ks < KR ? ks : 0], bc, acc1, 0, 0, 0);
+      } else {
+        const int kl = ks < KR ? 0 : ks - KR;
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alds[wave][0][kl][lane], bc, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alds[wave][1][kl][lane], bc, acc1, 0, 0, 0);
+      }
+      asm volatile("" ::: "memory");
+      bc = bn;
+      bn = bnn;
+    }
+  };
+  // the lane's two chunks (tokens vt + 16 h and vt + 32 + 16 h onwards), the
+  // in-chunk draw on the one that wins, the merge with the request's other
+  // lane; the tile's result goes to row `slot` of the per-tile results
+  auto fold_store = [&](const f32x16& acc0, const f32x16& acc1, float G0, float G1, int vt, int loc, int slot) {
+    LaneDraw dr;
+    lane_draw_init(dr);
+    f32x4 a[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] = f32x4{acc0[4 * m], acc0[4 * m + 1], acc0[4 * m + 2], acc0[4 * m + 3]};
+    fold_chunk(a, G0, vt + 16 * h, dr);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] = f32x4{acc1[4 * m], acc1[4 * m + 1], acc1[4 * m + 2], acc1[4 * m + 3]};
+    const bool take1 = fold_chunk(a, G1, vt + 32 + 16 * h, dr);
+    float bs = neg_inf();
+    int bo = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(&gsh[loc][4 * m]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = 4 * m + t;
+        const float sc = (take1 ? acc1[c] : acc0[c]) + gv[t];
+        if (sc > bs) {
+          bs = sc;
+          bo = c;
+        }
+      }
+    }
+    unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
+    float M2 = dr.M2, Ts = dr.T;
+    {   // the request's other lane (h ^ 1)
+      const unsigned long long ok = __shfl_xor(key, 32);
+      const float M2o = __shfl_xor(M2, 32), To = __shfl_xor(Ts, 32);
+      key = ok > key ? ok : key;
+      const float Mn = fmaxf(M2, M2o);
+      Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);
+      M2 = Mn;
+    }
+    if (h == 0) {
+      mkey[slot][loc] = key;
+      mlse[slot][loc] = make_float2(M2, Ts);
     }
   };
 
   const int s_end = ke * RB;
-  ResLane pa, pb;   // steps s and s + 1 in flight
+  ResLane pa, pb;   // steps s and s + 1 in flight (one block: the own tile and the LDS-held tile)
   if (active) {
     load_step(pa, kb * RB);
-    load_step(pb, min(kb * RB + 1, s_end - 1));
+    if (NX == 0) load_step(pb, min(kb * RB + 1, s_end - 1));
   }
+  if (NX > 0 && xact) load_at(pb, kb, 0, xv0);
   gather_e(kb, kb == 0);
   store_gq(load_gq(kb));
+  __builtin_amdgcn_s_waitcnt(0);   // the A fragments copied into LDS have landed
   __syncthreads();
 
   for (int k = kb; k < ke; ++k) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      ResLane& cur = (rb & 1) ? pb : pa;
+    if constexpr (NX > 0) {
+      // one request block: the own tile (its next position's logits go into
+      // pa), then the LDS-held tile if any (pb)
+      f32x16 acc0, acc1;
       if (active) {
-        f32x16 acc0, acc1;
+        products(pa, 0, acc0, acc1, std::false_type{});
+        const float G0 = pa.G[0], G1 = pa.G[1];
+        load_step(pa, min(k + 1, ke - 1));
+        fold_store(acc0, acc1, G0, G1, v0, j, wave);
+      }
+      if (xact) {
+        products(pb, 0, acc0, acc1, std::true_type{});
+        const float G0 = pb.G[0], G1 = pb.G[1];
+        load_at(pb, min(k + 1, ke - 1), 0, xv0);
+        fold_store(acc0, acc1, G0, G1, xv0, j, kResWaves + wave);
+      }
+    } else {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const uint32_t w0 = cur.u[0][q >> 3][(q >> 1) & 3];
-          const uint32_t w1 = cur.u[1][q >> 3][(q >> 1) & 3];
-          acc0[q] = __uint_as_float((q & 1) ? (w0 & 0xFFFF0000u) : (w0 << 16));
-          acc1[q] = __uint_as_float((q & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16));
-        }
-        const float G0 = cur.G[0], G1 = cur.G[1];
-        const int s = k * RB + rb;
-        load_step(cur, min(s + 2, s_end - 1));   // unconditional: no branch near the end
-        const uint8_t* erow = big + (32 * rb + j) * kE + h * 16;
-        // B fragments two k-steps ahead of their products; the empty asm
-        // with a memory clobber keeps the compiler from hoisting every read
-        // of the chain to the top, which would cost KS16 x 4 registers
-        __builtin_amdgcn_iglp_opt(1);   // interleave the products with the neighbouring vector work
-        bf16x8 bc = *reinterpret_cast<const bf16x8*>(erow);
-        bf16x8 bn = KS16 > 1 ? *reinterpret_cast<const bf16x8*>(erow + 32) : bc;
-#pragma unroll
-        for (int ks = 0; ks < KS16; ++ks) {
-          const bf16x8 bnn = ks + 2 < KS16 ? *reinterpret_cast<const bf16x8*>(erow + (ks + 2) * 32) : bn;
-          if (ks < KR) {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[0][ks < KR ? ks : 0], bc, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[1][ks < KR ? ks : 0], bc, acc1, 0, 0, 0);
-          } else {
-            const int kl = ks < KR ? 0 : ks - KR;
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alds[wave][0][kl][lane], bc, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alds[wave][1][kl][lane], bc, acc1, 0, 0, 0);
-          }
-          asm volatile("" ::: "memory");
-          bc = bn;
-          bn = bnn;
-        }
-        // the lane's two chunks (tokens v0 + 16 h and v0 + 32 + 16 h onwards),
-        // then the in-chunk draw on the one that wins
-        const int loc = 32 * rb + j;
-        LaneDraw dr;
-        lane_draw_init(dr);
-        f32x4 a[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = f32x4{acc0[4 * m], acc0[4 * m + 1], acc0[4 * m + 2], acc0[4 * m + 3]};
-        fold_chunk(a, G0, v0 + 16 * h, dr);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = f32x4{acc1[4 * m], acc1[4 * m + 1], acc1[4 * m + 2], acc1[4 * m + 3]};
-        const bool take1 = fold_chunk(a, G1, v0 + 32 + 16 * h, dr);
-        float bs = neg_inf();
-        int bo = 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f32x4 gv = *reinterpret_cast<const f32x4*>(&gsh[loc][4 * m]);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int c = 4 * m + t;
-            const float sc = (take1 ? acc1[c] : acc0[c]) + gv[t];
-            if (sc > bs) {
-              bs = sc;
-              bo = c;
-            }
-          }
-        }
-        unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
-        float M2 = dr.M2, Ts = dr.T;
-        {   // the request's other lane (h ^ 1)
-          const unsigned long long ok = __shfl_xor(key, 32);
-          const float M2o = __shfl_xor(M2, 32), To = __shfl_xor(Ts, 32);
-          key = ok > key ? ok : key;
-          const float Mn = fmaxf(M2, M2o);
-          Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);
-          M2 = Mn;
-        }
-        if (h == 0) {
-          mkey[wave][loc] = key;
-          mlse[wave][loc] = make_float2(M2, Ts);
+      for (int rb = 0; rb < RB; ++rb) {
+        ResLane& cur = (rb & 1) ? pb : pa;
+        if (active) {
+          f32x16 acc0, acc1;
+          products(cur, rb, acc0, acc1, std::false_type{});
+          const float G0 = cur.G[0], G1 = cur.G[1];
+          load_step(cur, min(k * RB + rb + 2, s_end - 1));   // unconditional: no branch near the end
+          fold_store(acc0, acc1, G0, G1, v0, 32 * rb + j, wave);
         }
       }
-    }
-    if (RB & 1) {   // an odd block count flips the step parity across positions
-      const ResLane t = pa;
-      pa = pb;
-      pb = t;
+      if (RB & 1) {   // an odd block count flips the step parity across positions
+        const ResLane t = pa;
+        pa = pb;
+        pb = t;
+      }
     }
     __syncthreads();
-    // one thread per request merges the waves (tile order) into its key
+    // one thread per request merges the tiles (in tile order) into its key
     // slot and log-sum-exp partial
     if (static_cast<int>(threadIdx.x) < NROWS) {
       const int i = static_cast<int>(threadIdx.x);
@@ -315,16 +361,21 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
 
 int compute_units();   // abi.hip
 
+// Tiles a work group can hold for a shape (see res_max_tiles).
+static int res_tiles_for(int R, int r) {
+  return R <= 32 && r == 256 ? res_max_tiles<1, 16>() : res_max_tiles<4, 16>();
+}
+
 // Work groups of the launch: one per compute unit (at most one per tile and
-// kMaxSampleWGs), or 0 when some group would get more than kResMaxTiles
-// tiles (the vocabulary is too large for the register files).
-int res_grid_x(int V, int max_wgs) {
+// max_wgs), or 0 when some group would get more tiles than it can hold (the
+// vocabulary is too large for the register files and LDS).
+int res_grid_x(int R, int V, int r, int max_wgs) {
   const int nTiles = (V + kChunk - 1) / kChunk;
   int gx = compute_units();
   if (gx > nTiles) gx = nTiles;
   if (gx > max_wgs) gx = max_wgs;
   if (gx < 1) return 0;
-  return (nTiles + gx - 1) / gx <= kResMaxTiles ? gx : 0;
+  return (nTiles + gx - 1) / gx <= res_tiles_for(R, r) ? gx : 0;
 }
 
 template <int RB, int KS16, bool VEC>
@@ -351,10 +402,10 @@ static bool res_fits_ks(int R, bool vec) {
 }
 
 // Whether the resident-W2t kernel takes a bf16 Markov-head launch of this
-// shape: R <= 128, r in {32, 64, 128, 256}, at most kResMaxTiles tiles per
-// work group, and the work group fits on a compute unit.
+// shape: R <= 128, r in {32, 64, 128, 256}, at most res_tiles_for(R, r)
+// tiles per work group, and the work group fits on a compute unit.
 bool res_usable(int R, int V, int r, int max_wgs) {
-  if (R < 1 || R > 128 || res_grid_x(V, max_wgs) == 0) return false;
+  if (R < 1 || R > 128 || res_grid_x(R, V, r, max_wgs) == 0) return false;
   const bool vec = (V % kGChunk) == 0;
   switch (r) {
     case 32: return res_fits_ks<2>(R, vec);

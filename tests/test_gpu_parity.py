@@ -60,6 +60,13 @@ SMALL = [
     # of 8 at 7 blocks
     W.custom("pipe_r96_g5_v40000_r256_bf16", R=96, gamma=5, V=40000, r=256, d=64, seed=23),
     W.custom("pipe_r200_g3_v20000_r256_bf16", R=200, gamma=3, V=20000, r=256, d=64, seed=24),
+    # single request blocks with more than eight tiles per compute unit (the
+    # resident kernel's LDS-held ninth and tenth tiles): some groups with a
+    # ninth tile, every group with ten (the largest vocabulary it takes),
+    # and a full block with V not a multiple of 16
+    W.custom("res9_r3_g3_v140000_r256_bf16", R=3, gamma=3, V=140000, r=256, d=64, seed=25),
+    W.custom("res10_r2_g4_v163840_r256_bf16", R=2, gamma=4, V=163840, r=256, d=64, seed=26),
+    W.custom("res10_r32_g2_v150003_r256_bf16", R=32, gamma=2, V=150003, r=256, d=64, seed=27),
 ]
 
 
@@ -347,9 +354,9 @@ def test_fused_round_equals_four_calls(dev, dtype):
 
 def test_sampling_kernel_choice(dev):
     """The sampling call names the kernel it runs: W2t held on chip up to
-    eight tiles per compute unit (one grid barrier per block of 32 requests
-    from 65 to 1024 requests, one per position up to 64), streamed
-    otherwise."""
+    eight tiles per compute unit, ten for a single block of 32 requests at
+    r = 256 (one grid barrier per block of 32 requests from 65 to 1024
+    requests, one per position up to 64), streamed otherwise."""
     from semi_ar_draft_round_amd import binding as B
     bf, f32 = torch.bfloat16, torch.float32
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 256).startswith("sample_steps_pipe")
@@ -358,5 +365,10 @@ def test_sampling_kernel_choice(dev):
     assert B.dspark_markov_sample_kernel(bf, 64, 16, 129280, 256).startswith("sample_steps_res")
     assert B.dspark_markov_sample_kernel(bf, 1, 16, 4096, 128).startswith("sample_steps_res")
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 151936, 256).startswith("sample_steps_wide")
+    assert B.dspark_markov_sample_kernel(bf, 1, 16, 151936, 256).startswith("sample_steps_res")
+    assert B.dspark_markov_sample_kernel(bf, 32, 16, 163840, 256).startswith("sample_steps_res")
+    assert B.dspark_markov_sample_kernel(bf, 32, 16, 163841, 256).startswith("sample_steps_wide")
+    assert B.dspark_markov_sample_kernel(bf, 33, 16, 151936, 256).startswith("sample_steps_wide")
+    assert B.dspark_markov_sample_kernel(bf, 1, 16, 151936, 128).startswith("sample_steps_wide")
     assert B.dspark_markov_sample_kernel(f32, 4, 3, 1000, 64).startswith("sample_step_f32")
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 96) is None
