@@ -36,6 +36,7 @@ def source_hash() -> str:
     """Hash of the sources the sampling launch is built from."""
     h = hashlib.sha256()
     for rel in ("semi_ar_draft_round_amd/csrc/sample.hip", "semi_ar_draft_round_amd/csrc/sample_res.hip",
+                "semi_ar_draft_round_amd/csrc/sample_pipe.hip",
                 "semi_ar_draft_round_amd/csrc/sample_common.hpp", "semi_ar_draft_round_amd/csrc/bias_tile.hpp",
                 "semi_ar_draft_round_amd/csrc/wide_tile.hpp", "semi_ar_draft_round_amd/csrc/common.hpp",
                 "semi_ar_draft_round_amd/csrc/sample_keys.hpp", "semi_ar_draft_round_amd/csrc/rnn_head.hpp",
