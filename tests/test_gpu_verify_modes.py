@@ -142,6 +142,9 @@ ACC_SMALL = [
     W.custom("acc_r70_g6_v4100_r64_bf16", R=70, gamma=6, V=4100, r=64, d=128, seed=33),
     W.custom("acc_r9_g7_v333_f32", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=34),
     W.custom("acc_r5_g64_v1000_bf16", R=5, gamma=64, V=1000, r=64, d=64, seed=35),
+    # the sweep that keeps W2t on chip: an odd number of 32-row blocks (9)
+    # over groups of two or three tiles, with 16-byte logit loads
+    W.custom("acc_r40_g7_v40000_r256_bf16", R=40, gamma=7, V=40000, r=256, d=64, seed=36),
 ]
 
 
