@@ -12,7 +12,7 @@
 namespace dspark {
 // sample.hip
 size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V);
-size_t rnn_workspace_bytes(int R, int r);
+size_t rnn_workspace_bytes(int R, int gamma, int r);
 // sts.hip
 size_t sts_workspace_bytes(int N, int gamma, int G, int M);
 bool sts_shape_ok(int N, int gamma, int G, int M);
@@ -133,7 +133,7 @@ static size_t sample_ws_any(int R, int gamma, int V) {
 
 // The sampler's workspace (256-byte aligned), then the RNN projection partials.
 static size_t rnn_sample_workspace_bytes(int R, int gamma, int V, int r) {
-  return ((sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255)) + rnn_workspace_bytes(R, r);
+  return ((sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255)) + rnn_workspace_bytes(R, gamma, r);
 }
 
 size_t dspark_workspace_size(dspark_ws_kind kind, int R, int gamma, int V, int r, int n_sps) {

@@ -6,21 +6,23 @@
 // W1[x_{k-1}]'s place.  The previous token comes from the sampler's argmax
 // keys of position k - 1 (the anchor at k = 0).
 //
-// bf16 storage: the projection runs on the matrix cores (32x32x16 MFMA,
-// fp32 accumulation) with z in bf16 -- its state part rounded from fp32 to
-// nearest, ties to even -- split along the inner dimension over kRnnSplits
-// work groups; a second kernel adds the partials in order and applies the
-// gates in fp32.  fp32 storage: one thread per output with fp32 FMAs.
+// bf16 storage: z enters the products in bf16 (its state part rounded from
+// fp32 to nearest, ties to even), with fp32 accumulation on the matrix
+// cores (32x32x16 MFMA).  The hidden-state part of y does not depend on the
+// loop: W_h h_k for every (request, position) is one matrix product, run
+// once before the first position (rnn_hproj_bf16, split along d into a few
+// partials).  Each position then multiplies only the state and W1-row parts
+// (2r of the 2r + d inner elements), adds the hidden-state partials in split
+// order and applies the gates in fp32, in one kernel (rnn_step_bf16).
+// fp32 storage: one thread per output with fp32 FMAs, then the gates.
 #include "bias_tile.hpp"
 #include "wide_tile.hpp"
 #include "rnn_head.hpp"
-#include "sample_keys.hpp"
+#include "sample_common.hpp"
 
 namespace dspark {
 
 typedef float f32x16_r __attribute__((ext_vector_type(16)));
-
-constexpr int kRnnThreads = 256;   // four waves split each work group's inner range
 
 // Round-to-nearest-even of an fp32 value to its bf16 bit pattern.
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
@@ -28,97 +30,291 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// Work group (jb, ib, sp): columns 32 jb .. 32 jb + 31 of each of the three
-// parts (gate, candidate, output), requests 32 ib .. 32 ib + 31, inner steps
-// of 16 in [sp * per, (sp + 1) * per), dealt out over the four waves.  Lane
-// (hh, j) brings weight row 32 jb + j of each part (the A operands) and z of
-// request 32 ib + j (the B operand), eight inner indices each.
-__global__ __launch_bounds__(kRnnThreads) void rnn_proj_bf16(int R, int gamma, int V, int r, int d, int k,
-                                                             const uint16_t* __restrict__ W,
+// ---- the hidden-state part, every position at once -------------------------
+//
+// Yh[sp][m][n] = sum over split sp's inner range of h[m][c] * W[n][2r + c]
+// (m = request * gamma + position, n < 3r).  A work group computes a
+// kHpBM x kHpBN block of one split: four waves, each 64 rows of h by the
+// block's 96 projection rows (2 x 3 MFMA tiles).  The inner range runs in
+// stages of kHpBK elements, double-buffered in LDS; a stage's loads are
+// issued into registers two stages before its products and written to the
+// free LDS buffer one stage before them.  In LDS a stage is 128 bytes
+// per row, in 1 KB blocks of 8 rows; the 16-byte piece c of row j sits at
+// slot c ^ (j mod 8), so each load instruction reads whole 128-byte lines,
+// each LDS write is 1 KB contiguous, and the fragment reads (row j, piece
+// 2t + half) hit eight different slots per eight lanes.
+constexpr int kHpBM = 256;
+constexpr int kHpBN = 96;
+constexpr int kHpBK = 64;
+constexpr int kHpThreads = 256;
+constexpr int kHpBlocks = (kHpBM + kHpBN) / 8;          // 1 KB copy blocks per stage
+constexpr int kHpCopies = kHpBlocks / (kHpThreads / kWave);   // per wave
+static_assert(kHpBlocks % (kHpThreads / kWave) == 0, "copy blocks must divide over the waves");
+
+// Splits of d: enough work groups to cover the compute units, at most
+// kHpMaxSplits.
+constexpr int kHpMaxSplits = 4;
+int hproj_max_splits(int64_t M, int r) {
+  const int64_t nN = 3 * r / kHpBN;   // 0 for the fp32 ranks that are not multiples of 32
+  const int64_t tiles = ((M + kHpBM - 1) / kHpBM) * (nN > 0 ? nN : 1);
+  const int64_t want = (256 + tiles - 1) / tiles;
+  return static_cast<int>(want < 1 ? 1 : want > kHpMaxSplits ? kHpMaxSplits : want);
+}
+
+struct HprojPlan {
+  int splits;   // partials actually written
+  int per;      // stages per split
+};
+
+HprojPlan hproj_plan(int64_t M, int r, int d) {
+  const int stages = ceil_div(d, kHpBK);
+  int sp = hproj_max_splits(M, r);
+  sp = sp < stages ? sp : stages;
+  const int per = ceil_div(stages, sp);
+  return HprojPlan{ceil_div(stages, per), per};
+}
+
+__device__ __forceinline__ bf16x8 hproj_frag(const uint8_t* buf, int row, int piece) {
+  return *reinterpret_cast<const bf16x8*>(buf + row * 128 + ((piece ^ (row & 7)) << 4));
+}
+
+// k-step t of a stage: the wave's 64 rows of h (A) by the 96 projection rows (B)
+__device__ __forceinline__ void hproj_kstep(const uint8_t* buf, f32x16_r (&acc)[2][3], int wave, int j, int hh, int t,
+                                            bool ok) {
+  bf16x8 a[2], bb[3];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const bf16x8 f = hproj_frag(buf, wave * 64 + mi * 32 + j, 2 * t + hh);
+    a[mi] = ok ? f : bf16x8{};
+  }
+#pragma unroll
+  for (int ni = 0; ni < 3; ++ni) {
+    const bf16x8 f = hproj_frag(buf, kHpBM + ni * 32 + j, 2 * t + hh);
+    bb[ni] = ok ? f : bf16x8{};
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 3; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], bb[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// A work-group barrier that waits for LDS traffic only (the copies into LDS
+// are waited for explicitly before it), so loads in flight stay in flight.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ __launch_bounds__(kHpThreads) void rnn_hproj_bf16(int M, int N, int d, int K, int nM, int nN, int per,
                                                              const uint16_t* __restrict__ h,
-                                                             const uint16_t* __restrict__ W1,
-                                                             const int32_t* __restrict__ x0,
-                                                             const unsigned long long* __restrict__ keys,
-                                                             const float* __restrict__ s, float* __restrict__ part,
-                                                             int per) {
-  __shared__ float red[3][kRnnThreads / kWave][16][kWave];
+                                                             const uint16_t* __restrict__ Wh,
+                                                             float* __restrict__ Yh) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[(kHpBM + kHpBN) * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[(kHpBM + kHpBN) * 128];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  // work groups that share an h block (same rows and split) are numbered so
+  // that they are dispatched to the same XCD (work group b goes to XCD b mod 8)
+  const int T = gridDim.x;
+  const int b = blockIdx.x;
+  const int g = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int nt = g % nN;
+  const int ms = g / nN;
+  const int mt = ms % nM;
+  const int sp = ms / nM;
+  const int m0 = mt * kHpBM, n0 = nt * kHpBN;
+  const int kb = sp * per * kHpBK;
+  const int ke = min(d, kb + per * kHpBK);
+  const int nst = ceil_div(ke - kb, kHpBK);
+  // the lane's load sources: block bi = wave + 4 c (rows of h first, then of W)
+  const int rib = lane >> 3;
+  const int piece = (lane & 7) ^ rib;
+  const uint16_t* src[kHpCopies];
+#pragma unroll
+  for (int c = 0; c < kHpCopies; ++c) {
+    const int bi = wave + 4 * c;
+    if (bi < kHpBM / 8) {
+      const int m = min(m0 + 8 * bi + rib, M - 1);
+      src[c] = h + static_cast<int64_t>(m) * d + kb;
+    } else {
+      src[c] = Wh + static_cast<int64_t>(n0 + 8 * (bi - kHpBM / 8) + rib) * K + kb;
+    }
+  }
+  const int j = lane & 31, hh = lane >> 5;
+  f32x16_r acc[2][3] = {};
+  auto koff = [&](int st) {
+    const int o = st * kHpBK + piece * 8;
+    return kb + o < ke ? o : st * kHpBK;   // a piece past the range loads a valid one; its k-step is zeroed
+  };
+  // a stage's k-steps; only the last stage of a split can hold k-steps past
+  // its range (d a multiple of 16, not of 64), and those multiply zeros
+  // (selected without a branch)
+  auto compute = [&](const uint8_t* buf, int st) {
+    const int valid = (ke - kb - st * kHpBK) >> 4;
+#pragma unroll
+    for (int t = 0; t < kHpBK / 16; ++t) hproj_kstep(buf, acc, wave, j, hh, t, t < valid);
+  };
+  // two register sets: each stage's loads are issued two stages before its
+  // products, written to LDS one stage before them
+  u32x4 stgA[kHpCopies], stgB[kHpCopies];
+  auto load_stage = [&](u32x4 (&stg)[kHpCopies], int st) {
+    const int o = koff(st);
+#pragma unroll
+    for (int c = 0; c < kHpCopies; ++c) stg[c] = *reinterpret_cast<const u32x4*>(src[c] + o);
+  };
+  auto store_stage = [&](const u32x4 (&stg)[kHpCopies], uint8_t* buf) {
+#pragma unroll
+    for (int c = 0; c < kHpCopies; ++c) *reinterpret_cast<u32x4*>(buf + (wave + 4 * c) * 1024 + lane * 16) = stg[c];
+  };
+  // The loop body is one basic block: the stage count is rounded up to even
+  // (a stage past the range multiplies zeros) and the loads are
+  // unconditional (past the last stage they repeat it), so the compiler
+  // neither sinks a load to its use nor waits for the younger register set
+  // before an LDS write.
+  load_stage(stgA, 0);
+  load_stage(stgB, min(1, nst - 1));
+  store_stage(stgA, buf0);
+  lds_sync();
+  for (int st = 0; st < nst; st += 2) {
+    // buf0 holds stage st, stgB stage st + 1 (in flight); stage st + 2 goes to stgA
+    load_stage(stgA, min(st + 2, nst - 1));
+    compute(buf0, st);
+    store_stage(stgB, buf1);
+    lds_sync();
+    load_stage(stgB, min(st + 3, nst - 1));
+    compute(buf1, st + 1);
+    store_stage(stgA, buf0);
+    lds_sync();
+  }
+  float* out = Yh + static_cast<int64_t>(sp) * M * N;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int m = m0 + wave * 64 + mi * 32 + 8 * (q >> 2) + 4 * hh + (q & 3);
+      if (m < M)
+#pragma unroll
+        for (int ni = 0; ni < 3; ++ni) out[static_cast<int64_t>(m) * N + n0 + ni * 32 + j] = acc[mi][ni][q];
+    }
+}
+
+// ---- one position: the state and W1-row parts, the sum, the gates ----------
+//
+// Work group (jb, ib): state columns 32 jb .. 32 jb + 31 (rows of each of
+// the three parts of W) for requests 32 ib .. 32 ib + 31.  Wave w takes the
+// k-steps w, w + 4, ... of the 2r/16 over [s_{k-1}; W1[x_{k-1}]]; lane (hh,
+// j) brings weight row 32 jb + j of each part (the A operands) and z of
+// request 32 ib + j (the B operand).  Everything that does not wait on the
+// previous token -- the weight fragments, the state fragments, the
+// hidden-state partials and s_{k-1} for the gates -- is loaded before the
+// keys are read.  The waves' sums meet in LDS; thread e then finishes
+// (request 32 ib + e / 32, column 32 jb + e % 32), four per thread.
+template <int NS>   // k-steps per wave: r / 32
+__global__ __launch_bounds__(256) void rnn_step_bf16(int R, int gamma, int V, int d, int k, int S, int64_t M,
+                                                      const uint16_t* __restrict__ W,
+                                                      const uint16_t* __restrict__ W1,
+                                                      const int32_t* __restrict__ x0,
+                                                      const unsigned long long* __restrict__ keys,
+                                                      const float* __restrict__ Yh, float* __restrict__ s,
+                                                      uint16_t* __restrict__ o) {
+  constexpr int r = NS * 32;
+  constexpr int kHalf = r / 16;   // k-steps of the state part
+  __shared__ float red[3][4][16][kWave];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int j = lane & 31;
   const int hh = lane >> 5;
-  const int jb = blockIdx.x, ib = blockIdx.y, sp = blockIdx.z;
+  const int jb = blockIdx.x, ib = blockIdx.y;
   const int K = 2 * r + d;
-  const int i = ib * 32 + j;
-  const int ic = min(i, R - 1);
-  const int st1 = min(K / 16, (sp + 1) * per);
+  const int ic = min(ib * 32 + j, R - 1);
+  // the gates' inputs that need no token, all loads issued together (a
+  // split past S reads split 0 and adds nothing)
+  float yp[4][3][kHpMaxSplits], sprev[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int rq = min(ib * 32 + (e >> 5), R - 1);
+    const int64_t row = static_cast<int64_t>(rq) * gamma + k;
+    const int col = jb * 32 + (e & 31);
+#pragma unroll
+    for (int g = 0; g < 3; ++g)
+#pragma unroll
+      for (int sp = 0; sp < kHpMaxSplits; ++sp)
+        yp[u][g][sp] = Yh[((sp < S ? sp : 0) * M + row) * (3 * r) + g * r + col];
+    sprev[u] = s[(k > 0 ? row - 1 : row) * r + col];   // read at k = 0 too (any value; unused)
+  }
+  bf16x8 a[NS][3], bz[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int kk = (wave + 4 * u) * 16 + 8 * hh;
+#pragma unroll
+    for (int g = 0; g < 3; ++g)
+      a[u][g] = load_bf16x8_global(W + static_cast<int64_t>(g * r + jb * 32 + j) * K + kk);
+  }
+  // the state part, loaded for every k-step without a branch (a k-step of
+  // the W1-row part reads the state row's start and is replaced below)
+  const float* srow = s + (static_cast<int64_t>(ic) * gamma + (k > 0 ? k - 1 : 0)) * r;
+  float4 sv[NS][2];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int st = wave + 4 * u;
+    const int kk = st < kHalf ? st * 16 + 8 * hh : 0;
+    sv[u][0] = *reinterpret_cast<const float4*>(srow + kk);
+    sv[u][1] = *reinterpret_cast<const float4*>(srow + kk + 4);
+  }
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const float4 lo = sv[u][0], hi = sv[u][1];
+    const uint32_t w0 = bf16_bits_rne(lo.x) | (bf16_bits_rne(lo.y) << 16);
+    const uint32_t w1 = bf16_bits_rne(lo.z) | (bf16_bits_rne(lo.w) << 16);
+    const uint32_t w2 = bf16_bits_rne(hi.x) | (bf16_bits_rne(hi.y) << 16);
+    const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
+    const bf16x8 v = __builtin_bit_cast(bf16x8, (uint4{w0, w1, w2, w3}));
+    bz[u] = k > 0 ? v : bf16x8{};   // z's state part is zero at the first position
+  }
   const int prev = previous_token(keys, kKeySlots, x0, R, V, k, ic);
-  const float* srow = s + (static_cast<int64_t>(ic) * gamma + (k > 0 ? k - 1 : 0)) * r;   // read when k > 0
   const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
-  const uint16_t* hrow = h + (static_cast<int64_t>(ic) * gamma + k) * d;
-  const uint16_t* wrow[3];
 #pragma unroll
-  for (int g = 0; g < 3; ++g) wrow[g] = W + static_cast<int64_t>(g * r + jb * 32 + j) * K;
+  for (int u = 0; u < NS; ++u) {
+    const int st = wave + 4 * u;
+    const bf16x8 v = load_bf16x8_global(erow + (st >= kHalf ? st * 16 + 8 * hh - r : 0));
+    if (st >= kHalf) bz[u] = v;
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every W1-row load issued before the first product
   f32x16_r acc[3] = {};
-  constexpr int kW = kRnnThreads / kWave;   // waves; the wave takes every kW-th step of the range
-  constexpr int kU = 4;                     // steps whose operands are in flight together
-  // the wave's steps of [lo, hi) within this work group's range, kU at a time:
-  // every load of a batch is issued before its products; a step past the
-  // range reloads a valid one and multiplies a zero B operand
-  auto run = [&](int lo, int hi, auto&& zfrag) {
-    lo = max(lo, sp * per);
-    hi = min(hi, st1);
-    int st = sp * per + wave;
-    if (st < lo) st += ceil_div(lo - st, kW) * kW;
-    for (; st < hi; st += kU * kW) {
-      bf16x8 a[kU][3], bz[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int su = st + u * kW < hi ? st + u * kW : st;
-        const int kk = su * 16 + 8 * hh;
-        bz[u] = zfrag(kk);
+  for (int u = 0; u < NS; ++u)
 #pragma unroll
-        for (int g = 0; g < 3; ++g) a[u][g] = load_bf16x8_global(wrow[g] + kk);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const bf16x8 bu = st + u * kW < hi ? bz[u] : bf16x8{};
-#pragma unroll
-        for (int g = 0; g < 3; ++g)
-          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][g], bu, acc[g], 0, 0, 0);
-      }
-    }
-  };
-  // the hidden state first, then z's state part (zero at the first
-  // position; rounded from fp32 to bf16), then the previous token's W1 row
-  // (a row of zeros when there is none), whose address waits on the keys
-  run(2 * r / 16, K / 16, [&](int kk) { return load_bf16x8_global(hrow + kk - 2 * r); });
-  if (k > 0)
-    run(0, r / 16, [&](int kk) {
-      const float4 lo = *reinterpret_cast<const float4*>(srow + kk);
-      const float4 hi = *reinterpret_cast<const float4*>(srow + kk + 4);
-      const uint32_t w0 = bf16_bits_rne(lo.x) | (bf16_bits_rne(lo.y) << 16);
-      const uint32_t w1 = bf16_bits_rne(lo.z) | (bf16_bits_rne(lo.w) << 16);
-      const uint32_t w2 = bf16_bits_rne(hi.x) | (bf16_bits_rne(hi.y) << 16);
-      const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
-      return __builtin_bit_cast(bf16x8, (uint4{w0, w1, w2, w3}));
-    });
-  run(r / 16, 2 * r / 16, [&](int kk) { return load_bf16x8_global(erow + kk - r); });
+    for (int g = 0; g < 3; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][g], bz[u], acc[g], 0, 0, 0);
 #pragma unroll
   for (int g = 0; g < 3; ++g)
 #pragma unroll
     for (int q = 0; q < 16; ++q) red[g][wave][q][lane] = acc[g][q];
   __syncthreads();
-  // output element (g, q, lane): part row 32 jb + 8 (q / 4) + 4 (lane / 32) + q % 4 of part g, request
-  // 32 ib + lane % 32
-  for (int e = threadIdx.x; e < 3 * 16 * kWave; e += kRnnThreads) {
-    const int g = e / (16 * kWave), q = (e / kWave) % 16, l = e % kWave;
-    float t = 0.f;
+  // accumulator q of lane l holds weight row 8 (q / 4) + 4 (l / 32) + q % 4
+  // of the block and request l % 32
 #pragma unroll
-    for (int w = 0; w < kRnnThreads / kWave; ++w) t += red[g][w][q][l];
-    const int req = ib * 32 + (l & 31);
-    const int col = jb * 32 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
-    if (req < R) part[(static_cast<int64_t>(sp) * R + req) * 3 * r + g * r + col] = t;
+  for (int u = 0; u < 4; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int rl = e >> 5, c = e & 31;
+    const int q = ((c >> 3) << 2) | (c & 3);
+    const int l = (((c >> 2) & 1) << 5) | rl;
+    float y[3];
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      float t = yp[u][g][0];
+#pragma unroll
+      for (int sp = 1; sp < kHpMaxSplits; ++sp)
+        if (sp < S) t += yp[u][g][sp];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t += red[g][w][q][l];
+      y[g] = t;
+    }
+    const int req = ib * 32 + rl;
+    if (req < R) {
+      const int64_t idx = (static_cast<int64_t>(req) * gamma + k) * r + jb * 32 + c;
+      const float gate = 1.f / (1.f + expf(-y[0]));
+      s[idx] = gate * (k > 0 ? sprev[u] : 0.f) + (1.f - gate) * tanhf(y[1]);
+      o[idx] = static_cast<uint16_t>(bf16_bits_rne(tanhf(y[2])));
+    }
   }
 }
 
@@ -180,17 +376,41 @@ __global__ __launch_bounds__(256) void rnn_gate(int R, int gamma, int r, int k, 
 hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& hd, int R, int gamma, int V, int r, int k,
                            const void* W1, const int32_t* x0, const unsigned long long* keys, hipStream_t s) {
   const int K = 2 * r + hd.d;
-  const int nthreads = ceil_div(static_cast<int64_t>(R) * r, 256);
   if (dt == DSPARK_BF16) {
-    const int per = ceil_div(K / 16, kRnnSplits);
-    hipLaunchKernelGGL(rnn_proj_bf16, dim3(r / 32, ceil_div(R, 32), kRnnSplits), dim3(kRnnThreads), 0, s, R, gamma,
-                       V, r, hd.d, k, static_cast<const uint16_t*>(hd.W), static_cast<const uint16_t*>(hd.h),
-                       static_cast<const uint16_t*>(W1), x0, keys, hd.s, hd.part, per);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(rnn_gate<BF16>, dim3(nthreads), dim3(256), 0, s, R, gamma, r, k, kRnnSplits, hd.part, hd.s,
-                       static_cast<uint16_t*>(hd.o));
+    const int64_t M = static_cast<int64_t>(R) * gamma;
+    const HprojPlan pl = hproj_plan(M, r, hd.d);
+    if (k == 0) {
+      const int nM = ceil_div(M, kHpBM), nN = 3 * r / kHpBN;
+      hipLaunchKernelGGL(rnn_hproj_bf16, dim3(nM * nN * pl.splits), dim3(kHpThreads), 0, s, static_cast<int>(M),
+                         3 * r, hd.d, K, nM, nN, pl.per, static_cast<const uint16_t*>(hd.h),
+                         static_cast<const uint16_t*>(hd.W) + 2 * r, hd.part);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+    const dim3 grid(r / 32, ceil_div(R, 32));
+    const uint16_t* Wb = static_cast<const uint16_t*>(hd.W);
+    const uint16_t* W1b = static_cast<const uint16_t*>(W1);
+    uint16_t* ob = static_cast<uint16_t*>(hd.o);
+    switch (r) {
+      case 32:
+        hipLaunchKernelGGL(rnn_step_bf16<1>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+                           keys, hd.part, hd.s, ob);
+        break;
+      case 64:
+        hipLaunchKernelGGL(rnn_step_bf16<2>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+                           keys, hd.part, hd.s, ob);
+        break;
+      case 128:
+        hipLaunchKernelGGL(rnn_step_bf16<4>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+                           keys, hd.part, hd.s, ob);
+        break;
+      default:
+        hipLaunchKernelGGL(rnn_step_bf16<8>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+                           keys, hd.part, hd.s, ob);
+        break;
+    }
   } else {
+    const int nthreads = ceil_div(static_cast<int64_t>(R) * r, 256);
     hipLaunchKernelGGL(rnn_proj_f32, dim3(ceil_div(static_cast<int64_t>(R) * 3 * r, 256)), dim3(256), 0, s, R,
                        gamma, V, r, hd.d, k, static_cast<const float*>(hd.W), static_cast<const float*>(hd.h),
                        static_cast<const float*>(W1), x0, keys, hd.s, hd.part);
@@ -202,8 +422,13 @@ hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& hd, int R, int gamma,
   return hipGetLastError();
 }
 
-size_t rnn_workspace_bytes(int R, int r) {
-  return (sizeof(float) * static_cast<size_t>(kRnnSplits) * R * 3 * r + 255) & ~static_cast<size_t>(255);
+// bf16: the hidden-state partials [splits][R gamma][3r]; fp32: the
+// projection of one position [R][3r].
+size_t rnn_workspace_bytes(int R, int gamma, int r) {
+  const int64_t M = static_cast<int64_t>(R) * gamma;
+  const size_t a = sizeof(float) * static_cast<size_t>(hproj_max_splits(M, r)) * M * 3 * r;
+  const size_t b = sizeof(float) * static_cast<size_t>(R) * 3 * r;
+  return ((a > b ? a : b) + 255) & ~static_cast<size_t>(255);
 }
 
 }  // namespace dspark

@@ -70,6 +70,16 @@ def test_workspace_sizes(lib):
     assert B.dspark_workspace_size(B.WS_SCHEDULE, 128, 16, 0, 0) == 8 * 128 * 16
     assert B.dspark_workspace_size(B.WS_SCHEDULE, 3, 5, 0, 0) == 256
     assert B.dspark_workspace_size(B.WS_SCHEDULE, 482, 16, 0, 0) == 0   # 482 * 17 > 8191
+    # the RNN head adds the hidden-state projection's partials for every
+    # (request, position), [splits][R gamma][3r] f32 (bf16 ranks; 4 splits at
+    # R gamma = 2048, r = 256: 64 blocks of 256 x 96 fill the compute units
+    # four times over), or one position's [R][3r] f32 (fp32 ranks of any size)
+    base = B.dspark_workspace_size(B.WS_SAMPLE, 128, 16, 129280, 256)
+    base = (base + 255) // 256 * 256
+    assert B.dspark_workspace_size(B.WS_RNN_SAMPLE, 128, 16, 129280, 256) == base + 4 * 4 * 2048 * 768
+    for r in (1, 20, 33, 1024):
+        base = (B.dspark_workspace_size(B.WS_SAMPLE, 9, 7, 333, r) + 255) // 256 * 256
+        assert B.dspark_workspace_size(B.WS_RNN_SAMPLE, 9, 7, 333, r) >= base + 4 * 9 * 3 * r
 
 
 P = ctypes.c_void_p
