@@ -82,6 +82,21 @@ __device__ __forceinline__ int key_token(unsigned long long key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key & 0xFFFFFFFFull));
 }
 
+// The value held by the lane 32 positions away (lane l and lane l ^ 32),
+// with v_permlane32_swap: a vector permute, no LDS round trip.  The swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, so with both operands x the first result holds x[l - 32] in the
+// upper lanes and the second x[l + 32] in the lower lanes.
+__device__ __forceinline__ uint32_t xor32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float xor32(float x) { return __uint_as_float(xor32(__float_as_uint(x))); }
+__device__ __forceinline__ unsigned long long xor32(unsigned long long x) {
+  return (static_cast<unsigned long long>(xor32(static_cast<uint32_t>(x >> 32))) << 32) |
+         xor32(static_cast<uint32_t>(x));
+}
+
 __device__ __forceinline__ float wave_reduce_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);

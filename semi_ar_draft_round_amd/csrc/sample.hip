@@ -486,7 +486,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void sample_steps_wide(
       Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);
       M2 = Mn;
     };
-    merge(__shfl_xor(key, 32), __shfl_xor(M2, 32), __shfl_xor(Ts, 32));
+    merge(xor32(key), xor32(M2), xor32(Ts));
     if (th == 1 && h == 0) {
       lsh[loc] = make_float2(M2, Ts);
       ksh[loc] = key;

@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
     float Ts = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) Ts += M2[q] == neg_inf() ? 0.f : T[q] * __builtin_amdgcn_exp2f(M2[q] - M);
-    const unsigned long long ko = __shfl_xor(key, 32);
-    const float Mo = __shfl_xor(M, 32), To = __shfl_xor(Ts, 32);
+    const unsigned long long ko = xor32(key);
+    const float Mo = xor32(M), To = xor32(Ts);
     key = ko > key ? ko : key;
     const float Mn = fmaxf(M, Mo);
     Ts = (M == neg_inf() ? 0.f : Ts * __builtin_amdgcn_exp2f(M - Mn)) + (Mo == neg_inf() ? 0.f : To * __builtin_amdgcn_exp2f(Mo - Mn));
@@ -206,10 +206,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
     return (__builtin_amdgcn_readlane(v, kBarGroups) | __builtin_amdgcn_readlane(v, kBarGroups + 1)) != 0u;
   };
   auto sum8 = [&](uint32_t v) {
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
-    return __builtin_amdgcn_readfirstlane(v);
+    uint32_t t = __builtin_amdgcn_readlane(v, 0);
+#pragma unroll
+    for (int l = 1; l < kBarGroups; ++l) t += __builtin_amdgcn_readlane(v, l);
+    return t;
   };
   // consumer, start of step c - 1: every work group has arrived for the
   // block at position k - 1 (wait, bounded, only if not yet); then load the
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
       unsigned long long b = kr[0];
 #pragma unroll
       for (int q = 1; q < kHalfSlots; ++q) b = kr[q] > b ? kr[q] : b;
-      const unsigned long long o = __shfl_xor(b, 32);
+      const unsigned long long o = xor32(b);
       b = o > b ? o : b;
       tok = 32 * rb + j < R ? token_or_none(key_token(b), V) : -1;
     }
@@ -361,8 +361,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void sample_steps_pipe(
       unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
       float M2 = dr.M2, Ts = dr.T;
       {   // the request's other lane (h ^ 1)
-        const unsigned long long ok = __shfl_xor(key, 32);
-        const float M2o = __shfl_xor(M2, 32), To = __shfl_xor(Ts, 32);
+        const unsigned long long ok = xor32(key);
+        const float M2o = xor32(M2), To = xor32(Ts);
         key = ok > key ? ok : key;
         const float Mn = fmaxf(M2, M2o);
         Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);

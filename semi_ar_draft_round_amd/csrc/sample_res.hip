@@ -265,8 +265,8 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     unsigned long long key = (dr.first >= 0 && bs > neg_inf()) ? pack_key(dr.best, dr.first + bo) : 0ull;
     float M2 = dr.M2, Ts = dr.T;
     {   // the request's other lane (h ^ 1)
-      const unsigned long long ok = __shfl_xor(key, 32);
-      const float M2o = __shfl_xor(M2, 32), To = __shfl_xor(Ts, 32);
+      const unsigned long long ok = xor32(key);
+      const float M2o = xor32(M2), To = xor32(Ts);
       key = ok > key ? ok : key;
       const float Mn = fmaxf(M2, M2o);
       Ts = Ts * __builtin_amdgcn_exp2f(M2 - Mn) + To * __builtin_amdgcn_exp2f(M2o - Mn);

@@ -582,7 +582,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     }
   }
   if constexpr (ACC) {
-    const float t = mn + __shfl_xor(mn, 32);   // the request's two lanes of this token half
+    const float t = mn + xor32(mn);   // the request's two lanes of this token half
     if (th == 1 && h == 0) accsh[rq * 32 + j] = t;
     __syncthreads();
     if (th == 0 && h == 0 && live)
