@@ -124,6 +124,9 @@ def traffic_record(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
+kEagerSkip = 60   # eager rounds run before the counted ones (about 25 ms of work)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +225,27 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps       # ms per replay
 
+    # the persistent sampling launch alone: eager rounds (the same calls as
+    # the graph, the same alternation of input sets), with the sampling call
+    # stamping two HIP events with that launch's start and end on its stream
+    # (the first kEagerSkip rounds are not counted: after the idle spell of
+    # graph capture the GPU's clocks take a few milliseconds of work to
+    # settle); each counted round has its own event pair, read after the
+    # last round, so the host never waits between rounds
+    timers = [binding.SweepTimer() for _ in range(max(args.steps, 10))]
+    for i in range(len(timers) + kEagerSkip):
+        d = rounds[i % 2]
+        DR.sample_conf(d, timer=timers[i - kEagerSkip] if i >= kEagerSkip else None)
+        DR.schedule(d)
+        DR.verify(d)
+    torch.cuda.synchronize()
+    sweeps = [t.elapsed_ms() * 1e3 for t in timers]
+    sweep_us = float(np.mean(sweeps))
+    log(f"[bench] persistent sampling launch: mean {sweep_us:.1f} us over {len(sweeps)} eager rounds "
+        f"(min {min(sweeps):.1f}, max {max(sweeps):.1f})")
+    # the round itself, timed after the eager rounds above: the GPU has then
+    # been busy for a while, so its clocks have settled (after an idle spell
+    # the first few rounds run several per cent slower)
     ms = timed("round", args.steps, args.warmup)
     log(f"[bench] round: {ms * 1e3:.1f} us")
     # the spread of single rounds, each bracketed by its own events (a second
@@ -241,22 +265,6 @@ def main():
     for name in ("sample_conf", "schedule", "verify"):
         parts[name] = timed(name, max(args.steps, 10), 2) * 1e3
         log(f"[bench] {name}: {parts[name]:.1f} us")
-    # the persistent sampling launch alone: eager rounds (the same calls as
-    # the graph, the same alternation of input sets), with the sampling call
-    # stamping two HIP events with that launch's start and end on its stream
-    timer = binding.SweepTimer()
-    sweeps = []
-    for i in range(max(args.steps, 10) + 2):
-        d = rounds[i % 2]
-        DR.sample_conf(d, timer=timer)
-        DR.schedule(d)
-        DR.verify(d)
-        if i >= 2:
-            sweeps.append(timer.elapsed_ms() * 1e3)
-    torch.cuda.synchronize()
-    sweep_us = float(np.mean(sweeps))
-    log(f"[bench] persistent sampling launch: mean {sweep_us:.1f} us over {len(sweeps)} eager rounds "
-        f"(min {min(sweeps):.1f}, max {max(sweeps):.1f})")
     # the other modes, each timed on its own and outside the round: the
     # sampling call without and the confidence head as a call of its own, the
     # production (asynchronous) scheduler's two calls, greedy verification of
