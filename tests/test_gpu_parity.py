@@ -195,7 +195,7 @@ def test_free_running_round_equals_oracle_round(dev):
         np.testing.assert_allclose(out["c"], ref["c"], rtol=1e-5)
 
 
-@pytest.mark.parametrize("R", [24, 100])
+@pytest.mark.parametrize("R", [24, 100, 200])
 def test_cancelled_sampler_reports_time_out(R, dev):
     """dspark_markov_sample_ex with its cancel word set: the persistent
     launch's grid-barrier waits give up at once (every work group exits
