@@ -60,6 +60,10 @@ SMALL = [
     # of 8 at 7 blocks
     W.custom("pipe_r96_g5_v40000_r256_bf16", R=96, gamma=5, V=40000, r=256, d=64, seed=23),
     W.custom("pipe_r200_g3_v20000_r256_bf16", R=200, gamma=3, V=20000, r=256, d=64, seed=24),
+    # the per-block kernel at r = 32 (every k-step in registers), and at its
+    # largest batch, 32 blocks
+    W.custom("pipe_r100_g5_v3000_r32_bf16", R=100, gamma=5, V=3000, r=32, d=64, seed=28),
+    W.custom("pipe_r1024_g2_v640_r64_bf16", R=1024, gamma=2, V=640, r=64, d=64, seed=29),
     # single request blocks with more than eight tiles per compute unit (the
     # resident kernel's LDS-held ninth and tenth tiles): some groups with a
     # ninth tile, every group with ten (the largest vocabulary it takes),
@@ -362,6 +366,8 @@ def test_sampling_kernel_choice(dev):
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 129280, 256).startswith("sample_steps_pipe")
     assert B.dspark_markov_sample_kernel(bf, 256, 16, 129280, 256).startswith("sample_steps_pipe")
     assert B.dspark_markov_sample_kernel(bf, 65, 16, 129280, 256).startswith("sample_steps_pipe")
+    assert B.dspark_markov_sample_kernel(bf, 1024, 2, 640, 64).startswith("sample_steps_pipe")
+    assert B.dspark_markov_sample_kernel(bf, 1025, 2, 640, 64).startswith("sample_steps_wide")
     assert B.dspark_markov_sample_kernel(bf, 64, 16, 129280, 256).startswith("sample_steps_res")
     assert B.dspark_markov_sample_kernel(bf, 1, 16, 4096, 128).startswith("sample_steps_res")
     assert B.dspark_markov_sample_kernel(bf, 128, 16, 151936, 256).startswith("sample_steps_wide")
