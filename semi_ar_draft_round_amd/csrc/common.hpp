@@ -36,6 +36,12 @@ struct BF16 {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Round-to-nearest-even of an fp32 value to its bf16 bit pattern.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
 // Online log-sum-exp state: value = M + log(S).
 struct Lse {
   float M, S;

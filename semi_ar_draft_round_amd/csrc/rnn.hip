@@ -11,9 +11,10 @@
 // cores (32x32x16 MFMA).  The hidden-state part of y does not depend on the
 // loop: W_h h_k for every (request, position) is one matrix product, run
 // once before the first position (rnn_hproj_bf16, split along d into a few
-// partials).  Each position then multiplies only the state and W1-row parts
-// (2r of the 2r + d inner elements), adds the hidden-state partials in split
-// order and applies the gates in fp32, in one kernel (rnn_step_bf16).
+// partials that rnn_hsum then adds in split order).  Each position then
+// multiplies only the state and W1-row parts (2r of the 2r + d inner
+// elements), adds the hidden-state part and applies the gates in fp32, in
+// one kernel (rnn_step_bf16).
 // fp32 storage: one thread per output with fp32 FMAs, then the gates.
 #include "bias_tile.hpp"
 #include "wide_tile.hpp"
@@ -24,11 +25,6 @@ namespace dspark {
 
 typedef float f32x16_r __attribute__((ext_vector_type(16)));
 
-// Round-to-nearest-even of an fp32 value to its bf16 bit pattern.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
 
 // ---- the hidden-state part, every position at once -------------------------
 //
@@ -208,7 +204,7 @@ __global__ __launch_bounds__(kHpThreads) void rnn_hproj_bf16(int M, int N, int d
 // keys are read.  The waves' sums meet in LDS; thread e then finishes
 // (request 32 ib + e / 32, column 32 jb + e % 32), four per thread.
 template <int NS>   // k-steps per wave: r / 32
-__global__ __launch_bounds__(256) void rnn_step_bf16(int R, int gamma, int V, int d, int k, int S, int64_t M,
+__global__ __launch_bounds__(256) void rnn_step_bf16(int R, int gamma, int V, int d, int k,
                                                       const uint16_t* __restrict__ W,
                                                       const uint16_t* __restrict__ W1,
                                                       const int32_t* __restrict__ x0,
@@ -225,9 +221,8 @@ __global__ __launch_bounds__(256) void rnn_step_bf16(int R, int gamma, int V, in
   const int jb = blockIdx.x, ib = blockIdx.y;
   const int K = 2 * r + d;
   const int ic = min(ib * 32 + j, R - 1);
-  // the gates' inputs that need no token, all loads issued together (a
-  // split past S reads split 0 and adds nothing)
-  float yp[4][3][kHpMaxSplits], sprev[4];
+  // the gates' inputs that need no token, loaded first
+  float yh[4][3], sprev[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int e = threadIdx.x + 256 * u;
@@ -235,10 +230,7 @@ __global__ __launch_bounds__(256) void rnn_step_bf16(int R, int gamma, int V, in
     const int64_t row = static_cast<int64_t>(rq) * gamma + k;
     const int col = jb * 32 + (e & 31);
 #pragma unroll
-    for (int g = 0; g < 3; ++g)
-#pragma unroll
-      for (int sp = 0; sp < kHpMaxSplits; ++sp)
-        yp[u][g][sp] = Yh[((sp < S ? sp : 0) * M + row) * (3 * r) + g * r + col];
+    for (int g = 0; g < 3; ++g) yh[u][g] = Yh[row * (3 * r) + g * r + col];
     sprev[u] = s[(k > 0 ? row - 1 : row) * r + col];   // read at k = 0 too (any value; unused)
   }
   bf16x8 a[NS][3], bz[NS];
@@ -300,10 +292,7 @@ __global__ __launch_bounds__(256) void rnn_step_bf16(int R, int gamma, int V, in
     float y[3];
 #pragma unroll
     for (int g = 0; g < 3; ++g) {
-      float t = yp[u][g][0];
-#pragma unroll
-      for (int sp = 1; sp < kHpMaxSplits; ++sp)
-        if (sp < S) t += yp[u][g][sp];
+      float t = yh[u][g];
 #pragma unroll
       for (int w = 0; w < 4; ++w) t += red[g][w][q][l];
       y[g] = t;
@@ -373,18 +362,45 @@ __global__ __launch_bounds__(256) void rnn_gate(int R, int gamma, int r, int k, 
     o[row * r + jj] = ov;
 }
 
+// The partials summed in split order into the first: float4 per thread.
+__global__ __launch_bounds__(256) void rnn_hsum(int64_t n4, int S, float4* __restrict__ Yh) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 t = Yh[i];
+  for (int sp = 1; sp < S; ++sp) {
+    const float4 v = Yh[sp * n4 + i];
+    t.x += v.x;
+    t.y += v.y;
+    t.z += v.z;
+    t.w += v.w;
+  }
+  Yh[i] = t;
+}
+
+// bf16: the hidden-state part of the projection for every position
+// (rnn_hproj_bf16) into hd.part, its split partials then summed in order
+// into the first (rnn_hsum), so the per-position kernels read one value.
+hipError_t rnn_hproj_launch(const RnnHead& hd, int R, int gamma, int r, hipStream_t s) {
+  const int K = 2 * r + hd.d;
+  const int64_t M = static_cast<int64_t>(R) * gamma;
+  const HprojPlan pl = hproj_plan(M, r, hd.d);
+  const int nM = ceil_div(M, kHpBM), nN = 3 * r / kHpBN;
+  hipLaunchKernelGGL(rnn_hproj_bf16, dim3(nM * nN * pl.splits), dim3(kHpThreads), 0, s, static_cast<int>(M), 3 * r,
+                     hd.d, K, nM, nN, pl.per, static_cast<const uint16_t*>(hd.h),
+                     static_cast<const uint16_t*>(hd.W) + 2 * r, hd.part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || pl.splits == 1) return err;
+  const int64_t n4 = M * 3 * r / 4;   // 3r is a multiple of 4
+  hipLaunchKernelGGL(rnn_hsum, dim3(ceil_div(n4, 256)), dim3(256), 0, s, n4, pl.splits,
+                     reinterpret_cast<float4*>(hd.part));
+  return hipGetLastError();
+}
+
 hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& hd, int R, int gamma, int V, int r, int k,
                            const void* W1, const int32_t* x0, const unsigned long long* keys, hipStream_t s) {
-  const int K = 2 * r + hd.d;
   if (dt == DSPARK_BF16) {
-    const int64_t M = static_cast<int64_t>(R) * gamma;
-    const HprojPlan pl = hproj_plan(M, r, hd.d);
     if (k == 0) {
-      const int nM = ceil_div(M, kHpBM), nN = 3 * r / kHpBN;
-      hipLaunchKernelGGL(rnn_hproj_bf16, dim3(nM * nN * pl.splits), dim3(kHpThreads), 0, s, static_cast<int>(M),
-                         3 * r, hd.d, K, nM, nN, pl.per, static_cast<const uint16_t*>(hd.h),
-                         static_cast<const uint16_t*>(hd.W) + 2 * r, hd.part);
-      hipError_t err = hipGetLastError();
+      hipError_t err = rnn_hproj_launch(hd, R, gamma, r, s);
       if (err != hipSuccess) return err;
     }
     const dim3 grid(r / 32, ceil_div(R, 32));
@@ -393,19 +409,19 @@ hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& hd, int R, int gamma,
     uint16_t* ob = static_cast<uint16_t*>(hd.o);
     switch (r) {
       case 32:
-        hipLaunchKernelGGL(rnn_step_bf16<1>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+        hipLaunchKernelGGL(rnn_step_bf16<1>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, Wb, W1b, x0,
                            keys, hd.part, hd.s, ob);
         break;
       case 64:
-        hipLaunchKernelGGL(rnn_step_bf16<2>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+        hipLaunchKernelGGL(rnn_step_bf16<2>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, Wb, W1b, x0,
                            keys, hd.part, hd.s, ob);
         break;
       case 128:
-        hipLaunchKernelGGL(rnn_step_bf16<4>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+        hipLaunchKernelGGL(rnn_step_bf16<4>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, Wb, W1b, x0,
                            keys, hd.part, hd.s, ob);
         break;
       default:
-        hipLaunchKernelGGL(rnn_step_bf16<8>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, pl.splits, M, Wb, W1b, x0,
+        hipLaunchKernelGGL(rnn_step_bf16<8>, grid, dim3(256), 0, s, R, gamma, V, hd.d, k, Wb, W1b, x0,
                            keys, hd.part, hd.s, ob);
         break;
     }

@@ -10,8 +10,8 @@ struct RnnHead {
   int d;
   float* s;        // [R][gamma][r] f32 out: the state after each position
   void* o;         // [R][gamma][r] storage type out: each position's bias vector
-  float* part;     // f32 workspace: bf16, the hidden-state partials [splits][R gamma][3r];
-                   // fp32, one position's projection [R][3r]
+  float* part;     // f32 workspace: bf16, the hidden-state partials [splits][R gamma][3r],
+                   // summed into the first; fp32, one position's projection [R][3r]
 };
 
 }  // namespace dspark

@@ -857,9 +857,18 @@ hipError_t pipe_launch(int R, int gamma, int V, int r, const void* U, const void
                        const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s);
 
 // rnn.hip: the RNN head's projection and gating for position k (reads the
-// keys of position k - 1 for the previous token)
+// keys of position k - 1 for the previous token); the hidden-state part of
+// the projection for every position (bf16), run before the first
 hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& h, int R, int gamma, int V, int r, int k,
                            const void* W1, const int32_t* x0, const unsigned long long* keys, hipStream_t s);
+hipError_t rnn_hproj_launch(const RnnHead& hd, int R, int gamma, int r, hipStream_t s);
+
+// sample_res.hip: the RNN head inside the W2t-on-chip persistent launch
+bool res_rnn_usable(int R, int V, int r, int max_wgs);
+hipError_t res_rnn_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
+                          const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
+                          const uint32_t* cancel, const void* Wrnn, const float* Yh, int d, float* st, void* o,
+                          hipStream_t s);
 
 // The kernel sample_launch runs the Markov-head positions with, for a shape
 // (the same choice, in the same order).
@@ -882,8 +891,12 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   // bf16 Markov head: W2t held in registers when the vocabulary fits the
   // register files (res), else streamed through LDS at every position (wide)
   const int gxp = dt == DSPARK_BF16 && !rnn ? pipe_grid(R, V, r, kMaxSampleWGs) : 0;
-  const int gxr =
-      gxp == 0 && dt == DSPARK_BF16 && !rnn && res_usable(R, V, r, kMaxSampleWGs) ? res_grid_x(R, V, r, kMaxSampleWGs) : 0;
+  // the RNN head keeps W2t on chip too where its projection fits between
+  // two grid barriers per position (rnn_phase in sample_res.hip)
+  const bool rnn_res = rnn && dt == DSPARK_BF16 && res_rnn_usable(R, V, r, kMaxSampleWGs);
+  const int gxr = gxp == 0 && dt == DSPARK_BF16 && ((!rnn && res_usable(R, V, r, kMaxSampleWGs)) || rnn_res)
+                      ? res_grid_x(R, V, r, kMaxSampleWGs)
+                      : 0;
   const int gxw = gxp == 0 && gxr == 0 && dt == DSPARK_BF16 && wide_fits_r(R, V, r) ? wide_grid_x(R, V) : 0;
   const SampleWs w = carve(ws, R, gamma, gxp > 0 ? kPipeKeySlots : kKeySlots);
   // the one-launch sweeps stamp the events themselves; the per-position
@@ -906,9 +919,15 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   if (gxp > 0 &&
       (err = pipe_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxp, cancel, ev0, ev1, s)) != hipSuccess)
     return err;
-  if (gxr > 0 &&
+  if (gxr > 0 && !rnn &&
       (err = res_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxr, 0, gamma, cancel, ev0, ev1, s)) != hipSuccess)
     return err;
+  if (gxr > 0 && rnn) {
+    if ((err = rnn_hproj_launch(*rnn, R, gamma, r, s)) != hipSuccess) return err;
+    if ((err = res_rnn_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxr, cancel, rnn->W, rnn->part, rnn->d,
+                              rnn->s, rnn->o, s)) != hipSuccess)
+      return err;
+  }
   for (int kb = 0; gxp == 0 && gxr == 0 && kb < gamma; kb += span) {
     if (rnn && (err = rnn_step_launch(dt, *rnn, R, gamma, V, r, kb, W1, x0, w.keys, s)) != hipSuccess) return err;
     if (gxw > 0) {

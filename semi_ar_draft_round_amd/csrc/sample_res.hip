@@ -50,6 +50,22 @@ namespace dspark {
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * kWave;   // 512
 
+// Data one work group writes and others read within the launch (the RNN
+// head's s and o): stored and loaded as agent-scope atomics, which are
+// coherent across the dies' L2 caches without a cache write-back; the
+// writers' stores have completed before they arrive at the grid barrier
+// that the readers wait on.
+__device__ __forceinline__ void store32_agent(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 load16_agent(const void* p) {
+  const unsigned long long* q = static_cast<const unsigned long long*>(p);
+  const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32), static_cast<uint32_t>(b),
+               static_cast<uint32_t>(b >> 32)};
+}
+
 // LDS bytes of one request's W1 row (r = 16 KS16 bf16) plus a 16-byte pad,
 // so the rows a half-wave reads for one B fragment fall in different banks.
 template <int KS16>
@@ -75,11 +91,20 @@ struct ResLane {
   float G[2];
 };
 
-template <int RB, int KS16, bool VEC>
+// The RNN head's arguments when the kernel runs it (see rnn_phase below).
+struct ResRnn {
+  const uint16_t* W;    // [3r][2r + d]: gate, candidate and output rows; columns follow z
+  const float* Yh;      // [R gamma][3r]: the hidden-state part of the projection
+  int d;
+  float* s;             // [R][gamma][r] out: the state after each position
+  uint16_t* o;          // [R][gamma][r] out: each position's bias vector
+};
+
+template <int RB, int KS16, bool VEC, bool RNN = false>
 __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     int R, int gamma, int V, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
-    const float* __restrict__ g, SampleWs ws, int kb, int ke, const uint32_t* __restrict__ cancel) {
+    const float* __restrict__ g, SampleWs ws, int kb, int ke, const uint32_t* __restrict__ cancel, ResRnn rnn) {
   static_assert(kGChunk == 16 && kChunk == 64, "one Gumbel chunk per lane of a 32x32 output block");
   constexpr int NROWS = 32 * RB;
   constexpr int kE = res_erow_bytes<KS16>();
@@ -148,6 +173,13 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
   auto gather_e = [&](int k, bool first) {
     const int i = static_cast<int>(threadIdx.x) / TPR;
     const int part = static_cast<int>(threadIdx.x) % TPR;
+    if constexpr (RNN) {   // the head's bias vectors o_k in the W1 rows' place (written this launch)
+      const uint16_t* src = i < R ? rnn.o + (static_cast<int64_t>(i) * gamma + k) * (KS16 * 16) : kZeroRow;
+#pragma unroll
+      for (int p = part; p < PPR; p += TPR)
+        *reinterpret_cast<u32x4*>(erows + i * kE + p * 16) = load16_agent(src + p * 8);
+      return;
+    }
     int prev = -1;
     if (i < R) {
       if (first) {
@@ -278,6 +310,146 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     }
   };
 
+  // The RNN head (DSpark reading notes, "implementation two: the RNN head",
+  // eq (6)) between positions: o_k and s_k for every request, then a grid
+  // barrier.  Work group b computes items b, b + gx, ...: item (jb, ib) is
+  // state columns 32 jb .. 32 jb + 31 of all three parts for requests
+  // 32 ib .. 32 ib + 31.  Its z rows (the state s_{k-1} rounded to bf16, then
+  // the previous token's W1 row; the hidden-state part is in Yh) go to LDS
+  // (the W1-row area, free here), waves 0-5 each multiply one part's 32 W
+  // rows by them over one half of the 2r inner elements, and all threads
+  // add the two halves and the hidden-state part (its split partials
+  // already summed) and apply the gates.  o and s are stored and read back as agent-scope
+  // atomics (store32_agent, load16_agent), coherent across the dies.
+  auto rnn_phase = [&](int k, unsigned int round) -> bool {
+    if constexpr (RNN) {
+      constexpr int r = KS16 * 16;
+      constexpr int kZ = 4 * r + 16;   // bytes of a z row in LDS (2r bf16 and a pad)
+      constexpr int nJB = r / 32;
+      const int K = 2 * r + rnn.d;
+      const int nItems = nJB * ((R + 31) / 32);
+      static_assert(32 * kZ <= NROWS * kE, "the z rows fit in the W1-row area");
+      static_assert(6 * 16 * kWave * 4 <= NROWS * kE, "the six partial products fit in the W1-row area");
+      for (int item = bx; item < nItems; item += gx) {
+        const int jb = item % nJB, ib = item / nJB;
+        {   // z rows: 16 threads per request
+          const int i = static_cast<int>(threadIdx.x) >> 4, u = static_cast<int>(threadIdx.x) & 15;
+          const int rc = min(32 * ib + i, R - 1);
+          int prev;
+          if (k == 0) {
+            prev = token_or_none(x0[rc], V);
+          } else {
+            const unsigned long long* kp = ws.keys + static_cast<int64_t>(k - 1) * kKeySlots * R + rc;
+            unsigned long long best = 0;
+#pragma unroll
+            for (int sl = 0; sl < kKeySlots; ++sl) {
+              const unsigned long long v =
+                  __hip_atomic_load(kp + static_cast<int64_t>(sl) * R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+              best = v > best ? v : best;
+            }
+            prev = token_or_none(key_token(best), V);
+          }
+          uint8_t* zr = erows + i * kZ;
+          // the state: r floats, r / 16 per thread, rounded to bf16 (zeros at k = 0)
+          const float* srow = rnn.s + (static_cast<int64_t>(rc) * gamma + (k > 0 ? k - 1 : 0)) * r;
+#pragma unroll
+          for (int p = u; p < r / 8; p += 16) {
+            const u32x4 a = load16_agent(srow + 8 * p), b = load16_agent(srow + 8 * p + 4);
+            float4 lo = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                                    __uint_as_float(a[3]));
+            float4 hi = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]),
+                                    __uint_as_float(b[3]));
+            if (k == 0) lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+            const uint32_t w0 = bf16_bits_rne(lo.x) | (bf16_bits_rne(lo.y) << 16);
+            const uint32_t w1 = bf16_bits_rne(lo.z) | (bf16_bits_rne(lo.w) << 16);
+            const uint32_t w2 = bf16_bits_rne(hi.x) | (bf16_bits_rne(hi.y) << 16);
+            const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
+            *reinterpret_cast<u32x4*>(zr + 16 * p) = u32x4{w0, w1, w2, w3};
+          }
+          // the previous token's W1 row (zeros when there is none)
+          const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
+#pragma unroll
+          for (int p = u; p < r / 8; p += 16)
+            *reinterpret_cast<u32x4*>(zr + 2 * r + 16 * p) = *reinterpret_cast<const u32x4*>(erow + 8 * p);
+        }
+        __syncthreads();
+        f32x16 acc = {};
+        if (wave < 6) {   // part g = wave / 2 over half wave % 2 of the 2r inner elements
+          constexpr int KSH = r / 16;   // k-steps per half
+          constexpr int B8 = KSH < 8 ? KSH : 8;
+          const int gp = wave >> 1, kh = (wave & 1) * KSH;
+          const uint16_t* wrow = rnn.W + static_cast<int64_t>(gp * r + 32 * jb + j) * K + 16 * kh + 8 * h;
+          const uint8_t* zrow = erows + j * kZ + 32 * kh + 16 * h;
+          bf16x8 a[B8];
+#pragma unroll
+          for (int kk = 0; kk < B8; ++kk) a[kk] = load_bf16x8_global(wrow + 16 * kk);
+#pragma unroll
+          for (int k0 = 0; k0 < KSH; k0 += B8) {
+            // each fragment is reloaded with the next batch's right after its
+            // product is issued (the last batch loads itself again)
+            const int kn = k0 + B8 < KSH ? k0 + B8 : k0;
+#pragma unroll
+            for (int kk = 0; kk < B8; ++kk) {
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], *reinterpret_cast<const bf16x8*>(zrow + 32 * (k0 + kk)),
+                                                            acc, 0, 0, 0);
+              a[kk] = load_bf16x8_global(wrow + 16 * (kn + kk));
+            }
+          }
+        }
+        __syncthreads();   // every z read is done
+        float* red = reinterpret_cast<float*>(erows);
+        if (wave < 6) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) red[(wave * 16 + q) * kWave + lane] = acc[q];
+        }
+        __syncthreads();
+        // 1024 outputs: thread t takes request 32 ib + t / 16 and columns
+        // 32 jb + c and c + 1, c = 2 (t % 16) (o_k's two bf16 in one store);
+        // accumulator q of lane l holds row 8 (q / 4) + 4 (l / 32) + q % 4 of
+        // the part's 32 and request l % 32.  Every load goes out before the
+        // first sum.
+        {
+          const int rl = static_cast<int>(threadIdx.x) >> 4, c0 = 2 * (static_cast<int>(threadIdx.x) & 15);
+          const int req = 32 * ib + rl;
+          const int rq = min(req, R - 1);
+          const int64_t row = static_cast<int64_t>(rq) * gamma + k;
+          const int col = 32 * jb + c0;
+          float2 yh[3];
+#pragma unroll
+          for (int gp = 0; gp < 3; ++gp) yh[gp] = *reinterpret_cast<const float2*>(rnn.Yh + row * (3 * r) + gp * r + col);
+          // s_{k-1} of the same columns (this work group's own stores), read
+          // at k = 0 too and unused there
+          const u32x4 sp4 = load16_agent(rnn.s + (k > 0 ? row - 1 : row) * r + (col & ~3));
+          const float sprev[2] = {__uint_as_float(sp4[col & 3]), __uint_as_float(sp4[(col & 3) + 1])};
+          float sn[2];
+          uint32_t ob = 0;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int c = c0 + t;
+            const int q = ((c >> 3) << 2) | (c & 3);
+            const int l = (((c >> 2) & 1) << 5) | rl;
+            float y[3];
+#pragma unroll
+            for (int gp = 0; gp < 3; ++gp)
+              y[gp] = (t ? yh[gp].y : yh[gp].x) +
+                      (red[(2 * gp * 16 + q) * kWave + l] + red[((2 * gp + 1) * 16 + q) * kWave + l]);
+            const float gate = 1.f / (1.f + expf(-y[0]));
+            sn[t] = gate * (k > 0 ? sprev[t] : 0.f) + (1.f - gate) * tanhf(y[1]);
+            ob |= bf16_bits_rne(tanhf(y[2])) << (16 * t);
+          }
+          if (req < R) {
+            store32_agent(rnn.s + row * r + col, __float_as_uint(sn[0]));
+            store32_agent(rnn.s + row * r + col + 1, __float_as_uint(sn[1]));
+            store32_agent(rnn.o + row * r + col, ob);
+          }
+        }
+        __syncthreads();   // the products area is reused
+      }
+      if (!grid_barrier(ws.bar, round, &barflag, cancel)) return false;
+    }
+    return true;
+  };
+
   const int s_end = ke * RB;
   ResLane pa, pb;   // steps s and s + 1 in flight (one block: the own tile and the LDS-held tile)
   if (active) {
@@ -285,6 +457,7 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     if (NX == 0) load_step(pb, min(kb * RB + 1, s_end - 1));
   }
   if (NX > 0 && xact) load_at(pb, kb, 0, xv0);
+  if (RNN && !rnn_phase(kb, 1)) return;   // o of the first position (the launch covers all of them)
   gather_e(kb, kb == 0);
   store_gq(load_gq(kb));
   __builtin_amdgcn_s_waitcnt(0);   // the A fragments copied into LDS have landed
@@ -350,7 +523,10 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     }
     if (k + 1 == ke) break;
     const f32x4 gq = load_gq(k + 1);
-    if (!grid_barrier(ws.bar, k + 1, &barflag, cancel)) return;
+    // the RNN head meets twice per position: the keys of position k, then o
+    // of position k + 1
+    if (!grid_barrier(ws.bar, RNN ? 2 * (k + 1) : k + 1, &barflag, cancel)) return;
+    if (RNN && !rnn_phase(k + 1, 2 * (k + 1) + 1)) return;
     gather_e(k + 1, false);
     store_gq(gq);
     __syncthreads();
@@ -378,7 +554,7 @@ int res_grid_x(int R, int V, int r, int max_wgs) {
   return (nTiles + gx - 1) / gx <= res_tiles_for(R, r) ? gx : 0;
 }
 
-template <int RB, int KS16, bool VEC>
+template <int RB, int KS16, bool VEC, bool RNN = false>
 static bool res_fits_one() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -387,7 +563,7 @@ static bool res_fits_one() {
   if (v == 0) {
     int n = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &n, reinterpret_cast<const void*>(&sample_steps_res<RB, KS16, VEC>), kResThreads, 0);
+        &n, reinterpret_cast<const void*>(&sample_steps_res<RB, KS16, VEC, RNN>), kResThreads, 0);
     v = (e == hipSuccess && n >= 1) ? 1 : 2;
     cache[dev].store(v, std::memory_order_relaxed);
   }
@@ -422,7 +598,7 @@ static void launch_res(int R, int gamma, int V, const void* U, const void* W1, c
                        const uint32_t* cancel, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
   hipExtLaunchKernelGGL((sample_steps_res<RB, KS16, VEC>), dim3(gx), dim3(kResThreads), 0, s, ev0, ev1, 0, R, gamma,
                         V, static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
-                        static_cast<const uint16_t*>(W2t), x0, G, g, w, kb, ke, cancel);
+                        static_cast<const uint16_t*>(W2t), x0, G, g, w, kb, ke, cancel, ResRnn{});
 }
 
 template <int KS16>
@@ -452,6 +628,51 @@ hipError_t res_launch(int R, int gamma, int V, int r, const void* U, const void*
     case 128: launch_res_ks<8>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s); break;
     default: launch_res_ks<16>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, kb, ke, cancel, ev0, ev1, s); break;
   }
+  return hipGetLastError();
+}
+
+// The RNN head in the same persistent launch (rnn_phase): 33 to 128
+// requests at r = 256, 65 to 128 at r = 128 (the W1-row area must hold
+// the z rows and six partial products), the tiles on chip as for the
+// Markov head, and the work group fits on a compute unit.
+bool res_rnn_usable(int R, int V, int r, int max_wgs) {
+  if (R > 128 || res_grid_x(R, V, r, max_wgs) == 0) return false;
+  const bool vec = (V % kGChunk) == 0;
+  if (r == 128 && R > 64) return vec ? res_fits_one<4, 8, true, true>() : res_fits_one<4, 8, false, true>();
+  if (r != 256 || R < 33) return false;
+  if (R <= 64) return vec ? res_fits_one<2, 16, true, true>() : res_fits_one<2, 16, false, true>();
+  return vec ? res_fits_one<4, 16, true, true>() : res_fits_one<4, 16, false, true>();
+}
+
+template <int RB, int KS16, bool VEC>
+static void launch_res_rnn(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
+                           const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
+                           const uint32_t* cancel, const ResRnn& rn, hipStream_t s) {
+  hipLaunchKernelGGL((sample_steps_res<RB, KS16, VEC, true>), dim3(gx), dim3(kResThreads), 0, s, R, gamma, V,
+                     static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
+                     static_cast<const uint16_t*>(W2t), x0, G, g, w, 0, gamma, cancel, rn);
+}
+
+// Launches all positions with the RNN head (the caller checked
+// res_rnn_usable and computed the hidden-state partials).
+hipError_t res_rnn_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
+                          const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
+                          const uint32_t* cancel, const void* Wrnn, const float* Yh, int d, float* st, void* o,
+                          hipStream_t s) {
+  const ResRnn rn{static_cast<const uint16_t*>(Wrnn), Yh, d, st, static_cast<uint16_t*>(o)};
+  const bool vec = (V % kGChunk) == 0;
+#define DSPARK_RES_RNN(RB, KS)                                                                   \
+  (vec ? launch_res_rnn<RB, KS, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, cancel, rn, s) \
+       : launch_res_rnn<RB, KS, false>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, cancel, rn, s))
+  if (r == 128) {
+    DSPARK_RES_RNN(4, 8);
+  } else {
+    if (R <= 64)
+      DSPARK_RES_RNN(2, 16);
+    else
+      DSPARK_RES_RNN(4, 16);
+  }
+#undef DSPARK_RES_RNN
   return hipGetLastError();
 }
 

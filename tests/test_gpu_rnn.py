@@ -94,6 +94,14 @@ CASES = [
     W.custom("rnn_r130_g4_v700_r128", R=130, gamma=4, V=700, r=128, d=256, seed=44),
     W.custom("rnn_r9_g7_v333_f32", R=9, gamma=7, V=333, r=20, d=36, dtype="f32", seed=45),
     W.custom("rnn_r5_g64_v1000_r32", R=5, gamma=64, V=1000, r=32, d=64, seed=46),
+    # the head inside the W2t-on-chip persistent launch (two grid barriers
+    # per position): four request blocks at r = 256 and r = 128, two at
+    # r = 256 with d = 48 (a hidden-state stage past the range), and a
+    # vocabulary that is not a multiple of 16
+    W.custom("rnn_r100_g5_v20000_r256", R=100, gamma=5, V=20000, r=256, d=64, seed=47),
+    W.custom("rnn_r90_g3_v6000_r128", R=90, gamma=3, V=6000, r=128, d=128, seed=48),
+    W.custom("rnn_r40_g4_v9000_r256", R=40, gamma=4, V=9000, r=256, d=48, seed=49),
+    W.custom("rnn_r70_g3_v5003_r256", R=70, gamma=3, V=5003, r=256, d=64, seed=50),
 ]
 
 
@@ -121,7 +129,7 @@ def test_rnn_full_size_sampled(dev):
     assert np.all((got[0].numpy() >= 0) & (got[0].numpy() < w.V))
 
 
-@pytest.mark.parametrize("name", ["rnn_r70_g6_v4100_r64", "rnn_r20_g5_v1000_r32"])
+@pytest.mark.parametrize("name", ["rnn_r70_g6_v4100_r64", "rnn_r20_g5_v1000_r32", "rnn_r100_g5_v20000_r256"])
 def test_rnn_reduces_to_markov_bit_for_bit(name, dev):
     from semi_ar_draft_round_amd import binding as B
     from semi_ar_draft_round_amd import device_round as DR
