@@ -528,11 +528,13 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     float cs = 0.f, ps = 0.f;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const float pt = __builtin_amdgcn_exp2f(fmaf(tv[q], kL2e, -lt2));
-      const float pd = __builtin_amdgcn_exp2f(fmaf(acc[q] + acc2[q], kL2e, -ld2));
+      const float at = fmaf(tv[q], kL2e, -lt2);
+      const float ad = fmaf(acc[q] + acc2[q], kL2e, -ld2);
       if constexpr (ACC) {
-        cs += fminf(pt, pd);
+        cs += __builtin_amdgcn_exp2f(fminf(at, ad));   // min(p_t, p_d): exp2 is monotone
       } else {
+        const float pt = __builtin_amdgcn_exp2f(at);
+        const float pd = __builtin_amdgcn_exp2f(ad);
         ps += pt;
         cs += rr.rej ? fmaxf(0.f, pt - pd) : pt;
       }
