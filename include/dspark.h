@@ -482,6 +482,18 @@ const char* dspark_status_string(dspark_status s);
  */
 const char* dspark_markov_sample_kernel(dspark_dtype dt, int R, int gamma, int V, int r);
 
+/*
+ * dspark_rnn_sample_kernel — the same for dspark_rnn_sample (DSpark reading
+ * notes, "implementation two: the RNN head", eq (6)): with bf16 storage,
+ * r = 256 and 33 to 128 requests, or r = 128 and 65 to 128, and W2t on chip
+ * as above, one persistent launch holds W2t on chip and computes each
+ * position's RNN step (o_k, s_k) between two grid barriers before that
+ * position's sweep; other shapes run a step kernel and a one-position
+ * sampling launch per position.  A static string, or NULL as above;
+ * enqueues nothing.
+ */
+const char* dspark_rnn_sample_kernel(dspark_dtype dt, int R, int gamma, int V, int r);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,7 @@ _SIGNATURES = {
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
     "dspark_status_string": [_I],
     "dspark_markov_sample_kernel": [_I, _I, _I, _I, _I],
+    "dspark_rnn_sample_kernel": [_I, _I, _I, _I, _I],
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dspark_workspace_size.restype = ctypes.c_size_t
     lib.dspark_status_string.restype = ctypes.c_char_p
     lib.dspark_markov_sample_kernel.restype = ctypes.c_char_p
+    lib.dspark_rnn_sample_kernel.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -86,6 +88,13 @@ def dspark_markov_sample_kernel(dtype: torch.dtype, R: int, gamma: int, V: int, 
     device (None when the call would reject the shape)."""
     name = load_library().dspark_markov_sample_kernel(BF16 if dtype == torch.bfloat16 else F32,
                                                       R, gamma, V, r)
+    return None if name is None else name.decode()
+
+
+def dspark_rnn_sample_kernel(dtype: torch.dtype, R: int, gamma: int, V: int, r: int):
+    """Which kernels the RNN-head sampling call runs for this shape on the
+    current device (None when the call would reject the shape)."""
+    name = load_library().dspark_rnn_sample_kernel(BF16 if dtype == torch.bfloat16 else F32, R, gamma, V, r)
     return None if name is None else name.decode()
 
 

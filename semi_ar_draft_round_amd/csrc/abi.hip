@@ -19,6 +19,7 @@ bool sts_shape_ok(int N, int gamma, int G, int M);
 hipError_t sts_launch(int N, int gamma, const float* z, const int32_t* n_acc, const float* grid, int G, int M,
                       float* T, double* ece_before, double* ece_after, double* auc, void* ws, hipStream_t s);
 const char* sample_kernel_name(dspark_dtype dt, int R, int V, int r);
+const char* rnn_kernel_name(dspark_dtype dt, int R, int V, int r);
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,
@@ -124,6 +125,12 @@ const char* dspark_markov_sample_kernel(dspark_dtype dt, int R, int gamma, int V
   if (!dtype_ok(dt) || !draft_shape_ok(R, gamma, V) || !rank_ok(dt, r)) return nullptr;
   if (check_device() != DSPARK_OK) return nullptr;
   return sample_kernel_name(dt, R, V, r);
+}
+
+const char* dspark_rnn_sample_kernel(dspark_dtype dt, int R, int gamma, int V, int r) {
+  if (!dtype_ok(dt) || !draft_shape_ok(R, gamma, V) || !rank_ok(dt, r)) return nullptr;
+  if (check_device() != DSPARK_OK) return nullptr;
+  return rnn_kernel_name(dt, R, V, r);
 }
 
 static size_t sample_ws_any(int R, int gamma, int V) {

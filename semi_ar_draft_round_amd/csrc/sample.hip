@@ -882,6 +882,15 @@ const char* sample_kernel_name(dspark_dtype dt, int R, int V, int r) {
   return dt == DSPARK_BF16 ? "sample_step_bf16: one launch per position" : "sample_step_f32: one launch per position";
 }
 
+const char* rnn_kernel_name(dspark_dtype dt, int R, int V, int r) {
+  if (dt == DSPARK_BF16 && res_rnn_usable(R, V, r, kMaxSampleWGs))
+    return "sample_steps_res with the RNN step: W2t held on chip, the step between two grid barriers per position, all positions in one persistent launch";
+  if (dt == DSPARK_BF16 && wide_fits_r(R, V, r))
+    return "rnn_step_bf16 and a one-position sample_steps_wide launch per position: W2t streamed through LDS";
+  return dt == DSPARK_BF16 ? "rnn_step_bf16 and sample_step_bf16 per position"
+                           : "rnn_proj_f32, rnn_gate and sample_step_f32 per position";
+}
+
 hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const void* U,
                          const void* W1, const void* W2t, const int32_t* x0, const float* G,
                          const float* g, int32_t* x, float* lse, float* logit, void* ws,

@@ -247,3 +247,6 @@ def test_sample_kernel_query_rejects_what_the_call_rejects(lib):
     assert lib.dspark_markov_sample_kernel(7, 128, 16, 129280, 256) is None
     assert lib.dspark_markov_sample_kernel(1, 0, 16, 129280, 256) is None
     assert lib.dspark_markov_sample_kernel(1, 128, 16, 129280, 96) is None
+    assert lib.dspark_rnn_sample_kernel(7, 128, 16, 129280, 256) is None
+    assert lib.dspark_rnn_sample_kernel(1, 0, 16, 129280, 256) is None
+    assert lib.dspark_rnn_sample_kernel(1, 128, 16, 129280, 96) is None

@@ -116,6 +116,27 @@ def test_rnn_small(w, dev):
     say(f"  {rep}")
 
 
+def test_rnn_kernel_choice(dev):
+    """The RNN-head call names the kernels it runs: the step inside the
+    W2t-on-chip launch for r = 256 with 33 to 128 requests and r = 128 with
+    65 to 128, a step kernel and a one-position launch per position
+    otherwise; the resident cases above take the resident launch."""
+    from semi_ar_draft_round_amd import binding as B
+    bf, f32 = torch.bfloat16, torch.float32
+    res = lambda *a: B.dspark_rnn_sample_kernel(bf, *a).startswith("sample_steps_res")
+    per = lambda *a: B.dspark_rnn_sample_kernel(bf, *a).startswith("rnn_step_bf16")
+    assert res(128, 16, 129280, 256) and res(33, 16, 129280, 256) and res(65, 4, 9000, 128)
+    assert per(32, 16, 129280, 256) and per(129, 16, 129280, 256) and per(64, 4, 9000, 128)
+    assert per(128, 16, 151936, 256)        # ten tiles per work group do not fit the RNN launch
+    assert per(100, 4, 4100, 64) and per(100, 4, 4100, 32)
+    assert B.dspark_rnn_sample_kernel(f32, 9, 7, 333, 20).startswith("rnn_proj_f32")
+    assert B.dspark_rnn_sample_kernel(bf, 128, 16, 129280, 96) is None
+    for w in CASES[6:]:
+        assert res(w.R, w.gamma, w.V, w.r), w.name
+    for w in CASES[:4]:
+        assert per(w.R, w.gamma, w.V, w.r), w.name
+
+
 def test_rnn_full_size_sampled(dev):
     w = W.BY_NAME["heavy_r128_g16_v129280"]
     say(f"[rnn] {w.name}: drawing inputs")
