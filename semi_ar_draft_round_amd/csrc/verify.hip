@@ -36,8 +36,7 @@ struct RowVec;
 template <>
 struct RowVec<BF16> {
   static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const uint16_t* p, float (&o)[8]) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
+  static __device__ __forceinline__ void unpack(uint4 v, float (&o)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -45,13 +44,18 @@ struct RowVec<BF16> {
       o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
+  static __device__ __forceinline__ void load(const uint16_t* p, float (&o)[8]) {
+    unpack(*reinterpret_cast<const uint4*>(p), o);
+  }
 };
 template <>
 struct RowVec<F32> {
   static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(uint4 v, float (&o)[4]) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+  }
   static __device__ __forceinline__ void load(const float* p, float (&o)[4]) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    unpack(*reinterpret_cast<const uint4*>(p), o);
   }
 };
 
@@ -78,16 +82,13 @@ constexpr int kLseThreads = 256;
 constexpr int kLseUnroll = 8;
 constexpr int kLseCompactR = 4096;
 
-// What a target-row part records, and which rows are needed:
-//   kPartLse     (max, sum exp) of rows 0..l_r
-//   kPartArgmax  (largest logit, its lowest index) of rows 0..l_r (greedy)
-//   kPartLseAll  (max, sum exp) of rows 0..gamma-1 of every request (the
-//                analytic acceptance; ell is not read)
-enum PartMode { kPartLse = 0, kPartArgmax = 1, kPartLseAll = 2 };
+// What a target-row part records (rows 0..l_r are the needed ones):
+//   kPartLse     (max, sum exp)
+//   kPartArgmax  (largest logit, its lowest index) (greedy)
+enum PartMode { kPartLse = 0, kPartArgmax = 1 };
 
-template <int MODE>
 __device__ __forceinline__ int needed_rows(const int32_t* ell, int r, int gamma) {
-  return MODE == kPartLseAll ? gamma : min(max(ell[r], 0), gamma) + 1;
+  return min(max(ell[r], 0), gamma) + 1;
 }
 
 // The larger logit, the lower index on equal logits.
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
     const int per = ceil_div(R, kLseThreads);
     const int b0 = min(static_cast<int>(threadIdx.x) * per, R), b1 = min(b0 + per, R);
     int mine = 0;
-    for (int q = b0; q < b1; ++q) mine += needed_rows<MODE>(ell, q, gamma);
+    for (int q = b0; q < b1; ++q) mine += needed_rows(ell, q, gamma);
     __shared__ int wtot[kLseThreads / kWave];
     int incl = mine;
 #pragma unroll
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
     if (threadIdx.x == 0) pref[R] = total;
     for (int q = b0; q < b1; ++q) {
       pref[q] = run;
-      run += needed_rows<MODE>(ell, q, gamma);
+      run += needed_rows(ell, q, gamma);
     }
     __syncthreads();
     const int64_t items = static_cast<int64_t>(pref[R]) * kLseSplits;
@@ -241,10 +242,110 @@ __global__ __launch_bounds__(kLseThreads) void verify_target_part(int R, int gam
       const int64_t ri = it / kLseSplits;
       const int r = static_cast<int>(ri / (gamma + 1));
       const int i = static_cast<int>(ri % (gamma + 1));
-      const int L = needed_rows<MODE>(ell, r, gamma) - 1;
+      const int L = needed_rows(ell, r, gamma) - 1;
       if (i > L) continue;   // uniform across the work group
       target_part_item<Elt, MODE>(r, i, sp, gamma, V, span, target, row0, part, sh);
     }
+  }
+}
+
+// The target log-normalisers of the analytic acceptance: rows 0..gamma-1 of
+// every request, each row whole in one work group (grid-stride over the
+// rows).  Each thread folds its 16-byte vectors into a running (max, sum)
+// in base 2: one exp2 per logit plus one per batch of kAccBatch vectors
+// when the batch raises the thread's max (the log2-scaled max's rounding is
+// taken out at the end); the next batch's loads are in
+// flight while the current one is folded.  The row's (max, sum) goes to part
+// 0 of the row and the other kLseSplits - 1 parts are left empty, so the
+// readers merge the parts as for the split rows.
+constexpr int kAccBatch = 8;
+
+template <typename Elt>
+__global__ __launch_bounds__(kLseThreads) void acceptance_target_lse(int R, int gamma, int V,
+                                                                     const typename Elt::T* __restrict__ target,
+                                                                     const int32_t* __restrict__ row0,
+                                                                     float2* __restrict__ part) {
+  constexpr float kL2e = 1.4426950408889634f;
+  constexpr int N = RowVec<Elt>::N;
+  constexpr int kStep = N * kLseThreads;            // elements per vector pass of the work group
+  __shared__ Lse sh[kLseThreads / kWave];
+  const int rows = R * gamma;
+  for (int rho = blockIdx.x; rho < rows; rho += gridDim.x) {
+    const int r = rho / gamma, k = rho % gamma;
+    const int64_t ri = static_cast<int64_t>(r) * (gamma + 1) + k;
+    const int64_t row = row0 ? static_cast<int64_t>(row0[r]) + k : ri;
+    const typename Elt::T* t = target + row * V;
+    // the thread's max Mn, M2 = Mn L2e rounded, and the sum of exp2(x L2e - M2)
+    float Mn = neg_inf(), M2 = neg_inf(), S = 0.f;
+    // batch vb: the thread's vectors at vb + u kStep, u < kAccBatch, kept as
+    // raw 16-byte words until they are folded (past the row: -inf)
+    auto fold = [&](const uint4 (&raw)[kAccBatch], int vb) {
+      float e[kAccBatch][N];
+      float m = neg_inf();
+#pragma unroll
+      for (int u = 0; u < kAccBatch; ++u) {
+        RowVec<Elt>::unpack(raw[u], e[u]);
+        const bool in = vb + u * kStep < V;
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+          e[u][q] = in ? e[u][q] : neg_inf();
+          m = fmaxf(m, e[u][q]);
+        }
+      }
+      if (m == neg_inf()) return;                    // nothing but empty slots and -inf logits
+      const float m2 = m * kL2e;
+      if (m2 > M2) {
+        S = S * __builtin_amdgcn_exp2f(M2 - m2);     // exp2(-inf) = 0 while S is still 0
+        M2 = m2;
+        Mn = m;
+      }
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kAccBatch; ++u)
+#pragma unroll
+        for (int q = 0; q < N; ++q) s4[q & 3] += __builtin_amdgcn_exp2f(fmaf(e[u][q], kL2e, -M2));
+      S += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    if ((V % N) == 0) {
+      uint4 ra[kAccBatch], rb[kAccBatch];
+      auto load = [&](uint4 (&raw)[kAccBatch], int vb) {
+#pragma unroll
+        for (int u = 0; u < kAccBatch; ++u) {
+          const int v = vb + u * kStep;
+          raw[u] = *reinterpret_cast<const uint4*>(t + (v < V ? v : 0));
+        }
+      };
+      const int v0 = static_cast<int>(threadIdx.x) * N;
+      load(ra, v0);
+      for (int vb = v0; vb < V; vb += 2 * kAccBatch * kStep) {
+        load(rb, vb + kAccBatch * kStep);
+        fold(ra, vb);
+        if (vb + kAccBatch * kStep >= V) break;
+        load(ra, vb + 2 * kAccBatch * kStep);
+        fold(rb, vb + kAccBatch * kStep);
+      }
+    } else {
+      for (int v = static_cast<int>(threadIdx.x); v < V; v += kLseThreads) {
+        const float x = Elt::load(t, v);
+        if (x == neg_inf()) continue;
+        const float x2 = x * kL2e;
+        if (x2 > M2) {
+          S = S * __builtin_amdgcn_exp2f(M2 - x2);
+          M2 = x2;
+          Mn = x;
+        }
+        S += __builtin_amdgcn_exp2f(fmaf(x, kL2e, -M2));
+      }
+    }
+    // natural units for the readers: (Mn, sum of exp(x - Mn)).  Each term
+    // is exp(x - Mn) 2^err with err = Mn L2e - M2, the rounding residual of
+    // M2 (exact as one fma), taken out here.
+    Lse acc = S > 0.f ? Lse{Mn, S * __builtin_amdgcn_exp2f(-fmaf(Mn, kL2e, -M2))} : Lse{neg_inf(), 0.f};
+    acc = block_reduce_lse(acc, sh);
+    if (threadIdx.x < kLseSplits)
+      part[ri * kLseSplits + threadIdx.x] =
+          threadIdx.x == 0 ? make_float2(acc.M, acc.S) : make_float2(neg_inf(), 0.f);
+    __syncthreads();   // sh is reused by the next row
   }
 }
 
@@ -1004,13 +1105,14 @@ hipError_t acceptance_launch(dspark_dtype dt, int R, int gamma, int V, int r, co
   float2* part = static_cast<float2*>(ws);
   float* accp = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                          align256(sizeof(float2) * R * (gamma + 1) * kLseSplits));
-  const int gridp = part_grid(R, gamma);
+  const int rowsn = R * gamma;
+  const int gridn = rowsn < 8 * compute_units() ? rowsn : 8 * compute_units();
   if (dt == DSPARK_BF16)
-    hipLaunchKernelGGL((verify_target_part<BF16, kPartLseAll>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma,
-                       V, static_cast<const uint16_t*>(target), row0, nullptr, part);
+    hipLaunchKernelGGL(acceptance_target_lse<BF16>, dim3(gridn), dim3(kLseThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(target), row0, part);
   else
-    hipLaunchKernelGGL((verify_target_part<F32, kPartLseAll>), dim3(gridp), dim3(kLseThreads), 0, s, R, gamma,
-                       V, static_cast<const float*>(target), row0, nullptr, part);
+    hipLaunchKernelGGL(acceptance_target_lse<F32>, dim3(gridn), dim3(kLseThreads), 0, s, R, gamma, V,
+                       static_cast<const float*>(target), row0, part);
   hipError_t err;
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int rows = R * gamma;
