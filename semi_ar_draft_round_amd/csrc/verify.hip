@@ -520,7 +520,8 @@ __device__ __forceinline__ ResidualRow acceptance_row(int rho, int gamma, int V,
 // chunk masses, stored directly.  Rows where every draft was accepted use
 // p_t (the bonus row) and skip nothing: their draft part is computed on U
 // row 0 and ignored.  W2t tiles go through registers into a double-buffered
-// LDS area one tile ahead; the lane's own logits are loaded two tiles ahead.
+// LDS area one tile ahead; the lane's own logits are loaded two tiles ahead
+// (four for ACC with V a multiple of 16, whose B rows sit in LDS).
 //
 // ACC: the same sweep over the R gamma rows of the analytic acceptance
 // (acceptance_row); each lane adds up min(p_t, p_d) over its tokens, and the
@@ -536,7 +537,12 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   constexpr float kL2e = 1.4426950408889634f;
   constexpr int NROWS = 32 * RQ;
   constexpr int kW = wide_tile_bytes<KS16>();
+  // ACC keeps the rows' B operands (W1 rows or bias vectors) in LDS rather
+  // than registers, which leaves room for more tiles of logits in flight
+  constexpr int kLaneAhead = ACC && VEC ? 4 : 2;   // tiles of the lane's logits in flight
+  constexpr int kEB = KS16 * 32 + 16;       // bytes of an LDS B row (padded: rows of a half wave in different banks)
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kW];
+  __shared__ __attribute__((aligned(16))) uint8_t elds[ACC ? NROWS * kEB : 16];
   __shared__ float accsh[ACC ? NROWS : 1];
   // chunk masses of the work group's tiles, [tile][row][chunk of the tile],
   // written out together after the sweep (when the group has at most
@@ -585,14 +591,24 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   };
   WideW<KS16, RQ> wr;
   wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(0) * kChunk);
-  Lane even, odd;
-  load_lane(even, 0);
-  load_lane(odd, 1);
+  Lane l0, l1, l2, l3;   // tiles it, it + 1, ... of the lane's logits (l2, l3 with four ahead)
+  load_lane(l0, 0);
+  load_lane(l1, 1);
+  if constexpr (kLaneAhead == 4) {
+    load_lane(l2, 2);
+    load_lane(l3, 3);
+  }
   bf16x8 e[KS16];
   const uint16_t* btab = bvec ? bvec : W1;
   const uint16_t* w1row = (rr.rej && rr.brow >= 0 ? btab + rr.brow * (KS16 * 16) : kZeroRow) + 8 * h;
 #pragma unroll
   for (int ks = 0; ks < KS16; ++ks) e[ks] = load_bf16x8_global(w1row + 16 * ks);
+  uint8_t* const erow = elds + (ACC ? (rq * 32 + j) * kEB + h * 16 : 0);   // the lane's B row (ACC)
+  if constexpr (ACC) {
+    if (th == 0)   // both token halves load the same rows
+#pragma unroll
+      for (int ks = 0; ks < KS16; ++ks) *reinterpret_cast<bf16x8*>(erow + ks * 32) = e[ks];
+  }
   wide_store_w<KS16, RQ>(lds, wr);
   wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(1)) * kChunk);
   __syncthreads();
@@ -610,7 +626,7 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
       const uint32_t w = cur.t[q >> 3][(q >> 1) & 3];
       tv[q] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
     }
-    load_lane(cur, it + 2);
+    load_lane(cur, it + kLaneAhead);
     const uint8_t* arow = lds + (it & 1) * kW + ((32 * th + j) * wide_row_pieces<KS16>() + h) * 16;
     constexpr int KB = KS16 < 8 ? KS16 : 8;
 #pragma unroll
@@ -620,10 +636,11 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
       for (int kk = 0; kk < KB; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(arow + (k0 + kk) * 32);
 #pragma unroll
       for (int kk = 0; kk < KB; ++kk) {
+        const bf16x8 b = ACC ? *reinterpret_cast<const bf16x8*>(erow + (k0 + kk) * 32) : e[k0 + kk];
         if (kk & 1)
-          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], e[k0 + kk], acc2, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b, acc2, 0, 0, 0);
         else
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], e[k0 + kk], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b, acc, 0, 0, 0);
       }
     }
     float cs = 0.f, ps = 0.f;
@@ -657,11 +674,23 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     __syncthreads();
   };
   int it = 0;
-  for (; it + 1 < nT; it += 2) {
-    step(it, even);
-    step(it + 1, odd);
+  if constexpr (kLaneAhead == 4) {
+    for (; it + 3 < nT; it += 4) {
+      step(it, l0);
+      step(it + 1, l1);
+      step(it + 2, l2);
+      step(it + 3, l3);
+    }
+    if (it < nT) step(it, l0);
+    if (it + 1 < nT) step(it + 1, l1);
+    if (it + 2 < nT) step(it + 2, l2);
+  } else {
+    for (; it + 1 < nT; it += 2) {
+      step(it, l0);
+      step(it + 1, l1);
+    }
+    if (it < nT) step(it, l0);
   }
-  if (it < nT) step(it, even);
   if (staged) {
     // the staged masses: four chunks (16 bytes) per (tile, row) item, a
     // request's items of consecutive tiles adjacent in memory
