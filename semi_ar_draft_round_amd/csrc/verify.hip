@@ -521,7 +521,8 @@ __device__ __forceinline__ ResidualRow acceptance_row(int rho, int gamma, int V,
 // p_t (the bonus row) and skip nothing: their draft part is computed on U
 // row 0 and ignored.  W2t tiles go through registers into a double-buffered
 // LDS area one tile ahead; the lane's own logits are loaded two tiles ahead
-// (four for ACC with V a multiple of 16, whose B rows sit in LDS).
+// (ACC with V a multiple of 16, whose B rows sit in LDS: the logits four
+// tiles ahead and the W2t tiles two).
 //
 // ACC: the same sweep over the R gamma rows of the analytic acceptance
 // (acceptance_row); each lane adds up min(p_t, p_d) over its tokens, and the
@@ -589,7 +590,12 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
     load_lane16<VEC>(ll.t, trow, v, V);
     load_lane16<VEC>(ll.u, urow, v, V);
   };
-  WideW<KS16, RQ> wr;
+  // W2t tiles in registers on their way to LDS: tile it + 1 waits in wr (in
+  // wr for even it and wr2 for odd it when the tiles come two steps ahead,
+  // at 128 rows per group and r >= 128)
+  constexpr int kWAhead = kLaneAhead == 4 && RQ == 4 && KS16 >= 8 ? 2 : 1;
+  WideW<KS16, RQ> wr, wr2;
+  WideW<KS16, RQ>& wodd = kWAhead == 2 ? wr2 : wr;   // the set of odd steps
   wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(0) * kChunk);
   Lane l0, l1, l2, l3;   // tiles it, it + 1, ... of the lane's logits (l2, l3 with four ahead)
   load_lane(l0, 0);
@@ -611,9 +617,13 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
   }
   wide_store_w<KS16, RQ>(lds, wr);
   wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(1)) * kChunk);
+  if constexpr (kWAhead == 2) wide_load_w<KS16, RQ>(wr2, W2t, V, tile_of(clampc(2)) * kChunk);
   __syncthreads();
 
-  auto step = [&](int it, Lane& cur) {
+  // step it: the products read tile it from LDS; at its end tile it + 1 goes
+  // from `wn` into the other LDS buffer and `wn` is reloaded with tile
+  // it + 1 + kWAhead
+  auto step = [&](int it, Lane& cur, WideW<KS16, RQ>& wn) {
     f32x16 acc, acc2 = {};
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -669,27 +679,27 @@ __global__ __launch_bounds__(wide_threads<RQ>(), 1) void verify_residual_wide(
         psum[static_cast<int64_t>(req) * ldm + c16] = ps;
       }
     }
-    wide_store_w<KS16, RQ>(lds + ((it + 1) & 1) * kW, wr);
-    wide_load_w<KS16, RQ>(wr, W2t, V, tile_of(clampc(it + 2)) * kChunk);
+    wide_store_w<KS16, RQ>(lds + ((it + 1) & 1) * kW, wn);
+    wide_load_w<KS16, RQ>(wn, W2t, V, tile_of(clampc(it + 1 + kWAhead)) * kChunk);
     __syncthreads();
   };
   int it = 0;
-  if constexpr (kLaneAhead == 4) {
+  if constexpr (kLaneAhead == 4) {   // even steps store tiles from wr, odd steps from wodd
     for (; it + 3 < nT; it += 4) {
-      step(it, l0);
-      step(it + 1, l1);
-      step(it + 2, l2);
-      step(it + 3, l3);
+      step(it, l0, wr);
+      step(it + 1, l1, wodd);
+      step(it + 2, l2, wr);
+      step(it + 3, l3, wodd);
     }
-    if (it < nT) step(it, l0);
-    if (it + 1 < nT) step(it + 1, l1);
-    if (it + 2 < nT) step(it + 2, l2);
+    if (it < nT) step(it, l0, wr);
+    if (it + 1 < nT) step(it + 1, l1, wodd);
+    if (it + 2 < nT) step(it + 2, l2, wr);
   } else {
     for (; it + 1 < nT; it += 2) {
-      step(it, l0);
-      step(it + 1, l1);
+      step(it, l0, wr);
+      step(it + 1, l1, wr);
     }
-    if (it < nT) step(it, l0);
+    if (it < nT) step(it, l0, wr);
   }
   if (staged) {
     // the staged masses: four chunks (16 bytes) per (tile, row) item, a
