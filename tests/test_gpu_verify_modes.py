@@ -145,6 +145,13 @@ ACC_SMALL = [
     # the sweep that keeps W2t on chip: an odd number of 32-row blocks (9)
     # over groups of two or three tiles, with 16-byte logit loads
     W.custom("acc_r40_g7_v40000_r256_bf16", R=40, gamma=7, V=40000, r=256, d=64, seed=36),
+    # V a multiple of 16, so the sweep keeps four tiles of logits in flight
+    # (B rows in LDS): 50 rows in groups of 64 at r = 256, 280 rows in groups
+    # of 128 at r = 64 (W2t one step ahead), 24 rows in one group of 32 at
+    # r = 128; the W2t tiles two steps ahead are the 280-row r = 256 case above
+    W.custom("acc_r10_g5_v4096_r256_bf16", R=10, gamma=5, V=4096, r=256, d=64, seed=37),
+    W.custom("acc_r70_g4_v8192_r64_bf16", R=70, gamma=4, V=8192, r=64, d=64, seed=38),
+    W.custom("acc_r8_g3_v2048_r128_bf16", R=8, gamma=3, V=2048, r=128, d=64, seed=39),
 ]
 
 
