@@ -126,6 +126,63 @@ def traffic_record(workload: str, kernel: str):
 
 kEagerSkip = 60   # eager rounds run before the counted ones (about 25 ms of work)
 
+# The other single-GPU bf16 workloads the bench line also reports.
+OTHER_WORKLOADS = ("latency_r1_g16_v151936", "batch_r32_g16_v151936", "heavy_r128_g16_v129280",
+                   "full_r256_g16_v129280_sts")
+
+
+def measure_other(w, dev, steps):
+    """The round (graph replays, two alternating input sets) and the
+    persistent sampling launch (events over eager rounds) of one workload."""
+    import numpy as np
+    import torch
+    from semi_ar_draft_round_amd import binding, workloads as W
+    from semi_ar_draft_round_amd import device_round as DR
+    t0 = time.perf_counter()
+    rounds = [DR.to_device(W.make_inputs(w, round_index=i), dev) for i in range(2)]
+    rounds[1].W1, rounds[1].W2t, rounds[1].w = rounds[0].W1, rounds[0].W2t, rounds[0].w
+    for d in rounds:
+        DR.run_round(d)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for d in rounds:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                DR.run_round(d)
+        torch.cuda.current_stream().wait_stream(stream)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    timers = [binding.SweepTimer() for _ in range(steps)]
+    for i in range(len(timers) + kEagerSkip):
+        d = rounds[i % 2]
+        DR.sample_conf(d, timer=timers[i - kEagerSkip] if i >= kEagerSkip else None)
+        DR.schedule(d)
+        DR.verify(d)
+    torch.cuda.synchronize()
+    launch_us = float(np.mean([t.elapsed_ms() * 1e3 for t in timers]))
+    for i in range(3):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        graphs[i % 2].replay()
+    end.record()
+    torch.cuda.synchronize()
+    round_us = start.elapsed_time(end) / steps * 1e3
+    kernel = binding.dspark_markov_sample_kernel(rounds[0].U.dtype, w.R, w.gamma, w.V, w.r)
+    bytes_launch = sample_bytes_per_position(w) * w.gamma
+    rec = {"round_us": round(round_us, 1), "tokens_per_s": round(w.R * w.gamma / (round_us * 1e-6), 1),
+           "launch_us": round(launch_us, 1), "frac": round(bytes_launch / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernel": kernel.split(":")[0], "seconds": round(time.perf_counter() - t0, 1)}
+    del graphs, rounds
+    torch.cuda.empty_cache()
+    return rec
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -138,6 +195,8 @@ def main():
     ap.add_argument("--no-modes", action="store_true",
                     help="skip timing the other modes (the production scheduler, greedy verification, the "
                          "analytic acceptance, the RNN-head draft, STS), e.g. for counter runs on the round")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the round and sampling-launch timings of the other bf16 workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB a few times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count) and exit")
@@ -318,6 +377,15 @@ def main():
         "modes_us": {k: round(v, 2) for k, v in modes.items()},
         "roofline": roofline,
     }
+    # the other bf16 workloads, each on its own inputs (two sets, as above):
+    # the sampling launch by its events over eager rounds and the round graph
+    if not args.no_other_workloads:
+        rec["other_workloads"] = {}
+        for name in OTHER_WORKLOADS:
+            if name == w.name:
+                continue
+            rec["other_workloads"][name] = measure_other(W.BY_NAME[name], dev, max(args.steps, 10))
+            log(f"[bench] {name}: {rec['other_workloads'][name]}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(inps, args.cpu_requests)
