@@ -40,14 +40,16 @@
  *     obligations and are not checked.
  *   - No call keeps state between calls.  Calls on different streams with
  *     different workspaces may run concurrently, with one exception: with
- *     bf16 storage, dspark_markov_sample(_ex) runs all gamma positions in one
- *     persistent launch whose work groups (one per compute unit) meet at a
- *     grid barrier between positions, so it needs every compute unit of the
- *     device at once.  Do not overlap it with other work on the device (the
- *     library cannot see or serialise the caller's streams).  If its grid is
- *     not resident as a whole, the barrier gives up after 0.5 s instead of
- *     hanging: every x is then -1 and every lse and logit NaN, and the status
- *     word of dspark_markov_sample_ex reads DSPARK_ETIMEOUT.
+ *     bf16 storage, dspark_markov_sample(_ex), and dspark_rnn_sample at the
+ *     shapes where it keeps W2t on chip (dspark_rnn_sample_kernel), run all
+ *     gamma positions in one persistent launch whose work groups (one per
+ *     compute unit) meet at grid barriers between positions, so they need
+ *     every compute unit of the device at once.  Do not overlap them with
+ *     other work on the device (the library cannot see or serialise the
+ *     caller's streams).  If the grid is not resident as a whole, the barrier
+ *     gives up after 0.5 s instead of hanging: every x is then -1 and every
+ *     lse and logit NaN (s and o of dspark_rnn_sample are then undefined),
+ *     and the status word of dspark_markov_sample_ex reads DSPARK_ETIMEOUT.
  *   - dt selects the storage type of the large tensors (U, W1, W2, w, h,
  *     target): fp32 or bf16.  Arithmetic is fp32 (scheduler: fp64 and exact
  *     integers).  Random draws are inputs, drawn by the caller.
