@@ -211,6 +211,38 @@ dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r,
                                 float* logit, float* s, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dspark_rnn_prepare — the W1-row part of the RNN head's projection for
+ * every token, computed once per set of weights.
+ *
+ * Passage: notes eq (6).  z's middle block is W1[x_{k-1}], so W's columns
+ * r .. 2r - 1 contribute P[x_{k-1}] with P[v] = W[:, r:2r] W1[v] (3r values
+ * per token: the gate, candidate and output rows).  The product is a plain
+ * matrix product, bf16 inputs with fp32 accumulation, stored in fp32.
+ *
+ *   W1    [V][r] bf16, Wrnn [3r][2r + d] bf16 as in dspark_rnn_sample
+ *   P     [V][3r] f32 out (4 * V * 3r bytes: 397 MB at V = 129280, r = 256)
+ *
+ * Limits: bf16 storage only (DSPARK_EDTYPE otherwise); r in {32, 64, 128,
+ * 256}; 2 <= V < 2^24; d a multiple of 16.
+ */
+dspark_status dspark_rnn_prepare(dspark_dtype dt, int V, int r, int d, const void* W1, const void* Wrnn, float* P,
+                                 void* stream);
+
+/*
+ * dspark_rnn_sample_ex — dspark_rnn_sample with P from dspark_rnn_prepare
+ * (for the same W1 and Wrnn; NULL: as dspark_rnn_sample).  Where the call
+ * keeps W2t on chip (dspark_rnn_sample_kernel) the step then looks the
+ * W1-row part of y up in P instead of multiplying W1[x_{k-1}] by W on the
+ * matrix cores; the result is the same product up to the order of the fp32
+ * sums.  Other shapes, and fp32 storage, ignore P.
+ */
+dspark_status dspark_rnn_sample_ex(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                   const void* W1, const void* W2t, const void* Wrnn, const void* h,
+                                   const int32_t* x0, const float* G, const float* g, const float* P, int32_t* x,
+                                   float* lse, float* logit, float* s, void* o, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/*
  * dspark_confidence — conditional survival of every drafted position.
  *
  * Passage: notes eq (7), c_k = sigmoid(w^T [h_k ; W1[x_{k-1}]]), and the

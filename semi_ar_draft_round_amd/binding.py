@@ -44,6 +44,9 @@ _SIGNATURES = {
                          _SZ, _P],
     "dspark_rnn_sample": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _SZ, _P],
+    "dspark_rnn_sample_ex": [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _P, _SZ, _P],
+    "dspark_rnn_prepare": [_I, _I, _I, _I, _P, _P, _P, _P],
     "dspark_sts_fit": [_I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
     "dspark_workspace_size": [_I, _I, _I, _I, _I, _I],
     "dspark_status_string": [_I],
@@ -449,9 +452,25 @@ def dspark_acceptance(target, U, W1, W2t, x0, x, lse, row0=None, c_star=None, ws
     return c_star
 
 
-def dspark_rnn_sample(U, W1, W2t, Wrnn, h, x0, G, g, x=None, lse=None, logit=None, s=None, o=None, ws=None):
+def dspark_rnn_prepare(W1, Wrnn, d, P=None):
+    """P [V][3r] f32: the W1-row part of the RNN head's projection for every
+    token (bf16 weights)."""
+    lib = load_library()
+    V, r = W1.shape
+    dev = W1.device
+    _check(W1, "W1", (V, r), (torch.bfloat16,), dev)
+    _check(Wrnn, "Wrnn", (3 * r, 2 * r + d), (torch.bfloat16,), dev)
+    P = torch.empty((V, 3 * r), dtype=torch.float32, device=dev) if P is None else P
+    _check(P, "P", (V, 3 * r), (torch.float32,), dev)
+    _raise("dspark_rnn_prepare", lib.dspark_rnn_prepare(BF16, V, r, d, _ptr(W1), _ptr(Wrnn), _ptr(P), _stream()))
+    return P
+
+
+def dspark_rnn_sample(U, W1, W2t, Wrnn, h, x0, G, g, x=None, lse=None, logit=None, s=None, o=None, ws=None,
+                      P=None):
     """x [R][gamma] int32, lse and logit [R][gamma] f32, s [R][gamma][r] f32 (the
-    states) and o [R][gamma][r] (the bias vectors): sampling with the RNN head."""
+    states) and o [R][gamma][r] (the bias vectors): sampling with the RNN head
+    (with P from dspark_rnn_prepare: dspark_rnn_sample_ex)."""
     lib = load_library()
     R, gamma, V = U.shape
     r = W1.shape[1]
@@ -473,10 +492,17 @@ def dspark_rnn_sample(U, W1, W2t, Wrnn, h, x0, G, g, x=None, lse=None, logit=Non
     s = torch.empty((R, gamma, r), dtype=torch.float32, device=dev) if s is None else s
     o = torch.empty((R, gamma, r), dtype=U.dtype, device=dev) if o is None else o
     ws = workspace(WS_RNN_SAMPLE, R, gamma, V, r, dev) if ws is None else ws
-    st = lib.dspark_rnn_sample(_dt(U), R, gamma, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(Wrnn), _ptr(h),
-                               _ptr(x0), _ptr(G), _ptr(g), _ptr(x), _ptr(lse), _ptr(logit), _ptr(s), _ptr(o),
-                               _ptr(ws), ws.numel(), _stream())
-    _raise("dspark_rnn_sample", st)
+    if P is None:
+        st = lib.dspark_rnn_sample(_dt(U), R, gamma, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(Wrnn), _ptr(h),
+                                   _ptr(x0), _ptr(G), _ptr(g), _ptr(x), _ptr(lse), _ptr(logit), _ptr(s), _ptr(o),
+                                   _ptr(ws), ws.numel(), _stream())
+        _raise("dspark_rnn_sample", st)
+    else:
+        _check(P, "P", (V, 3 * r), (torch.float32,), dev)
+        st = lib.dspark_rnn_sample_ex(_dt(U), R, gamma, V, r, d, _ptr(U), _ptr(W1), _ptr(W2t), _ptr(Wrnn),
+                                      _ptr(h), _ptr(x0), _ptr(G), _ptr(g), _ptr(P), _ptr(x), _ptr(lse),
+                                      _ptr(logit), _ptr(s), _ptr(o), _ptr(ws), ws.numel(), _stream())
+        _raise("dspark_rnn_sample_ex", st)
     return x, lse, logit, s, o
 
 

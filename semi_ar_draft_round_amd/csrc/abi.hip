@@ -13,6 +13,8 @@ namespace dspark {
 // sample.hip
 size_t sample_workspace_bytes(dspark_dtype dt, int R, int gamma, int V);
 size_t rnn_workspace_bytes(int R, int gamma, int r);
+hipError_t rnn_prepare_launch(int V, int r, int d, const uint16_t* W1, const uint16_t* Wrnn, float* P,
+                              hipStream_t s);
 // sts.hip
 size_t sts_workspace_bytes(int N, int gamma, int G, int M);
 bool sts_shape_ok(int N, int gamma, int G, int M);
@@ -335,10 +337,11 @@ dspark_status dspark_acceptance(dspark_dtype dt, int R, int gamma, int V, int r,
   return DSPARK_OK;
 }
 
-dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
-                                const void* W1, const void* W2t, const void* Wrnn, const void* h,
-                                const int32_t* x0, const float* G, const float* g, int32_t* x, float* lse,
-                                float* logit, float* s, void* o, void* ws, size_t ws_bytes, void* stream) {
+static dspark_status rnn_sample_impl(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                     const void* W1, const void* W2t, const void* Wrnn, const void* h,
+                                     const int32_t* x0, const float* G, const float* g, const float* P, int32_t* x,
+                                     float* lse, float* logit, float* s, void* o, void* ws, size_t ws_bytes,
+                                     void* stream) {
   if (!dtype_ok(dt)) return DSPARK_EDTYPE;
   if (!draft_shape_ok(R, gamma, V)) return DSPARK_EINVAL;
   if (!rank_ok(dt, r)) return DSPARK_EDTYPE;
@@ -349,9 +352,41 @@ dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r,
   dspark_status st = check_device();
   if (st != DSPARK_OK) return st;
   const size_t off = (sample_ws_any(R, gamma, V) + 255) & ~static_cast<size_t>(255);
-  const RnnHead head{Wrnn, h, d, s, o, reinterpret_cast<float*>(static_cast<char*>(ws) + off)};
+  const RnnHead head{Wrnn, h, d, s, o, reinterpret_cast<float*>(static_cast<char*>(ws) + off),
+                     dt == DSPARK_BF16 ? P : nullptr};
   if (sample_launch(dt, R, gamma, V, r, U, W1, W2t, x0, G, g, x, lse, logit, ws, static_cast<hipStream_t>(stream),
                     &head, nullptr, nullptr, nullptr, nullptr, nullptr) != hipSuccess)
+    return DSPARK_ELAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_rnn_sample(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                const void* W1, const void* W2t, const void* Wrnn, const void* h,
+                                const int32_t* x0, const float* G, const float* g, int32_t* x, float* lse,
+                                float* logit, float* s, void* o, void* ws, size_t ws_bytes, void* stream) {
+  return rnn_sample_impl(dt, R, gamma, V, r, d, U, W1, W2t, Wrnn, h, x0, G, g, nullptr, x, lse, logit, s, o, ws,
+                         ws_bytes, stream);
+}
+
+dspark_status dspark_rnn_sample_ex(dspark_dtype dt, int R, int gamma, int V, int r, int d, const void* U,
+                                   const void* W1, const void* W2t, const void* Wrnn, const void* h,
+                                   const int32_t* x0, const float* G, const float* g, const float* P, int32_t* x,
+                                   float* lse, float* logit, float* s, void* o, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return rnn_sample_impl(dt, R, gamma, V, r, d, U, W1, W2t, Wrnn, h, x0, G, g, P, x, lse, logit, s, o, ws,
+                         ws_bytes, stream);
+}
+
+dspark_status dspark_rnn_prepare(dspark_dtype dt, int V, int r, int d, const void* W1, const void* Wrnn, float* P,
+                                 void* stream) {
+  if (!dtype_ok(dt)) return DSPARK_EDTYPE;
+  if (dt != DSPARK_BF16 || !rank_ok(dt, r)) return DSPARK_EDTYPE;
+  if (V < 2 || V >= (1 << 24) || d < 1 || d > (1 << 20) || d % 16 != 0) return DSPARK_EINVAL;
+  if (!W1 || !Wrnn || !P) return DSPARK_EINVAL;
+  dspark_status st = check_device();
+  if (st != DSPARK_OK) return st;
+  if (rnn_prepare_launch(V, r, d, static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(Wrnn), P,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ELAUNCH;
   return DSPARK_OK;
 }

@@ -396,6 +396,19 @@ hipError_t rnn_hproj_launch(const RnnHead& hd, int R, int gamma, int r, hipStrea
   return hipGetLastError();
 }
 
+// P[v] = W's W1-row columns applied to W1 row v, for every token: the
+// projection kernel with W1 in h's place (V rows, inner length r) and the
+// W1-row block of W (columns r .. 2r - 1) as the weights, in one split.
+hipError_t rnn_prepare_launch(int V, int r, int d, const uint16_t* W1, const uint16_t* Wrnn, float* P,
+                              hipStream_t s) {
+  const int K = 2 * r + d;
+  const int nM = ceil_div(V, kHpBM), nN = 3 * r / kHpBN;
+  const int per = ceil_div(r, kHpBK);
+  hipLaunchKernelGGL(rnn_hproj_bf16, dim3(nM * nN), dim3(kHpThreads), 0, s, V, 3 * r, r, K, nM, nN, per, W1,
+                     Wrnn + r, P);
+  return hipGetLastError();
+}
+
 hipError_t rnn_step_launch(dspark_dtype dt, const RnnHead& hd, int R, int gamma, int V, int r, int k,
                            const void* W1, const int32_t* x0, const unsigned long long* keys, hipStream_t s) {
   if (dt == DSPARK_BF16) {

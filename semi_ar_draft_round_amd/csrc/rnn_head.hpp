@@ -12,6 +12,7 @@ struct RnnHead {
   void* o;         // [R][gamma][r] storage type out: each position's bias vector
   float* part;     // f32 workspace: bf16, the hidden-state partials [splits][R gamma][3r],
                    // summed into the first; fp32, one position's projection [R][3r]
+  const float* P;  // [V][3r] f32 or null: W's W1-row columns applied to every W1 row
 };
 
 }  // namespace dspark

@@ -868,7 +868,7 @@ bool res_rnn_usable(int R, int V, int r, int max_wgs);
 hipError_t res_rnn_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
                           const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
                           const uint32_t* cancel, const void* Wrnn, const float* Yh, int d, float* st, void* o,
-                          hipStream_t s);
+                          const float* P, hipStream_t s);
 
 // The kernel sample_launch runs the Markov-head positions with, for a shape
 // (the same choice, in the same order).
@@ -934,7 +934,7 @@ hipError_t sample_launch(dspark_dtype dt, int R, int gamma, int V, int r, const 
   if (gxr > 0 && rnn) {
     if ((err = rnn_hproj_launch(*rnn, R, gamma, r, s)) != hipSuccess) return err;
     if ((err = res_rnn_launch(R, gamma, V, r, U, W1, W2t, x0, G, g, w, gxr, cancel, rnn->W, rnn->part, rnn->d,
-                              rnn->s, rnn->o, s)) != hipSuccess)
+                              rnn->s, rnn->o, rnn->P, s)) != hipSuccess)
       return err;
   }
   for (int kb = 0; gxp == 0 && gxr == 0 && kb < gamma; kb += span) {

@@ -98,9 +98,13 @@ struct ResRnn {
   int d;
   float* s;             // [R][gamma][r] out: the state after each position
   uint16_t* o;          // [R][gamma][r] out: each position's bias vector
+  const float* P;       // [V][3r] or null: W's W1-row columns times every W1 row (dspark_rnn_prepare)
 };
 
-template <int RB, int KS16, bool VEC, bool RNN = false>
+// RNN: 0 the Markov head; 1 the RNN head, its step taking z = [s; W1 row]
+// on the matrix cores; 2 the RNN head with the W1-row part looked up in P,
+// so the step's products cover the state part only.
+template <int RB, int KS16, bool VEC, int RNN = 0>
 __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     int R, int gamma, int V, const uint16_t* __restrict__ U, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W2t, const int32_t* __restrict__ x0, const float* __restrict__ G,
@@ -322,9 +326,10 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
   // already summed) and apply the gates.  o and s are stored and read back as agent-scope
   // atomics (store32_agent, load16_agent), coherent across the dies.
   auto rnn_phase = [&](int k, unsigned int round) -> bool {
-    if constexpr (RNN) {
+    if constexpr (RNN != 0) {
+      constexpr bool kP = RNN == 2;
       constexpr int r = KS16 * 16;
-      constexpr int kZ = 4 * r + 16;   // bytes of a z row in LDS (2r bf16 and a pad)
+      constexpr int kZ = (kP ? 2 : 4) * r + 16;   // bytes of a z row in LDS (r or 2r bf16 and a pad)
       constexpr int nJB = r / 32;
       const int K = 2 * r + rnn.d;
       const int nItems = nJB * ((R + 31) / 32);
@@ -332,6 +337,9 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
       static_assert(6 * 16 * kWave * 4 <= NROWS * kE, "the six partial products fit in the W1-row area");
       for (int item = bx; item < nItems; item += gx) {
         const int jb = item % nJB, ib = item / nJB;
+        // kP: this thread's request's previous token (the gate thread below
+        // is the same thread and looks the W1-row part of y up in P)
+        int pprev = -1;
         {   // z rows: 16 threads per request
           const int i = static_cast<int>(threadIdx.x) >> 4, u = static_cast<int>(threadIdx.x) & 15;
           const int rc = min(32 * ib + i, R - 1);
@@ -349,6 +357,7 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
             }
             prev = token_or_none(key_token(best), V);
           }
+          if constexpr (kP) pprev = prev;
           uint8_t* zr = erows + i * kZ;
           // the state: r floats, r / 16 per thread, rounded to bf16 (zeros at k = 0)
           const float* srow = rnn.s + (static_cast<int64_t>(rc) * gamma + (k > 0 ? k - 1 : 0)) * r;
@@ -366,16 +375,17 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
             const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
             *reinterpret_cast<u32x4*>(zr + 16 * p) = u32x4{w0, w1, w2, w3};
           }
-          // the previous token's W1 row (zeros when there is none)
-          const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
+          if constexpr (!kP) {   // the previous token's W1 row (zeros when there is none)
+            const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
 #pragma unroll
-          for (int p = u; p < r / 8; p += 16)
-            *reinterpret_cast<u32x4*>(zr + 2 * r + 16 * p) = *reinterpret_cast<const u32x4*>(erow + 8 * p);
+            for (int p = u; p < r / 8; p += 16)
+              *reinterpret_cast<u32x4*>(zr + 2 * r + 16 * p) = *reinterpret_cast<const u32x4*>(erow + 8 * p);
+          }
         }
         __syncthreads();
         f32x16 acc = {};
-        if (wave < 6) {   // part g = wave / 2 over half wave % 2 of the 2r inner elements
-          constexpr int KSH = r / 16;   // k-steps per half
+        if (wave < 6) {   // part g = wave / 2 over half wave % 2 of the 2r (kP: r) inner elements
+          constexpr int KSH = kP ? r / 32 : r / 16;   // k-steps per half
           constexpr int B8 = KSH < 8 ? KSH : 8;
           const int gp = wave >> 1, kh = (wave & 1) * KSH;
           const uint16_t* wrow = rnn.W + static_cast<int64_t>(gp * r + 32 * jb + j) * K + 16 * kh + 8 * h;
@@ -417,6 +427,15 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
           float2 yh[3];
 #pragma unroll
           for (int gp = 0; gp < 3; ++gp) yh[gp] = *reinterpret_cast<const float2*>(rnn.Yh + row * (3 * r) + gp * r + col);
+          float2 pv[3] = {};   // kP: the W1-row part (zero without a previous token)
+          if constexpr (kP) {
+            const float* prow = rnn.P + static_cast<int64_t>(pprev >= 0 ? pprev : 0) * (3 * r) + col;
+#pragma unroll
+            for (int gp = 0; gp < 3; ++gp) {
+              const float2 v = *reinterpret_cast<const float2*>(prow + gp * r);
+              pv[gp] = pprev >= 0 ? v : make_float2(0.f, 0.f);
+            }
+          }
           // s_{k-1} of the same columns (this work group's own stores), read
           // at k = 0 too and unused there
           const u32x4 sp4 = load16_agent(rnn.s + (k > 0 ? row - 1 : row) * r + (col & ~3));
@@ -432,7 +451,8 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
 #pragma unroll
             for (int gp = 0; gp < 3; ++gp)
               y[gp] = (t ? yh[gp].y : yh[gp].x) +
-                      (red[(2 * gp * 16 + q) * kWave + l] + red[((2 * gp + 1) * 16 + q) * kWave + l]);
+                      ((red[(2 * gp * 16 + q) * kWave + l] + red[((2 * gp + 1) * 16 + q) * kWave + l]) +
+                       (kP ? (t ? pv[gp].y : pv[gp].x) : 0.f));
             const float gate = 1.f / (1.f + expf(-y[0]));
             sn[t] = gate * (k > 0 ? sprev[t] : 0.f) + (1.f - gate) * tanhf(y[1]);
             ob |= bf16_bits_rne(tanhf(y[2])) << (16 * t);
@@ -554,7 +574,7 @@ int res_grid_x(int R, int V, int r, int max_wgs) {
   return (nTiles + gx - 1) / gx <= res_tiles_for(R, r) ? gx : 0;
 }
 
-template <int RB, int KS16, bool VEC, bool RNN = false>
+template <int RB, int KS16, bool VEC, int RNN = 0>
 static bool res_fits_one() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -638,28 +658,35 @@ hipError_t res_launch(int R, int gamma, int V, int r, const void* U, const void*
 bool res_rnn_usable(int R, int V, int r, int max_wgs) {
   if (R > 128 || res_grid_x(R, V, r, max_wgs) == 0) return false;
   const bool vec = (V % kGChunk) == 0;
-  if (r == 128 && R > 64) return vec ? res_fits_one<4, 8, true, true>() : res_fits_one<4, 8, false, true>();
+  if (r == 128 && R > 64) return vec ? res_fits_one<4, 8, true, 1>() : res_fits_one<4, 8, false, 1>();
   if (r != 256 || R < 33) return false;
-  if (R <= 64) return vec ? res_fits_one<2, 16, true, true>() : res_fits_one<2, 16, false, true>();
-  return vec ? res_fits_one<4, 16, true, true>() : res_fits_one<4, 16, false, true>();
+  if (R <= 64) return vec ? res_fits_one<2, 16, true, 1>() : res_fits_one<2, 16, false, 1>();
+  return vec ? res_fits_one<4, 16, true, 1>() : res_fits_one<4, 16, false, 1>();
 }
 
 template <int RB, int KS16, bool VEC>
 static void launch_res_rnn(int R, int gamma, int V, const void* U, const void* W1, const void* W2t,
                            const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
                            const uint32_t* cancel, const ResRnn& rn, hipStream_t s) {
-  hipLaunchKernelGGL((sample_steps_res<RB, KS16, VEC, true>), dim3(gx), dim3(kResThreads), 0, s, R, gamma, V,
-                     static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
-                     static_cast<const uint16_t*>(W2t), x0, G, g, w, 0, gamma, cancel, rn);
+  // with P, the variant whose step looks the W1-row part up, if it fits
+  if (rn.P && res_fits_one<RB, KS16, VEC, 2>())
+    hipLaunchKernelGGL((sample_steps_res<RB, KS16, VEC, 2>), dim3(gx), dim3(kResThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
+                       static_cast<const uint16_t*>(W2t), x0, G, g, w, 0, gamma, cancel, rn);
+  else
+    hipLaunchKernelGGL((sample_steps_res<RB, KS16, VEC, 1>), dim3(gx), dim3(kResThreads), 0, s, R, gamma, V,
+                       static_cast<const uint16_t*>(U), static_cast<const uint16_t*>(W1),
+                       static_cast<const uint16_t*>(W2t), x0, G, g, w, 0, gamma, cancel, rn);
 }
 
 // Launches all positions with the RNN head (the caller checked
-// res_rnn_usable and computed the hidden-state partials).
+// res_rnn_usable and computed the hidden-state partials).  P, when given,
+// is W's W1-row columns applied to every W1 row (dspark_rnn_prepare).
 hipError_t res_rnn_launch(int R, int gamma, int V, int r, const void* U, const void* W1, const void* W2t,
                           const int32_t* x0, const float* G, const float* g, const SampleWs& w, int gx,
                           const uint32_t* cancel, const void* Wrnn, const float* Yh, int d, float* st, void* o,
-                          hipStream_t s) {
-  const ResRnn rn{static_cast<const uint16_t*>(Wrnn), Yh, d, st, static_cast<uint16_t*>(o)};
+                          const float* P, hipStream_t s) {
+  const ResRnn rn{static_cast<const uint16_t*>(Wrnn), Yh, d, st, static_cast<uint16_t*>(o), P};
   const bool vec = (V % kGChunk) == 0;
 #define DSPARK_RES_RNN(RB, KS)                                                                   \
   (vec ? launch_res_rnn<RB, KS, true>(R, gamma, V, U, W1, W2t, x0, G, g, w, gx, cancel, rn, s) \

@@ -173,7 +173,13 @@ def rnn_sample(d: DeviceRound):
     """The round's draft with the RNN head instead of the Markov head."""
     q = d.rnn
     B.dspark_rnn_sample(d.U, d.W1, d.W2t, q["W"], d.h, d.x0, d.G, d.g, q["x"], q["lse"], q["logit"], q["s"],
-                        q["o"], q["ws"])
+                        q["o"], q["ws"], P=q.get("P"))
+
+
+def rnn_prepare(d: DeviceRound):
+    """The W1-row part of the RNN head's projection for every token, kept
+    with the round's RNN weights (bf16; done once per set of weights)."""
+    d.rnn["P"] = B.dspark_rnn_prepare(d.W1, d.rnn["W"], d.h.shape[2], P=d.rnn.get("P"))
 
 
 def verify_greedy(d: DeviceRound):

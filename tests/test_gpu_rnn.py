@@ -48,12 +48,14 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _run(inp, Wrnn, dev, E=None):
+def _run(inp, Wrnn, dev, E=None, prepared=False):
     from semi_ar_draft_round_amd import binding as B
     from semi_ar_draft_round_amd import device_round as DR
     d = DR.to_device(inp, dev)
     W1 = d.W1 if E is None else DR._dev_store(E, inp.w.dtype, dev)
-    out = B.dspark_rnn_sample(d.U, W1, d.W2t, DR._dev_store(Wrnn, inp.w.dtype, dev), d.h, d.x0, d.G, d.g)
+    Wd = DR._dev_store(Wrnn, inp.w.dtype, dev)
+    P = B.dspark_rnn_prepare(W1, Wd, inp.w.d) if prepared else None
+    out = B.dspark_rnn_sample(d.U, W1, d.W2t, Wd, d.h, d.x0, d.G, d.g, P=P)
     torch.cuda.synchronize()
     return d, W1, [t.cpu() for t in out]
 
@@ -114,6 +116,42 @@ def test_rnn_small(w, dev):
     _, _, got = _run(inp, Wrnn, dev)
     rep = _check(inp, Wrnn, got, np.arange(w.R))
     say(f"  {rep}")
+
+
+@pytest.mark.parametrize("w", CASES[6:], ids=[w.name for w in CASES[6:]])
+def test_rnn_small_prepared(w, dev):
+    """The resident launch with the W1-row part looked up in P
+    (dspark_rnn_prepare, dspark_rnn_sample_ex): the same checks against the
+    oracle, which forms y = W z directly (notes eq (6))."""
+    say(f"[rnn, P] {w.name}")
+    inp = W.make_inputs(w)
+    inp.x0[0] = -1                                   # no previous token at the first position: P unused
+    Wrnn = W.make_rnn_weights(w)
+    _, _, got = _run(inp, Wrnn, dev, prepared=True)
+    rep = _check(inp, Wrnn, got, np.arange(w.R))
+    say(f"  {rep}")
+
+
+def test_rnn_prepare_is_the_product(dev):
+    """P[v] = W[:, r:2r] W1[v] (the matrix product, fp32 accumulation of the
+    bf16 entries) on sampled tokens, the first and the last among them."""
+    from semi_ar_draft_round_amd import binding as B
+    from semi_ar_draft_round_amd import device_round as DR
+    for w in (CASES[6], CASES[7]):
+        inp = W.make_inputs(w)
+        Wrnn = W.make_rnn_weights(w)
+        W1 = DR._dev_store(inp.E, w.dtype, dev)
+        P = B.dspark_rnn_prepare(W1, DR._dev_store(Wrnn, w.dtype, dev), w.d).cpu().numpy().astype(np.float64)
+        E = as_f64(inp.E, w.dtype)
+        Wd = as_f64(Wrnn, w.dtype)[:, w.r:2 * w.r]
+        rng = np.random.default_rng(5)
+        vs = np.unique(np.concatenate([[0, w.V - 1], rng.choice(w.V, size=64, replace=False)]))
+        want = E[vs] @ Wd.T                               # [tokens][3r]
+        # fp32 sums of r products of bf16 values (exact in fp32): within
+        # r 2^-24 of the sum of their magnitudes (a sequential sum's bound)
+        scale = np.abs(E[vs]) @ np.abs(Wd.T)
+        err = np.abs(P[vs] - want)
+        assert np.all(err <= w.r * 2.0 ** -24 * scale), (w.name, float((err / np.maximum(scale, 1e-30)).max()))
 
 
 def test_rnn_kernel_choice(dev):
