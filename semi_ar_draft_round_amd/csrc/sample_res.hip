@@ -325,6 +325,34 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
   // add the two halves and the hidden-state part (its split partials
   // already summed) and apply the gates.  o and s are stored and read back as agent-scope
   // atomics (store32_agent, load16_agent), coherent across the dies.
+  // z's state rows of step item block ib at position k into LDS (the
+  // W1-row area): s_{k-1} of the block's 32 requests rounded to bf16, zeros
+  // at k = 0; 16 threads per request
+  auto z_state = [&](int k, int ib) {
+    if constexpr (RNN != 0) {
+      constexpr int r = KS16 * 16;
+      constexpr int kZ = (RNN == 2 ? 2 : 4) * r + 16;
+      const int i = static_cast<int>(threadIdx.x) >> 4, u = static_cast<int>(threadIdx.x) & 15;
+      const int rc = min(32 * ib + i, R - 1);
+      uint8_t* zr = erows + i * kZ;
+      const float* srow = rnn.s + (static_cast<int64_t>(rc) * gamma + (k > 0 ? k - 1 : 0)) * r;
+#pragma unroll
+      for (int p = u; p < r / 8; p += 16) {
+        const u32x4 a = load16_agent(srow + 8 * p), b = load16_agent(srow + 8 * p + 4);
+        float4 lo = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                                __uint_as_float(a[3]));
+        float4 hi = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]),
+                                __uint_as_float(b[3]));
+        if (k == 0) lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint32_t w0 = bf16_bits_rne(lo.x) | (bf16_bits_rne(lo.y) << 16);
+        const uint32_t w1 = bf16_bits_rne(lo.z) | (bf16_bits_rne(lo.w) << 16);
+        const uint32_t w2 = bf16_bits_rne(hi.x) | (bf16_bits_rne(hi.y) << 16);
+        const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
+        *reinterpret_cast<u32x4*>(zr + 16 * p) = u32x4{w0, w1, w2, w3};
+      }
+    }
+  };
+
   auto rnn_phase = [&](int k, unsigned int round) -> bool {
     if constexpr (RNN != 0) {
       constexpr bool kP = RNN == 2;
@@ -358,23 +386,10 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
             prev = token_or_none(key_token(best), V);
           }
           if constexpr (kP) pprev = prev;
+          // the state rows (with P, the first item's were gathered before
+          // the barrier, right after the previous position's sweep)
+          if (!(kP && item == bx && k > kb)) z_state(k, ib);
           uint8_t* zr = erows + i * kZ;
-          // the state: r floats, r / 16 per thread, rounded to bf16 (zeros at k = 0)
-          const float* srow = rnn.s + (static_cast<int64_t>(rc) * gamma + (k > 0 ? k - 1 : 0)) * r;
-#pragma unroll
-          for (int p = u; p < r / 8; p += 16) {
-            const u32x4 a = load16_agent(srow + 8 * p), b = load16_agent(srow + 8 * p + 4);
-            float4 lo = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
-                                    __uint_as_float(a[3]));
-            float4 hi = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]),
-                                    __uint_as_float(b[3]));
-            if (k == 0) lo = hi = make_float4(0.f, 0.f, 0.f, 0.f);
-            const uint32_t w0 = bf16_bits_rne(lo.x) | (bf16_bits_rne(lo.y) << 16);
-            const uint32_t w1 = bf16_bits_rne(lo.z) | (bf16_bits_rne(lo.w) << 16);
-            const uint32_t w2 = bf16_bits_rne(hi.x) | (bf16_bits_rne(hi.y) << 16);
-            const uint32_t w3 = bf16_bits_rne(hi.z) | (bf16_bits_rne(hi.w) << 16);
-            *reinterpret_cast<u32x4*>(zr + 16 * p) = u32x4{w0, w1, w2, w3};
-          }
           if constexpr (!kP) {   // the previous token's W1 row (zeros when there is none)
             const uint16_t* erow = prev >= 0 ? W1 + static_cast<int64_t>(prev) * r : kZeroRow;
 #pragma unroll
@@ -543,6 +558,12 @@ __global__ __launch_bounds__(kResThreads, 1) void sample_steps_res(
     }
     if (k + 1 == ke) break;
     const f32x4 gq = load_gq(k + 1);
+    // with P, the first step item's state rows for position k + 1 (s_k is
+    // complete: its step ended before this position's sweep) go to LDS
+    // while the barrier is pending
+    if constexpr (RNN == 2) {
+      if (bx < (KS16 / 2) * ((R + 31) / 32)) z_state(k + 1, bx / (KS16 / 2));
+    }
     // the RNN head meets twice per position: the keys of position k, then o
     // of position k + 1
     if (!grid_barrier(ws.bar, RNN ? 2 * (k + 1) : k + 1, &barflag, cancel)) return;
