@@ -176,6 +176,28 @@ def test_rnn_sample_rejects_bad_arguments(lib):
     assert call(ws_bytes=8) == EWORKSPACE
 
 
+def test_rnn_sample_ex_and_prepare_reject_bad_arguments(lib):
+    def call_ex(dt=1, R=2, gamma=3, V=500, r=64, d=32, ptr=FAKE, P=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        args = [ptr] * 8 + [P] + [ptr] * 5      # U W1 W2t Wrnn h x0 G g, P, x lse logit s o
+        return lib.dspark_rnn_sample_ex(dt, R, gamma, V, r, d, *args, ws, ws_bytes, None)
+    assert call_ex(dt=5) == EDTYPE
+    assert call_ex(r=48) == EDTYPE
+    assert call_ex(d=24) == EINVAL
+    assert call_ex(ptr=None) == EINVAL
+    assert call_ex(ws_bytes=8) == EWORKSPACE
+
+    def prep(dt=1, V=500, r=64, d=32, W1=FAKE, W=FAKE, P=FAKE):
+        return lib.dspark_rnn_prepare(dt, V, r, d, W1, W, P, None)
+    assert prep(dt=0) == EDTYPE                 # the table is made for bf16 weights only
+    assert prep(dt=5) == EDTYPE
+    assert prep(r=48) == EDTYPE
+    assert prep(V=1) == EINVAL
+    assert prep(V=1 << 24) == EINVAL
+    assert prep(d=24) == EINVAL
+    assert prep(W1=None) == EINVAL
+    assert prep(P=None) == EINVAL
+
+
 def test_sts_fit_rejects_bad_arguments(lib):
     def call(N=100, gamma=4, G=16, M=15, ptr=FAKE, ws=FAKE, ws_bytes=1 << 30):
         return lib.dspark_sts_fit(N, gamma, ptr, ptr, ptr, G, M, ptr, ptr, ptr, ptr, ws, ws_bytes, None)
